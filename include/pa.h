@@ -1,0 +1,148 @@
+/*
+ * pa.h — C ABI of libpa: paged KV-cache decode attention for AMD MI355X (gfx950).
+ *
+ * Sources cited in this header (the method is defined there; nothing else is):
+ *   [PA-summary]  azimuth.plus, "Efficient Memory Management for Large Language Model Serving
+ *                 with PagedAttention" (an Arabic summary of Kwon et al., SOSP 2023).
+ *   [PA-tutorial] un.csdn.net, "PagedAttention实战：如何用Python手搓一个高效KV缓存管理器"
+ *                 ("PagedAttention in practice: a KV-cache manager built by hand in Python").
+ *
+ * Data layout shared by every call (all arrays dense, row-major, no padding):
+ *   k_cache, v_cache   [num_blocks][num_kv_heads][block_size][head_dim]   dtype `dt`
+ *                      The physical block pool. One (block, head) tile is block_size*head_dim
+ *                      contiguous elements, the per-head B x d view of a block that
+ *                      [PA-summary] "The PagedAttention algorithm" (K_j, V_j in R^{B x d}) uses.
+ *   block_tables       int32 [num_seqs][max_blocks_per_seq]; entry j of row s is the physical
+ *                      block that holds tokens j*B .. j*B+B-1 of sequence s ([PA-summary]
+ *                      "Key idea: virtual memory for the KV cache"; [PA-tutorial] §2.1 PageTable).
+ *                      Entries at or beyond ceil(context_lens[s]/B) are never read.
+ *   context_lens       int32 [num_seqs]; T_s, the number of cached tokens of sequence s.
+ *   slot_mapping       int32 [n_tokens]; slot = physical_block*block_size + offset_in_block
+ *                      ([PA-tutorial] §3.1 append_kv: page = pos // page_size, offset =
+ *                      pos % page_size); a negative slot means "skip this token".
+ *   q, out             [num_seqs][num_q_heads][head_dim]                 dtype `dt`
+ *   k_new, v_new       [n_tokens][num_kv_heads][head_dim]                dtype `dt`
+ *   block_pairs        int32 [n_pairs][2] = (src, dst) physical block ids.
+ *
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads) (contiguous groups).
+ *
+ * Ownership and execution: every pointer except the return of pa_status_string is a DEVICE
+ * pointer owned by the caller. The library allocates no memory and keeps no per-call state;
+ * it reads the device's compute-unit count once. Each call validates its scalar arguments on the
+ * host, enqueues its kernel(s) on `stream` (a hipStream_t; NULL = the null stream) and returns
+ * without waiting for completion.
+ *
+ * Device-resident indices (block ids, slots, context lengths) are not validated on the host.
+ * The kernels clamp them into the buffers the sizes describe, so a bad index gives an undefined
+ * result but never an access outside the caller's buffers: block ids are clamped to
+ * [0, num_blocks), context lengths to [0, min(max_context_len, max_blocks_per_seq*block_size)],
+ * and slots outside [0, num_blocks*block_size) are skipped.
+ *
+ * Errors: no exception crosses the ABI. PA_ERR_INVALID_ARG for a null pointer, a non-positive
+ * size, num_q_heads % num_kv_heads != 0 or an element count that overflows int64;
+ * PA_ERR_UNSUPPORTED for a (dtype, head_dim, block_size) the kernels are not built for;
+ * PA_ERR_WORKSPACE for a workspace smaller than pa_decode_workspace_size; PA_ERR_HIP when the
+ * HIP runtime reports an error at launch.
+ *
+ * Supported shapes: dtype f32, f16, bf16; head_dim 64 or 128; block_size 8, 16 or 32.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,
+  PA_ERR_UNSUPPORTED = 2,
+  PA_ERR_WORKSPACE = 3,
+  PA_ERR_HIP = 4
+} pa_status;
+
+/*
+ * pa_write_kv — slot-mapped append of new keys and values into the block pool.
+ * [PA-tutorial] §3.1 (SequenceManager.append_kv): a token at position pos lands in logical page
+ * pos // B at offset pos % B of the physical page the page table maps it to; [PA-summary]
+ * "Key idea": physical blocks are filled one at a time as tokens arrive.
+ * For every i < n_tokens with 0 <= slot_mapping[i] < num_blocks*block_size and every KV head h:
+ *   k_cache[slot/B][h][slot%B][:] = k_new[i][h][:]   and the same for v_cache / v_new.
+ * A bit copy. Tokens with a negative or out-of-pool slot are skipped. Two tokens with the same
+ * slot in one call are a caller error (which write wins is unspecified). n_tokens == 0 is a
+ * valid no-op. Copy-on-write of a shared block is the caller's job (pa_copy_blocks) before
+ * the write.
+ */
+pa_status pa_write_kv(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
+                      const int32_t *slot_mapping, int n_tokens, int num_kv_heads,
+                      int head_dim, int block_size, int64_t num_blocks, pa_dtype dt,
+                      void *stream);
+
+/*
+ * pa_decode_workspace_size — bytes of device workspace pa_decode needs for these sizes.
+ * The workspace holds per-partition partial results (running max, running sum and partial
+ * output, fp32) plus one int32 arrival counter per (sequence, query-head group).
+ * partition_tokens: 0 = let the library choose (the same choice pa_decode makes for the same
+ * arguments); > 0 must be a multiple of 2*block_size.
+ * Returns 0 for invalid sizes.
+ */
+size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                int block_size, int max_context_len, int partition_tokens,
+                                pa_dtype dt);
+
+/*
+ * pa_decode — single-query (decode) attention of every sequence's query heads over its cached
+ * tokens, read block by block through the block table.
+ * [PA-summary] "The PagedAttention algorithm": for each query vector the kernel walks the
+ * block table, fetches K_j and V_j from non-contiguous physical blocks, forms partial attention
+ * per block with the block's own score maximum and merges the blocks with the log-sum-exp
+ * rescaling of the block-wise attention equation; the result equals standard attention.
+ * For every sequence s and query head h, with T = context_lens[s] and g = H_q/H_kv:
+ *   s_t  = scale * q[s][h] . K_t,   t < T,   K_t = k_cache[block_tables[s][t/B]][h/g][t%B]
+ *   out[s][h] = sum_t exp(s_t - M) V_t / sum_t exp(s_t - M),  M = max_t s_t
+ * computed in fp32 and rounded to nearest-even in `dt`. T == 0 gives out = 0 ([PA-tutorial]
+ * §3.2 returns zeros when a sequence has no pages). Tail slots of the last block (t >= T) and
+ * blocks the table does not reach never influence the result, whatever they hold.
+ * Long contexts are split into partitions of partition_tokens tokens processed by separate
+ * workgroups; each writes its (max, sum, partial output) to `workspace` and the last one to
+ * finish for a (sequence, head group) merges them with the same log-sum-exp rescaling.
+ * max_context_len: a host-known upper bound on context_lens (sizes the grid; no device read).
+ * workspace: device buffer of >= pa_decode_workspace_size(...) bytes, 256-byte aligned, ZERO-
+ * FILLED before its first use; every call leaves its counter words zero again on completion,
+ * so one workspace is reused across calls that are ordered on one stream. Calls that overlap
+ * in time must not share a workspace.
+ */
+pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *block_tables, const int32_t *context_lens, float scale,
+                    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                    int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                    int max_context_len, int partition_tokens, void *workspace,
+                    size_t workspace_bytes, pa_dtype dt, void *stream);
+
+/*
+ * pa_copy_blocks — copy-on-write of shared blocks.
+ * [PA-summary] "Memory sharing: copy-on-write for parallel decoding": when a sequence must
+ * write into a block it shares with others, only that block is copied to a new physical block
+ * (and that sequence's table is repointed by the caller), as fork() does for pages.
+ * For each pair p < n_pairs: k_cache[dst] = k_cache[src] and v_cache[dst] = v_cache[src], the
+ * whole block (all KV heads, all block_size slots, including unused tail slots), bit-exact.
+ * Pairs with an id outside [0, num_blocks) are skipped. A dst that is also some pair's src, or
+ * a dst repeated, is a caller error (result unspecified). n_pairs == 0 is a valid no-op.
+ */
+pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *block_pairs, int n_pairs,
+                         int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                         pa_dtype dt, void *stream);
+
+/* Static, never-null description of a status code. */
+const char *pa_status_string(pa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,125 @@
+"""Host toy block manager that builds block tables, slot mappings and copy-on-write pairs.
+
+It follows the block manager the pages describe:
+  - [PA-summary] azimuth.plus, "Efficient Memory Management for Large Language Model Serving
+    with PagedAttention", sections "Key idea: virtual memory for the KV cache" (blocks are
+    allocated one at a time, on demand, as tokens are generated), "vLLM" (the block manager
+    keeps the free physical blocks and reference counts of shared blocks) and "Memory sharing:
+    copy-on-write" (a write into a shared block first copies that block only);
+  - [PA-tutorial] un.csdn.net, "PagedAttention实战：如何用Python手搓一个高效KV缓存管理器",
+    §2.2 BlockManager (a free list popped from the end; allocation fails when it is empty),
+    §3.1 append_kv (page = pos // page_size, offset = pos % page_size) and §5.1 clone_sequence
+    (a fork shares every page and raises its reference count).
+
+Reading where the pages leave the step open: when a shared block (reference count r > 1) is
+written, the writer copies it and the count drops by one; the last holder (r == 1) writes in
+place. The allocator is host logic for tests and benchmarks; the GPU library only consumes the
+tables, slots and pairs it produces.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+class PoolExhausted(MemoryError):
+    """No free physical block is left."""
+
+
+class BlockAllocator:
+    """Free list (LIFO) and reference counts over `num_blocks` physical blocks.
+
+    With `rng`, the free list is a seeded permutation of the block ids, so consecutive
+    allocations land at scattered physical positions."""
+
+    def __init__(self, num_blocks: int, rng: np.random.Generator | None = None):
+        if num_blocks < 0:
+            raise ValueError("num_blocks must be >= 0")
+        self.num_blocks = int(num_blocks)
+        order = np.arange(num_blocks) if rng is None else rng.permutation(num_blocks)
+        # pop() takes from the end: reverse so the first allocation is order[0].
+        self.free = [int(b) for b in order[::-1]]
+        self.ref = np.zeros(num_blocks, dtype=np.int64)
+
+    def allocate(self) -> int:
+        if not self.free:
+            raise PoolExhausted("no free physical blocks")
+        b = self.free.pop()
+        assert self.ref[b] == 0
+        self.ref[b] = 1
+        return b
+
+    def incref(self, b: int) -> None:
+        assert self.ref[b] > 0
+        self.ref[b] += 1
+
+    def decref(self, b: int) -> None:
+        assert self.ref[b] > 0
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            self.free.append(b)
+
+    @property
+    def num_free(self) -> int:
+        return len(self.free)
+
+
+@dataclass
+class Sequence:
+    """Logical-to-physical block map and current length of one sequence."""
+
+    block_size: int
+    table: list = field(default_factory=list)
+    length: int = 0
+
+
+def append_tokens(alloc: BlockAllocator, seq: Sequence, n: int):
+    """Reserve slots for `n` new tokens of `seq`.
+
+    Returns (slots, cow_pairs): slots[i] = phys*B + offset of token seq.length+i; cow_pairs are
+    (src, dst) whole-block copies that must run before the tokens are written."""
+    B = seq.block_size
+    slots, pairs = [], []
+    for _ in range(n):
+        pos = seq.length
+        j, off = divmod(pos, B)
+        if j == len(seq.table):
+            seq.table.append(alloc.allocate())
+        elif alloc.ref[seq.table[j]] > 1:
+            old = seq.table[j]
+            new = alloc.allocate()
+            pairs.append((old, new))
+            alloc.decref(old)
+            seq.table[j] = new
+        slots.append(seq.table[j] * B + off)
+        seq.length += 1
+    return slots, pairs
+
+
+def fork(alloc: BlockAllocator, seq: Sequence) -> Sequence:
+    """A child that shares every block of `seq` (reference counts raised)."""
+    for b in seq.table:
+        alloc.incref(b)
+    return Sequence(seq.block_size, list(seq.table), seq.length)
+
+
+def release(alloc: BlockAllocator, seq: Sequence) -> None:
+    for b in seq.table:
+        alloc.decref(b)
+    seq.table.clear()
+    seq.length = 0
+
+
+def block_tables_array(seqs, pad: int = -1, min_width: int = 1) -> np.ndarray:
+    """Dense int32 [S, max_blocks] table, unused entries set to `pad`."""
+    width = max([len(s.table) for s in seqs] + [min_width])
+    out = np.full((len(seqs), width), pad, dtype=np.int32)
+    for i, s in enumerate(seqs):
+        out[i, : len(s.table)] = s.table
+    return out
+
+
+def wasted_slots(seq: Sequence) -> int:
+    """Reserved-but-unused token slots of one sequence (internal fragmentation)."""
+    return len(seq.table) * seq.block_size - seq.length
