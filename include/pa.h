@@ -27,10 +27,11 @@
  * Query head h reads KV head h / (num_q_heads / num_kv_heads) (contiguous groups).
  *
  * Ownership and execution: every pointer except the return of pa_status_string is a DEVICE
- * pointer owned by the caller. The library allocates no memory and keeps no per-call state;
- * it reads the device's compute-unit count once. Each call validates its scalar arguments on the
- * host, enqueues its kernel(s) on `stream` (a hipStream_t; NULL = the null stream) and returns
- * without waiting for completion.
+ * pointer owned by the caller. The library allocates no memory and keeps no state between
+ * calls. Each call validates its scalar arguments and pointer alignment on the host, enqueues
+ * its kernel(s) on `stream` (a hipStream_t; NULL = the null stream) and returns without waiting
+ * for completion. q, k_cache, v_cache, k_new and v_new must be 16-byte aligned; the workspace
+ * 256-byte aligned; index arrays 4-byte aligned (PA_ERR_INVALID_ARG otherwise).
  *
  * Device-resident indices (block ids, slots, context lengths) are not validated on the host.
  * The kernels clamp them into the buffers the sizes describe, so a bad index gives an undefined
@@ -88,8 +89,9 @@ pa_status pa_write_kv(void *k_cache, void *v_cache, const void *k_new, const voi
  * The workspace holds per-partition partial results (running max, running sum and partial
  * output, fp32) plus one int32 arrival counter per (sequence, query-head group).
  * partition_tokens: 0 = let the library choose (the same choice pa_decode makes for the same
- * arguments); > 0 must be a multiple of 2*block_size.
- * Returns 0 for invalid sizes.
+ * arguments); > 0 must be a multiple of 32.
+ * Returns 0 when no workspace is needed (every sequence fits one partition) and for invalid
+ * sizes.
  */
 size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                 int block_size, int max_context_len, int partition_tokens,

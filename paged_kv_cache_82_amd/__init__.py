@@ -1,0 +1,11 @@
+"""Paged KV-cache decode attention for AMD MI355X (gfx950).
+
+The compute lives in libpa.so (hand-written HIP kernels behind the C ABI in include/pa.h);
+this package is its thin Python binding. Importing it never falls back to any other code
+path: if the library is missing, calls raise.
+"""
+from ._binding import (PAError, lib_path, load, pa_copy_blocks, pa_decode,
+                       pa_decode_workspace_size, pa_status_string, pa_write_kv)
+
+__all__ = ["PAError", "lib_path", "load", "pa_copy_blocks", "pa_decode",
+           "pa_decode_workspace_size", "pa_status_string", "pa_write_kv"]

@@ -1,0 +1,127 @@
+"""ctypes binding of libpa.so (C ABI in include/pa.h): argument marshalling only.
+
+Functions take torch tensors that live on the GPU (PyTorch provides device memory and the
+stream) and pass their data pointers, sizes and the current HIP stream to the library; every
+step of the computation runs in the library's kernels. A missing library raises: there is no
+other implementation to fall back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(PKG, "libpa.so")
+_lock = threading.Lock()
+_lib = None
+
+PA_OK = 0
+_DTYPE_NAMES = {"float32": 0, "float16": 1, "bfloat16": 2}
+
+
+class PAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: status {status} ({pa_status_string(status)})")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libpa.so (once). Raises FileNotFoundError if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        p = path or _LIB_PATH
+        if not os.path.exists(p):
+            raise FileNotFoundError(
+                f"{p} is missing: build it first (python -m paged_kv_cache_82_amd.build)")
+        lib = ctypes.CDLL(p)
+        P, I, I64, F, SZ = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                            ctypes.c_size_t)
+        lib.pa_write_kv.argtypes = [P, P, P, P, P, I, I, I, I, I64, I, P]
+        lib.pa_write_kv.restype = I
+        lib.pa_decode_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
+        lib.pa_decode_workspace_size.restype = SZ
+        lib.pa_decode.argtypes = [P, P, P, P, P, P, F, I, I, I, I, I, I, I64, I, I, P, SZ, I, P]
+        lib.pa_decode.restype = I
+        lib.pa_copy_blocks.argtypes = [P, P, P, I, I, I, I, I64, I, P]
+        lib.pa_copy_blocks.restype = I
+        lib.pa_status_string.argtypes = [I]
+        lib.pa_status_string.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def pa_status_string(status: int) -> str:
+    try:
+        return load().pa_status_string(int(status)).decode()
+    except FileNotFoundError:
+        return "library not loaded"
+
+
+def _dtype_code(t) -> int:
+    name = str(t.dtype).replace("torch.", "")
+    if name not in _DTYPE_NAMES:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DTYPE_NAMES[name]
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _check(fn: str, status: int) -> None:
+    if status != PA_OK:
+        raise PAError(fn, status)
+
+
+def pa_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None) -> None:
+    """k_cache/v_cache [N, Hkv, B, d]; k_new/v_new [n, Hkv, d]; slot_mapping int32 [n]."""
+    N, Hkv, B, d = k_cache.shape
+    n = slot_mapping.shape[0]
+    _check("pa_write_kv", load().pa_write_kv(
+        _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), n, Hkv, d,
+        B, N, _dtype_code(k_cache), _stream(stream)))
+
+
+def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                             max_context_len, partition_tokens, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _DTYPE_NAMES[str(dtype).replace("torch.", "")]
+    return int(load().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                               block_size, max_context_len, partition_tokens,
+                                               code))
+
+
+def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+              workspace=None, partition_tokens=0, stream=None) -> None:
+    """out, q [S, Hq, d]; pools [N, Hkv, B, d]; block_tables int32 [S, M]; context_lens int32
+    [S]; workspace: a zero-initialised uint8 tensor of >= pa_decode_workspace_size bytes."""
+    S, Hq, d = q.shape
+    N, Hkv, B, _ = k_cache.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pa_decode", load().pa_decode(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), float(scale), S, Hq, Hkv, d, B, block_tables.shape[1], N,
+        int(max_context_len), int(partition_tokens), _ptr(workspace), ws_bytes,
+        _dtype_code(q), _stream(stream)))
+
+
+def pa_copy_blocks(k_cache, v_cache, block_pairs, stream=None) -> None:
+    """block_pairs int32 [n, 2] of (src, dst) physical block ids."""
+    N, Hkv, B, d = k_cache.shape
+    _check("pa_copy_blocks", load().pa_copy_blocks(
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_pairs), block_pairs.shape[0], Hkv, d, B, N,
+        _dtype_code(k_cache), _stream(stream)))

@@ -1,0 +1,192 @@
+// pa_api.hip — the C ABI of libpa (declared in include/pa.h): argument checks, path and
+// partition choice, and kernel launches on the caller's stream. No allocation, no host sync.
+#include <stdlib.h>
+#include <string.h>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+using pa::DecodePath;
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int elem_bytes(pa_dtype dt) { return dt == PA_F32 ? 4 : 2; }
+
+bool valid_dtype(pa_dtype dt) { return dt == PA_F32 || dt == PA_F16 || dt == PA_BF16; }
+
+// Pool element count num_blocks * heads * B * d, or -1 on overflow of int64.
+int64_t pool_elems(int64_t num_blocks, int heads, int block_size, int head_dim) {
+  const int64_t per_block = (int64_t)heads * block_size * head_dim;
+  if (per_block <= 0 || num_blocks < 0) return -1;
+  if (num_blocks > INT64_MAX / 4 / per_block) return -1;
+  return num_blocks * per_block;
+}
+
+// Kernel path: grouped-query MFMA kernel for 16-bit inputs with at least two query heads per
+// KV head, the VALU kernel otherwise. PA_DECODE_PATH=valu|mfma overrides (tests use it to
+// exercise both kernels on one input).
+bool choose_path(pa_dtype dt, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                 DecodePath* path) {
+  const int g = num_q_heads / num_kv_heads;
+  DecodePath p = (dt != PA_F32 && g >= 2) ? DecodePath::Mfma : DecodePath::Valu;
+  if (const char* env = getenv("PA_DECODE_PATH")) {
+    if (strcmp(env, "valu") == 0) p = DecodePath::Valu;
+    else if (strcmp(env, "mfma") == 0) p = DecodePath::Mfma;
+  }
+  *path = p;
+  return pa::decode_supported(p, (int)dt, head_dim, block_size);
+}
+
+// Tokens per partition. A workgroup covers P tokens of one (sequence, head unit); long
+// contexts are split so the grid has enough workgroups to fill 256 compute units several
+// times over and no single workgroup carries a long tail. 0 = automatic.
+int choose_partition(int num_seqs, int units_per_seq, int max_context_len, int requested) {
+  if (requested > 0) return requested;
+  int P = 512;
+  const int64_t units = (int64_t)num_seqs * units_per_seq;
+  // expected workgroups if lengths average half the maximum
+  int64_t est = units * (max_context_len / (2 * P) > 1 ? max_context_len / (2 * P) : 1);
+  while (est < 2048 && P > 128) {
+    P /= 2;
+    est *= 2;
+  }
+  return P;
+}
+
+int parts_for(int max_context_len, int P) {
+  const int n = (max_context_len + P - 1) / P;
+  return n > 1 ? n : 1;
+}
+
+pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported dtype/head_dim/block_size combination";
+    case PA_ERR_WORKSPACE: return "workspace too small";
+    case PA_ERR_HIP: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+pa_status pa_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                      const int32_t* slot_mapping, int n_tokens, int num_kv_heads, int head_dim,
+                      int block_size, int64_t num_blocks, pa_dtype dt, void* stream) {
+  if (!valid_dtype(dt)) return PA_ERR_INVALID_ARG;
+  if (n_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (pool_elems(num_blocks, num_kv_heads, block_size, head_dim) < 0) return PA_ERR_INVALID_ARG;
+  if ((int64_t)n_tokens * num_kv_heads * head_dim > INT64_MAX / 8) return PA_ERR_INVALID_ARG;
+  const int row_bytes = head_dim * elem_bytes(dt);
+  if (row_bytes % 16) return PA_ERR_UNSUPPORTED;
+  if (n_tokens == 0) return PA_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping) return PA_ERR_INVALID_ARG;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_new, 16) ||
+      !aligned(v_new, 16) || !aligned(slot_mapping, 4))
+    return PA_ERR_INVALID_ARG;
+  return from_hip(pa::launch_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, n_tokens,
+                                      num_kv_heads, row_bytes, block_size, num_blocks,
+                                      (hipStream_t)stream));
+}
+
+size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                int block_size, int max_context_len, int partition_tokens,
+                                pa_dtype dt) {
+  if (!valid_dtype(dt) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads || head_dim <= 0 || block_size <= 0 || max_context_len < 0 ||
+      partition_tokens < 0 || partition_tokens % 32)
+    return 0;
+  DecodePath path;
+  if (!choose_path(dt, num_q_heads, num_kv_heads, head_dim, block_size, &path)) return 0;
+  const int P = choose_partition(num_seqs,
+                                 pa::decode_units_per_seq(path, num_q_heads, num_kv_heads),
+                                 max_context_len, partition_tokens);
+  return pa::workspace_layout(num_seqs, num_q_heads, head_dim, parts_for(max_context_len, P))
+      .total;
+}
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, float scale,
+                    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                    int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                    int max_context_len, int partition_tokens, void* workspace,
+                    size_t workspace_bytes, pa_dtype dt, void* stream) {
+  if (!valid_dtype(dt)) return PA_ERR_INVALID_ARG;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || max_blocks_per_seq < 0 || num_blocks <= 0 || max_context_len < 0 ||
+      partition_tokens < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads) return PA_ERR_INVALID_ARG;
+  if (partition_tokens % 32) return PA_ERR_INVALID_ARG;
+  if (pool_elems(num_blocks, num_kv_heads, block_size, head_dim) < 0) return PA_ERR_INVALID_ARG;
+  if (num_seqs > 65535 || num_q_heads > 65535) return PA_ERR_INVALID_ARG;  // grid limits
+  DecodePath path;
+  if (!choose_path(dt, num_q_heads, num_kv_heads, head_dim, block_size, &path))
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(out, elem_bytes(dt)) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return PA_ERR_INVALID_ARG;
+
+  const int P = choose_partition(num_seqs,
+                                 pa::decode_units_per_seq(path, num_q_heads, num_kv_heads),
+                                 max_context_len, partition_tokens);
+  const int max_parts = parts_for(max_context_len, P);
+  const pa::WorkspaceLayout L =
+      pa::workspace_layout(num_seqs, num_q_heads, head_dim, max_parts);
+  if (workspace_bytes < L.total || (L.total > 0 && !workspace)) return PA_ERR_WORKSPACE;
+  if (L.total > 0 && !aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
+
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.partition_tokens = P;
+  a.max_parts = max_parts;
+  char* ws = (char*)workspace;
+  a.part_m = L.total ? (float*)(ws + L.m_off) : nullptr;
+  a.part_l = L.total ? (float*)(ws + L.l_off) : nullptr;
+  a.part_o = L.total ? (float*)(ws + L.o_off) : nullptr;
+  a.counters = L.total ? (int*)(ws + L.cnt_off) : nullptr;
+  return from_hip(pa::launch_decode(path, (int)dt, head_dim, block_size, a, (hipStream_t)stream));
+}
+
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int n_pairs,
+                         int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                         pa_dtype dt, void* stream) {
+  if (!valid_dtype(dt)) return PA_ERR_INVALID_ARG;
+  if (n_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (pool_elems(num_blocks, num_kv_heads, block_size, head_dim) < 0) return PA_ERR_INVALID_ARG;
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elem_bytes(dt);
+  if (block_bytes % 16) return PA_ERR_UNSUPPORTED;
+  if (n_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_pairs) return PA_ERR_INVALID_ARG;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_pairs, 4))
+    return PA_ERR_INVALID_ARG;
+  return from_hip(pa::launch_copy_blocks(k_cache, v_cache, block_pairs, n_pairs, block_bytes,
+                                         num_blocks, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,586 @@
+// pa_decode.hip — paged decode attention kernels for gfx950 (CDNA4, wave64).
+//
+// Method: [PA-summary] azimuth.plus, "Efficient Memory Management for Large Language Model
+// Serving with PagedAttention", section "The PagedAttention algorithm" and its block-wise
+// attention equation: for each query vector the kernel walks the block table, fetches the
+// keys and values of each logical block from wherever its physical block sits, scores the
+// block's tokens, and folds them into a running (maximum, sum, output) state with the
+// log-sum-exp rescaling; the result equals standard softmax attention. The last block of a
+// sequence contributes only its valid tokens (B_j in the equation).
+//
+// Work decomposition (not on the pages; chosen for MI355X):
+//   - a workgroup of NW waves owns one (sequence, head unit, partition of P tokens);
+//     waves take blocks (VALU path) or 32-token steps (MFMA path) of the partition in turn;
+//   - every wave keeps its own running state; states are merged across lanes, then across
+//     waves through LDS, with the same rescaling as the equation;
+//   - when a sequence needs more than one partition, each workgroup stores its partial
+//     (max, sum, unnormalised output) and bumps an arrival counter; the last arrival merges
+//     all partials (split-K with the merge fused into the same launch, no spin-waits).
+// Scores are kept in the base-2 exponent domain: s' = s * log2(e), exp(s - m) = 2^(s' - m').
+//
+// Two kernels:
+//   decode_valu_kernel: one query head per workgroup; 16-byte coalesced loads, q.K on the
+//     vector ALU with a DPP all-reduce across the lanes of a token row; p.V accumulated per
+//     lane. Used for single-head groups (MHA) and for fp32.
+//   decode_mfma_kernel: one KV head and up to 16 query heads per workgroup (grouped-query
+//     attention); each K/V tile is read once for all heads of the group and both products run
+//     on 16x16x32 MFMA: S^T = K Q^T (tokens x heads) and O^T += V^T P^T (dims x heads).
+//     V is read with 16-byte row loads; the transposition the p.V product needs is absorbed by
+//     pairing M-tile row r with head dimension (D/16)*r + mt, so no LDS staging is needed.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+// ---- shared pieces ----------------------------------------------------------------------
+
+// Context length of sequence s, clamped into what the table and grid can address.
+__device__ __forceinline__ int seq_len(const DecodeArgs& a, int s, int BS) {
+  int T = a.context_lens[s];
+  const int64_t cap64 = (int64_t)a.max_blocks_per_seq * BS;
+  const int cap = (int)(cap64 < (int64_t)a.max_context_len ? cap64 : (int64_t)a.max_context_len);
+  return T < 0 ? 0 : (T > cap ? cap : T);
+}
+
+__device__ __forceinline__ int64_t clamp_block(int32_t phys, int64_t n) {
+  return phys < 0 ? 0 : (phys >= n ? n - 1 : (int64_t)phys);
+}
+
+// After a workgroup has merged its partition into (fm, fl, fo[nh][D]) in LDS: either store the
+// final output (single partition) or store the partial and, if this workgroup is the last of
+// its (sequence, head unit) to arrive, merge every partition's partial into the output.
+template <DT dt, int D, int NT>
+__device__ void finish_partition(const DecodeArgs& a, int s, int h0, int nh, int p, int nparts,
+                                 const float* fm, const float* fl, const float* fo,
+                                 int* lds_flag) {
+  const int tid = threadIdx.x;
+  const int Hq = a.num_q_heads;
+  if (nparts == 1) {
+    for (int idx = tid; idx < nh * D; idx += NT) {
+      const int hh = idx / D, dim = idx % D;
+      store_elem<dt>(a.out, ((int64_t)s * Hq + h0 + hh) * D + dim, fo[idx] / fl[hh]);
+    }
+    return;
+  }
+  const int MP = a.max_parts;
+  for (int idx = tid; idx < nh * D; idx += NT) {
+    const int hh = idx / D, dim = idx % D;
+    a.part_o[(((int64_t)s * Hq + h0 + hh) * MP + p) * D + dim] = fo[idx];
+  }
+  if (tid < nh) {
+    a.part_m[((int64_t)s * Hq + h0 + tid) * MP + p] = fm[tid];
+    a.part_l[((int64_t)s * Hq + h0 + tid) * MP + p] = fl[tid];
+  }
+  __threadfence();  // release this workgroup's partial to the whole device
+  __syncthreads();
+  if (tid == 0) {
+    const int prev = atomicAdd(&a.counters[(int64_t)s * Hq + h0], 1);
+    *lds_flag = (prev == nparts - 1);
+  }
+  __syncthreads();
+  if (!*lds_flag) return;
+  __threadfence();  // acquire the other workgroups' partials
+  for (int idx = tid; idx < nh * D; idx += NT) {
+    const int hh = idx / D, dim = idx % D;
+    const int64_t base = ((int64_t)s * Hq + h0 + hh) * MP;
+    float M = kNegInf;
+    for (int pp = 0; pp < nparts; ++pp) M = fmaxf(M, a.part_m[base + pp]);
+    float acc = 0.0f, L = 0.0f;
+    for (int pp = 0; pp < nparts; ++pp) {
+      const float wgt = rescale(a.part_m[base + pp], M);
+      acc = fmaf(wgt, a.part_o[(base + pp) * D + dim], acc);
+      L = fmaf(wgt, a.part_l[base + pp], L);
+    }
+    store_elem<dt>(a.out, ((int64_t)s * Hq + h0 + hh) * D + dim, acc / L);
+  }
+  if (tid == 0) a.counters[(int64_t)s * Hq + h0] = 0;  // ready for the next call
+}
+
+template <DT dt, int D, int NT>
+__device__ void store_zeros(const DecodeArgs& a, int s, int h0, int nh) {
+  for (int idx = threadIdx.x; idx < nh * D; idx += NT)
+    store_elem<dt>(a.out, ((int64_t)s * a.num_q_heads + h0) * D + idx, 0.0f);
+}
+
+// ---- VALU kernel ------------------------------------------------------------------------
+
+template <DT dt, int D, int BS, int NW>
+struct ValuCfg {
+  static constexpr int E = Elem<dt>::bytes;
+  static constexpr int VEC = 16 / E;    // elements per 16-byte chunk
+  static constexpr int R = D / VEC;     // lanes that share one token row
+  static constexpr int TPI = 64 / R;    // token rows covered by one wave-wide load
+  static constexpr int NL = BS / TPI;   // loads per block per tensor
+  static constexpr int NT = NW * 64;
+  static_assert(64 % R == 0 && R >= 1, "row must split evenly over the wave");
+  static_assert(BS % TPI == 0, "block must cover whole wave loads");
+  static_assert(D <= NT, "one thread per head dimension in the merge");
+};
+
+// One block of one wave: scores, running-state update and p.V accumulation. Lane (c, r) holds
+// head dimensions c*VEC.. of token rows i*TPI + r. TAIL masks tokens at or beyond t_end.
+template <DT dt, int D, int BS, int NW, bool TAIL>
+__device__ __forceinline__ void valu_block(const float (&qf)[ValuCfg<dt, D, BS, NW>::VEC],
+                                           const u32x4* kr, const u32x4* vr, int tok0,
+                                           int t_end, int r, float& m, float& l,
+                                           float (&o)[ValuCfg<dt, D, BS, NW>::VEC]) {
+  using C = ValuCfg<dt, D, BS, NW>;
+  float sc[C::NL];
+#pragma unroll
+  for (int i = 0; i < C::NL; ++i) {
+    const uint32_t w[4] = {kr[i][0], kr[i][1], kr[i][2], kr[i][3]};
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < C::VEC; ++e) acc = fmaf(qf[e], elem_of<dt>(w, e), acc);
+    sc[i] = group_sum<C::R>(acc);
+    if (TAIL && tok0 + i * C::TPI + r >= t_end) sc[i] = kNegInf;
+  }
+  float bm = sc[0];
+#pragma unroll
+  for (int i = 1; i < C::NL; ++i) bm = fmaxf(bm, sc[i]);
+  const float mn = fmaxf(m, bm);
+  const bool empty = (mn == kNegInf);  // no valid token seen yet by this lane row
+  const float corr = empty ? 1.0f : fast_exp2(m - mn);
+  float ps = 0.0f;
+  float pr[C::NL];
+#pragma unroll
+  for (int i = 0; i < C::NL; ++i) {
+    pr[i] = empty ? 0.0f : fast_exp2(sc[i] - mn);
+    ps += pr[i];
+  }
+  l = fmaf(l, corr, ps);
+#pragma unroll
+  for (int e = 0; e < C::VEC; ++e) o[e] *= corr;
+#pragma unroll
+  for (int i = 0; i < C::NL; ++i) {
+    const uint32_t w[4] = {vr[i][0], vr[i][1], vr[i][2], vr[i][3]};
+    const bool ok = !TAIL || (tok0 + i * C::TPI + r < t_end);
+#pragma unroll
+    for (int e = 0; e < C::VEC; ++e) {
+      float v = elem_of<dt>(w, e);
+      if (TAIL) v = ok ? v : 0.0f;  // select, never multiply: tail slots may hold NaN
+      o[e] = fmaf(pr[i], v, o[e]);
+    }
+  }
+  m = mn;
+}
+
+template <DT dt, int D, int BS, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a) {
+  using C = ValuCfg<dt, D, BS, NW>;
+  constexpr int E = C::E, VEC = C::VEC, R = C::R, TPI = C::TPI, NL = C::NL, NT = C::NT;
+  __shared__ float lds_o[NW][D];
+  __shared__ float lds_m[NW], lds_l[NW];
+  __shared__ float lds_fm[1], lds_fl[1];
+  __shared__ int lds_flag;
+
+  const int p = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int T = seq_len(a, s, BS);
+  const int P = a.partition_tokens;
+  const int nparts = (T + P - 1) / P;
+  if (T == 0) {
+    if (p == 0) store_zeros<dt, D, NT>(a, s, h, 1);
+    return;
+  }
+  if (p >= nparts) return;
+  const int kvh = h / (a.num_q_heads / a.num_kv_heads);
+  const int t0 = p * P;
+  const int t1 = (T < t0 + P) ? T : t0 + P;
+  const int jb0 = t0 / BS, jb1 = (t1 + BS - 1) / BS;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane % R, r = lane / R;
+
+  float qf[VEC];
+  {
+    const char* qp =
+        (const char*)a.q + (((int64_t)s * a.num_q_heads + h) * D + c * VEC) * E;
+    const u32x4 raw = load16(qp);
+    const uint32_t wq[4] = {raw[0], raw[1], raw[2], raw[3]};
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) qf[e] = elem_of<dt>(wq, e) * a.scale_log2;
+  }
+
+  float m = kNegInf, l = 0.0f;
+  float o[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) o[e] = 0.0f;
+
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const char* kbase = (const char*)a.k_cache;
+  const char* vbase = (const char*)a.v_cache;
+  constexpr int64_t row_bytes = (int64_t)D * E;
+  for (int j = jb0 + w; j < jb1; j += NW) {
+    const int64_t phys = clamp_block(bt[j], a.num_blocks);
+    const int64_t tile = (phys * a.num_kv_heads + kvh) * BS * row_bytes;
+    u32x4 kr[NL], vr[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int64_t off = tile + (int64_t)(i * TPI + r) * row_bytes + c * 16;
+      kr[i] = load16(kbase + off);
+      vr[i] = load16(vbase + off);
+    }
+    const int tok0 = j * BS;
+    if (tok0 + BS <= t1)
+      valu_block<dt, D, BS, NW, false>(qf, kr, vr, tok0, t1, r, m, l, o);
+    else
+      valu_block<dt, D, BS, NW, true>(qf, kr, vr, tok0, t1, r, m, l, o);
+  }
+
+  // Merge the TPI row states of this wave (lanes with equal c), then the waves.
+#pragma unroll
+  for (int off = R; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(m, off);
+    const float l2 = __shfl_xor(l, off);
+    const float M = fmaxf(m, m2);
+    const float wa = rescale(m, M), wb = rescale(m2, M);
+    l = wa * l + wb * l2;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) o[e] = wa * o[e] + wb * __shfl_xor(o[e], off);
+    m = M;
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) lds_o[w][c * VEC + e] = o[e];
+  }
+  if (lane == 0) {
+    lds_m[w] = m;
+    lds_l[w] = l;
+  }
+  __syncthreads();
+  float* fo = &lds_o[0][0];  // merged output reuses wave 0's row (read-before-write per thread)
+  if (threadIdx.x < D) {
+    const int dim = threadIdx.x;
+    float M = kNegInf;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) M = fmaxf(M, lds_m[k]);
+    float acc = 0.0f, L = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const float wgt = rescale(lds_m[k], M);
+      acc = fmaf(wgt, lds_o[k][dim], acc);
+      L = fmaf(wgt, lds_l[k], L);
+    }
+    fo[dim] = acc;
+    if (dim == 0) {
+      lds_fm[0] = M;
+      lds_fl[0] = L;
+    }
+  }
+  __syncthreads();
+  finish_partition<dt, D, NT>(a, s, h, 1, p, nparts, lds_fm, lds_fl, fo, &lds_flag);
+}
+
+// ---- MFMA kernel (grouped query heads) -----------------------------------------------------
+
+template <DT dt>
+struct MfmaT;
+template <>
+struct MfmaT<DT::BF16> {
+  using vec8 = bf16x8;
+  using scalar = __bf16;
+  static __device__ __forceinline__ f32x4 mma(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct MfmaT<DT::F16> {
+  using vec8 = f16x8;
+  using scalar = _Float16;
+  static __device__ __forceinline__ f32x4 mma(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// V row fragment of one token: D/16 consecutive head dimensions (16 bytes for D = 128,
+// 8 bytes for D = 64).
+template <int D>
+struct VFrag;
+template <>
+struct VFrag<128> {
+  using T = u32x4;
+  static constexpr int words = 4;
+  static __device__ __forceinline__ T load(const char* p) { return load16(p); }
+};
+template <>
+struct VFrag<64> {
+  using T = u32x2;
+  static constexpr int words = 2;
+  static __device__ __forceinline__ T load(const char* p) { return load8(p); }
+};
+
+// 16-bit element `e` of a V fragment, as raw bits in the low half.
+template <int D>
+__device__ __forceinline__ uint32_t vfrag_elem(const typename VFrag<D>::T& f, int e) {
+  const uint32_t w = f[e >> 1];
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+template <DT dt, int D, int BS, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a) {
+  static_assert(dt != DT::F32, "MFMA path takes 16-bit inputs");
+  static_assert(BS <= 32 && 32 % BS == 0, "a 32-token step spans whole blocks");
+  using M = MfmaT<dt>;
+  using vec8 = typename M::vec8;
+  using VF = VFrag<D>;
+  constexpr int E = 2;
+  constexpr int KC = D / 32;  // q.K MFMAs per 16-token tile
+  constexpr int MT = D / 16;  // p.V M-tiles; row r of tile mt is head dimension MT*r + mt
+  constexpr int NBS = 32 / BS;
+  constexpr int NT = NW * 64;
+  __shared__ float lds_o[NW][16][D];
+  __shared__ float lds_m[NW][16], lds_l[NW][16];
+  __shared__ float lds_fm[16], lds_fl[16];
+  __shared__ int lds_flag;
+
+  const int p = blockIdx.x, unit = blockIdx.y, s = blockIdx.z;
+  const int Hq = a.num_q_heads;
+  const int g = Hq / a.num_kv_heads;
+  const int ntile = (g + 15) / 16;
+  const int kvh = unit / ntile, ht = unit % ntile;
+  const int h0 = kvh * g + ht * 16;
+  const int nh = (g - ht * 16 < 16) ? g - ht * 16 : 16;
+  const int T = seq_len(a, s, BS);
+  const int P = a.partition_tokens;
+  const int nparts = (T + P - 1) / P;
+  if (T == 0) {
+    if (p == 0) store_zeros<dt, D, NT>(a, s, h0, nh);
+    return;
+  }
+  if (p >= nparts) return;
+  const int t0 = p * P;
+  const int t1 = (T < t0 + P) ? T : t0 + P;
+  const int st0 = t0 / 32, st1 = (t1 + 31) / 32;
+  const int jlast = (t1 - 1) / BS;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int hh = lane & 15, gq = lane >> 4;
+
+  // Q^T operand: column hh = query head h0 + hh, k = head dims 32*kk + 8*gq + e.
+  vec8 qop[KC];
+#pragma unroll
+  for (int kk = 0; kk < KC; ++kk) {
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (hh < nh)
+      raw = load16((const char*)a.q +
+                   (((int64_t)s * Hq + h0 + hh) * D + 32 * kk + 8 * gq) * E);
+    qop[kk] = __builtin_bit_cast(vec8, raw);
+  }
+
+  f32x4 oacc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf, lsum = 0.0f;
+
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const char* kbase = (const char*)a.k_cache;
+  const char* vbase = (const char*)a.v_cache;
+  const int64_t Hkv = a.num_kv_heads;
+
+  for (int st = st0 + w; st < st1; st += NW) {
+    const int tau0 = st * 32;
+    int64_t ph[NBS];
+#pragma unroll
+    for (int b = 0; b < NBS; ++b) {
+      int j = tau0 / BS + b;
+      j = (j < jlast) ? j : jlast;  // never read the table past this partition's last block
+      ph[b] = clamp_block(bt[j], a.num_blocks);
+    }
+    // K operand of tile u: row hh = token tau0 + 16u + hh, k = dims 32*kk + 8*gq + e.
+    u32x4 kreg[2][KC];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tk = 16 * u + hh;
+      const int64_t row = (ph[tk / BS] * Hkv + kvh) * BS + (tk % BS);
+      const char* rp = kbase + row * D * E + 8 * gq * E;
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk) kreg[u][kk] = load16(rp + 32 * kk * E);
+    }
+    // V rows of tokens 16u + 4*gq + i (i < 4): head dims MT*hh .. MT*hh + MT - 1.
+    typename VF::T vreg[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tk = 16 * u + 4 * gq + i;
+        const int64_t row = (ph[tk / BS] * Hkv + kvh) * BS + (tk % BS);
+        vreg[u][i] = VF::load(vbase + (row * D + MT * hh) * E);
+      }
+
+    // S^T = K Q^T: sacc[u][i] = score of token tau0 + 16u + 4*gq + i for head hh.
+    f32x4 sacc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      sacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk)
+        sacc[u] = M::mma(__builtin_bit_cast(vec8, kreg[u][kk]), qop[kk], sacc[u]);
+    }
+    const bool tail = tau0 + 32 > t1;
+    float sc[8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = sacc[u][i] * a.scale_log2;
+        if (tail && tau0 + 16 * u + 4 * gq + i >= t1) x = kNegInf;
+        sc[4 * u + i] = x;
+      }
+    float bm = sc[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sc[e]);
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mn = fmaxf(m, bm);
+    const bool empty = (mn == kNegInf);
+    const float corr = empty ? 1.0f : fast_exp2(m - mn);
+    vec8 pop;
+    float ps = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pe = empty ? 0.0f : fast_exp2(sc[e] - mn);
+      ps += pe;
+      pop[e] = (typename M::scalar)pe;
+    }
+    lsum = fmaf(lsum, corr, ps);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) oacc[mt] *= corr;
+    if (tail) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (tau0 + 16 * u + 4 * gq + i >= t1) vreg[u][i] = typename VF::T{};  // select
+    }
+    // O^T += V^T P^T with k element e <-> token 16*(e/4) + 4*gq + (e%4).
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      u32x4 vw;
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        const int e0 = 2 * q2, e1 = 2 * q2 + 1;
+        const uint32_t lo = vfrag_elem<D>(vreg[e0 / 4][e0 % 4], mt);
+        const uint32_t hi = vfrag_elem<D>(vreg[e1 / 4][e1 % 4], mt);
+        vw[q2] = lo | (hi << 16);
+      }
+      oacc[mt] = M::mma(__builtin_bit_cast(vec8, vw), pop, oacc[mt]);
+    }
+    m = mn;
+  }
+
+  // Sum the per-lane partial sums over the four lane groups of each head.
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  // oacc[mt][i] is O[head hh][dim MT*(4*gq + i) + mt].
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_o[w][hh][MT * (4 * gq + i) + mt] = oacc[mt][i];
+  if (gq == 0) {
+    lds_m[w][hh] = m;
+    lds_l[w][hh] = lsum;
+  }
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    const int k = threadIdx.x;
+    float Mx = kNegInf;
+#pragma unroll
+    for (int x = 0; x < NW; ++x) Mx = fmaxf(Mx, lds_m[x][k]);
+    float L = 0.0f;
+#pragma unroll
+    for (int x = 0; x < NW; ++x) L = fmaf(rescale(lds_m[x][k], Mx), lds_l[x][k], L);
+    lds_fm[k] = Mx;
+    lds_fl[k] = L;
+  }
+  float* fo = &lds_o[0][0][0];  // merged output reuses wave 0's slab (read-before-write)
+  for (int idx = threadIdx.x; idx < 16 * D; idx += NT) {
+    const int k = idx / D, dim = idx % D;
+    float Mx = kNegInf;
+#pragma unroll
+    for (int x = 0; x < NW; ++x) Mx = fmaxf(Mx, lds_m[x][k]);
+    float acc = 0.0f;
+#pragma unroll
+    for (int x = 0; x < NW; ++x) acc = fmaf(rescale(lds_m[x][k], Mx), lds_o[x][k][dim], acc);
+    fo[idx] = acc;
+  }
+  __syncthreads();
+  finish_partition<dt, D, NT>(a, s, h0, nh, p, nparts, lds_fm, lds_fl, fo, &lds_flag);
+}
+
+// ---- host launchers -----------------------------------------------------------------------
+
+constexpr int kWaves = 4;
+
+WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_parts) {
+  WorkspaceLayout L{};
+  if (max_parts <= 1 || num_seqs <= 0) return L;  // a single partition needs no workspace
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t sh = (size_t)num_seqs * num_q_heads;
+  L.m_off = 0;
+  L.l_off = up(L.m_off + sh * max_parts * sizeof(float));
+  L.o_off = up(L.l_off + sh * max_parts * sizeof(float));
+  L.cnt_off = up(L.o_off + sh * max_parts * (size_t)head_dim * sizeof(float));
+  L.total = up(L.cnt_off + sh * sizeof(int));
+  return L;
+}
+
+int decode_units_per_seq(DecodePath path, int num_q_heads, int num_kv_heads) {
+  if (path == DecodePath::Valu) return num_q_heads;
+  const int g = num_q_heads / num_kv_heads;
+  return num_kv_heads * ((g + 15) / 16);
+}
+
+template <DT dt, int D, int BS>
+static hipError_t launch_t(DecodePath path, const DecodeArgs& a, hipStream_t stream) {
+  const dim3 block(kWaves * 64);
+  const dim3 grid((unsigned)a.max_parts,
+                  (unsigned)decode_units_per_seq(path, a.num_q_heads, a.num_kv_heads),
+                  (unsigned)a.num_seqs);
+  if (path == DecodePath::Mfma) {
+    if constexpr (dt != DT::F32) {
+      hipLaunchKernelGGL((decode_mfma_kernel<dt, D, BS, kWaves>), grid, block, 0, stream, a);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL((decode_valu_kernel<dt, D, BS, kWaves>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+template <DT dt, int D>
+static hipError_t launch_bs(DecodePath path, int bs, const DecodeArgs& a, hipStream_t st) {
+  switch (bs) {
+    case 8: return launch_t<dt, D, 8>(path, a, st);
+    case 16: return launch_t<dt, D, 16>(path, a, st);
+    case 32: return launch_t<dt, D, 32>(path, a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <DT dt>
+static hipError_t launch_d(DecodePath path, int d, int bs, const DecodeArgs& a, hipStream_t st) {
+  switch (d) {
+    case 64: return launch_bs<dt, 64>(path, bs, a, st);
+    case 128: return launch_bs<dt, 128>(path, bs, a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+bool decode_supported(DecodePath path, int dt, int head_dim, int block_size) {
+  if (dt < 0 || dt > 2) return false;
+  if (head_dim != 64 && head_dim != 128) return false;
+  if (block_size != 8 && block_size != 16 && block_size != 32) return false;
+  if (path == DecodePath::Mfma && dt == 0) return false;
+  return true;
+}
+
+hipError_t launch_decode(DecodePath path, int dt, int head_dim, int block_size,
+                         const DecodeArgs& a, hipStream_t stream) {
+  if (a.num_seqs == 0) return hipSuccess;
+  switch (dt) {
+    case 0: return launch_d<DT::F32>(path, head_dim, block_size, a, stream);
+    case 1: return launch_d<DT::F16>(path, head_dim, block_size, a, stream);
+    case 2: return launch_d<DT::BF16>(path, head_dim, block_size, a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

@@ -1,0 +1,115 @@
+// pa_device.h — device-side helpers shared by the libpa kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+enum class DT : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+template <DT dt>
+struct Elem {
+  static constexpr int bytes = (dt == DT::F32) ? 4 : 2;
+};
+
+constexpr float kLog2e = 1.4426950408889634f;  // log2(e): exp(x) = exp2(x * log2(e))
+constexpr float kNegInf = -__builtin_inff();
+
+// ---- element access inside packed 32-bit words ------------------------------------------
+
+// Widen 16-bit element `half` (0 = low, 1 = high) of word w to float.
+template <DT dt>
+__device__ __forceinline__ float widen16(uint32_t w, int half) {
+  if constexpr (dt == DT::BF16) {
+    return __uint_as_float(half ? (w & 0xffff0000u) : (w << 16));
+  } else {
+    f16x2 h = __builtin_bit_cast(f16x2, w);
+    return half ? (float)h[1] : (float)h[0];
+  }
+}
+
+// Element i of a chunk of 32-bit words holding `dt` values.
+template <DT dt, int NWORDS>
+__device__ __forceinline__ float elem_of(const uint32_t (&w)[NWORDS], int i) {
+  if constexpr (dt == DT::F32) {
+    return __uint_as_float(w[i]);
+  } else {
+    return widen16<dt>(w[i >> 1], i & 1);
+  }
+}
+
+// Round a float to the storage type (nearest, ties to even), returned as raw bits.
+template <DT dt>
+__device__ __forceinline__ uint32_t narrow_bits(float x) {
+  if constexpr (dt == DT::F32) {
+    return __float_as_uint(x);
+  } else if constexpr (dt == DT::F16) {
+    _Float16 h = (_Float16)x;
+    return (uint32_t)__builtin_bit_cast(uint16_t, h);
+  } else {
+    __bf16 b = (__bf16)x;
+    return (uint32_t)__builtin_bit_cast(uint16_t, b);
+  }
+}
+
+template <DT dt>
+__device__ __forceinline__ void store_elem(void* base, int64_t idx, float x) {
+  if constexpr (dt == DT::F32) {
+    reinterpret_cast<float*>(base)[idx] = x;
+  } else {
+    reinterpret_cast<uint16_t*>(base)[idx] = (uint16_t)narrow_bits<dt>(x);
+  }
+}
+
+// ---- loads ------------------------------------------------------------------------------
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x2 load8(const void* p) {
+  return *reinterpret_cast<const u32x2*>(p);
+}
+
+// ---- cross-lane reductions ----------------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_amdgcn_update_dpp(0.0f, x, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i inside each group of 8
+constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i inside each row of 16
+
+// Sum over aligned groups of N lanes (N = 1..64, power of two); every lane gets its group's
+// sum. Uses DPP inside a row of 16 (after the quad steps every quad holds one value, so the
+// mirrors pair up whole quads / halves) and lane shuffles across rows.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp<kDppXor1>(x);
+  if constexpr (N >= 4) x += dpp<kDppXor2>(x);
+  if constexpr (N >= 8) x += dpp<kDppHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kDppMirror>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+// exp2 via the hardware instruction (inputs here are <= 0 or -inf).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Weight of a state with maximum m against the merged maximum M, treating an empty state
+// (m == -inf) as weight 0 even when M is -inf too.
+__device__ __forceinline__ float rescale(float m, float M) {
+  return (m == kNegInf) ? 0.0f : fast_exp2(m - M);
+}
+
+}  // namespace pa

@@ -1,0 +1,54 @@
+// pa_internal.h — host-side launch interface between the C ABI (pa_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Arguments of the decode kernels (passed by value as the kernel argument block).
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float scale_log2;  // scale * log2(e): scores are kept in the base-2 exponent domain
+  int num_seqs;
+  int num_q_heads;
+  int num_kv_heads;
+  int max_blocks_per_seq;
+  int64_t num_blocks;
+  int max_context_len;
+  int partition_tokens;  // P, a multiple of 32
+  int max_parts;         // ceil(max_context_len / P), at least 1
+  float* part_m;         // [S][Hq][max_parts]   running maxima (base-2 domain)
+  float* part_l;         // [S][Hq][max_parts]   running sums
+  float* part_o;         // [S][Hq][max_parts][D] unnormalised partial outputs
+  int* counters;         // [S][Hq] arrivals per (sequence, head unit); zero between calls
+};
+
+// Workspace layout for a given problem: byte offsets of each region.
+struct WorkspaceLayout {
+  size_t m_off, l_off, o_off, cnt_off, total;
+};
+WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_parts);
+
+enum class DecodePath : int { Valu = 0, Mfma = 1 };
+
+// Launchers return hipSuccess or the launch error. `dt` uses pa_dtype codes.
+hipError_t launch_decode(DecodePath path, int dt, int head_dim, int block_size,
+                         const DecodeArgs& a, hipStream_t stream);
+bool decode_supported(DecodePath path, int dt, int head_dim, int block_size);
+int decode_units_per_seq(DecodePath path, int num_q_heads, int num_kv_heads);
+
+hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                           const int32_t* slot_mapping, int n_tokens, int num_kv_heads,
+                           int row_bytes, int block_size, int64_t num_blocks,
+                           hipStream_t stream);
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int n_pairs,
+                              int64_t block_bytes, int64_t num_blocks, hipStream_t stream);
+
+}  // namespace pa

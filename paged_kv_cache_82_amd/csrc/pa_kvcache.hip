@@ -1,0 +1,100 @@
+// pa_kvcache.hip — slot-mapped KV write and whole-block copy kernels (gfx950).
+//
+// [PA-tutorial] un.csdn.net, "PagedAttention实战：如何用Python手搓一个高效KV缓存管理器",
+// §3.1 append_kv: a token at position pos goes to offset pos % B of the physical page that
+// holds logical page pos // B. The caller turns that into a slot = phys * B + offset.
+// [PA-summary] azimuth.plus, "Efficient Memory Management for Large Language Model Serving
+// with PagedAttention", "Memory sharing: copy-on-write": a write into a shared block first
+// copies that block alone to a new physical block.
+//
+// Both kernels are pure data movement: one thread moves one 16-byte chunk (the unit of a
+// dwordx4 load/store), consecutive threads move consecutive chunks of a row or block, so
+// reads and writes are fully coalesced.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+// One thread per (token, kv head, 16-byte chunk of the row). Both K and V are moved.
+__global__ __launch_bounds__(256) void write_kv_kernel(
+    void* __restrict__ k_cache, void* __restrict__ v_cache, const void* __restrict__ k_new,
+    const void* __restrict__ v_new, const int32_t* __restrict__ slot_mapping, int n_tokens,
+    int num_kv_heads, int chunks_per_row, int block_size, int64_t num_slots) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)n_tokens * num_kv_heads * chunks_per_row;
+  if (idx >= total) return;
+  const int c = (int)(idx % chunks_per_row);
+  const int64_t th = idx / chunks_per_row;  // token * num_kv_heads + head
+  const int h = (int)(th % num_kv_heads);
+  const int i = (int)(th / num_kv_heads);
+  const int64_t slot = slot_mapping[i];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / block_size;
+  const int64_t off = slot % block_size;
+  const int64_t dst_row = (blk * num_kv_heads + h) * block_size + off;
+  const int64_t dst = dst_row * chunks_per_row + c;  // in 16-byte chunks
+  const int64_t src = th * chunks_per_row + c;
+  reinterpret_cast<u32x4*>(k_cache)[dst] = reinterpret_cast<const u32x4*>(k_new)[src];
+  reinterpret_cast<u32x4*>(v_cache)[dst] = reinterpret_cast<const u32x4*>(v_new)[src];
+}
+
+// grid = (chunk groups, n_pairs, 2 for K|V); each thread copies kUnroll chunks spaced a
+// workgroup apart, so a workgroup covers kUnroll * 256 * 16 bytes of one block.
+constexpr int kCopyUnroll = 4;
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(
+    void* __restrict__ k_cache, void* __restrict__ v_cache, const int32_t* __restrict__ pairs,
+    int64_t chunks_per_block, int64_t num_blocks) {
+  const int pair = blockIdx.y;
+  const int64_t src = pairs[2 * pair];
+  const int64_t dst = pairs[2 * pair + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  u32x4* base = reinterpret_cast<u32x4*>(blockIdx.z == 0 ? k_cache : v_cache);
+  const u32x4* from = base + src * chunks_per_block;
+  u32x4* to = base + dst * chunks_per_block;
+  const int64_t first = (int64_t)blockIdx.x * (kCopyUnroll * 256) + threadIdx.x;
+  u32x4 tmp[kCopyUnroll];
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t c = first + u * 256;
+    if (c < chunks_per_block) tmp[u] = from[c];
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t c = first + u * 256;
+    if (c < chunks_per_block) to[c] = tmp[u];
+  }
+}
+
+hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                           const int32_t* slot_mapping, int n_tokens, int num_kv_heads,
+                           int row_bytes, int block_size, int64_t num_blocks,
+                           hipStream_t stream) {
+  if (n_tokens == 0) return hipSuccess;
+  const int chunks = row_bytes / 16;
+  const int64_t total = (int64_t)n_tokens * num_kv_heads * chunks;
+  const int64_t grid = (total + 255) / 256;
+  hipLaunchKernelGGL(write_kv_kernel, dim3((unsigned)grid), dim3(256), 0, stream, k_cache,
+                     v_cache, k_new, v_new, slot_mapping, n_tokens, num_kv_heads, chunks,
+                     block_size, num_blocks * block_size);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int n_pairs,
+                              int64_t block_bytes, int64_t num_blocks, hipStream_t stream) {
+  if (n_pairs == 0) return hipSuccess;
+  const int64_t chunks = block_bytes / 16;
+  const int64_t per_wg = kCopyUnroll * 256;
+  const int64_t gx = (chunks + per_wg - 1) / per_wg;
+  // grid.y is limited to 65535: launch pairs in batches of at most that many.
+  for (int first = 0; first < n_pairs; first += 65535) {
+    const int n = (n_pairs - first < 65535) ? (n_pairs - first) : 65535;
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)gx, (unsigned)n, 2), dim3(256), 0,
+                       stream, k_cache, v_cache, pairs + 2 * (int64_t)first, chunks, num_blocks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace pa

@@ -1,0 +1,134 @@
+"""The C ABI library on the CPU: it loads, exports every function include/pa.h declares, and
+rejects invalid arguments on the host before any GPU work (no kernel is launched here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_kv_cache_82_amd as pa
+from paged_kv_cache_82_amd import build as pa_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE = 0, 1, 2, 3
+F32, F16, BF16 = 0, 1, 2
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pa.lib_path()):
+        pa_build.build()
+    return pa.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(pa_\w+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_header_declares_the_calls():
+    assert declared_functions() == ["pa_copy_blocks", "pa_decode", "pa_decode_workspace_size",
+                                    "pa_status_string", "pa_write_kv"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(declared_functions()) <= exported
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "pa.h"\nint main(void){ return (int)PA_OK; }\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
+                    str(src), "-o", str(tmp_path / "t")], check=True)
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert isinstance(pa.pa_status_string(s), str) and pa.pa_status_string(s)
+    assert pa.pa_status_string(99) == "unknown status"
+
+
+V = ctypes.c_void_p
+BAD = V(0x1000)  # never dereferenced: every call below fails its host-side checks first
+
+
+def test_write_kv_argument_checks(lib):
+    f = lib.pa_write_kv
+    assert f(BAD, BAD, BAD, BAD, BAD, 0, 8, 128, 16, 10, F16, None) == PA_OK  # empty: no-op
+    assert f(None, BAD, BAD, BAD, BAD, 4, 8, 128, 16, 10, F16, None) == PA_ERR_INVALID_ARG
+    assert f(BAD, BAD, BAD, BAD, BAD, -1, 8, 128, 16, 10, F16, None) == PA_ERR_INVALID_ARG
+    assert f(BAD, BAD, BAD, BAD, BAD, 4, 8, 128, 16, 10, 7, None) == PA_ERR_INVALID_ARG
+    assert f(BAD, BAD, BAD, BAD, BAD, 4, 8, 4, 16, 10, F16, None) == PA_ERR_UNSUPPORTED
+    assert f(V(0x1002), BAD, BAD, BAD, BAD, 4, 8, 128, 16, 10, F16, None) == PA_ERR_INVALID_ARG
+    assert f(BAD, BAD, BAD, BAD, BAD, 4, 8, 128, 16, 1 << 62, F16, None) == PA_ERR_INVALID_ARG
+
+
+def test_decode_argument_checks(lib, monkeypatch):
+    f = lib.pa_decode
+    args = [BAD, BAD, BAD, BAD, BAD, BAD, 0.125, 4, 8, 8, 128, 16, 4, 64, 50, 0, None, 0, F16,
+            None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["out", "q", "k", "v", "bt", "cl", "scale", "S", "Hq", "Hkv", "d", "B", "M", "N",
+                 "maxT", "P", "ws", "wsb", "dt", "stream"]
+        for k, val in kw.items():
+            a[names.index(k)] = val
+        return f(*a)
+
+    assert call(S=0) == PA_OK
+    assert call(q=None) == PA_ERR_INVALID_ARG
+    assert call(Hq=8, Hkv=3) == PA_ERR_INVALID_ARG
+    assert call(d=96) == PA_ERR_UNSUPPORTED
+    assert call(B=64) == PA_ERR_UNSUPPORTED
+    assert call(P=48) == PA_ERR_INVALID_ARG
+    assert call(dt=9) == PA_ERR_INVALID_ARG
+    assert call(M=0) == PA_ERR_INVALID_ARG
+    assert call(N=0) == PA_ERR_INVALID_ARG
+    # long contexts need a workspace; none given
+    assert call(maxT=4096) == PA_ERR_WORKSPACE
+    assert call(maxT=4096, P=1024, ws=BAD, wsb=16) == PA_ERR_WORKSPACE
+    need = lib.pa_decode_workspace_size(4, 8, 8, 128, 16, 4096, 1024, F16)
+    assert need > 0
+    assert call(maxT=4096, P=1024, ws=V(0x1010), wsb=need) == PA_ERR_INVALID_ARG  # misaligned
+    # the MFMA path does not take fp32
+    monkeypatch.setenv("PA_DECODE_PATH", "mfma")
+    assert call(dt=F32) == PA_ERR_UNSUPPORTED
+
+
+def test_workspace_size(lib):
+    ws = lib.pa_decode_workspace_size
+    assert ws(4, 8, 8, 128, 16, 50, 0, F32) == 0  # one partition: no workspace
+    a = ws(64, 40, 40, 128, 16, 2048, 512, F16)
+    parts = 4
+    sh = 64 * 40
+    assert a >= sh * parts * (128 + 2) * 4 + sh * 4
+    assert ws(64, 40, 40, 128, 16, 2048, 48, F16) == 0  # invalid partition size
+    assert ws(64, 40, 7, 128, 16, 2048, 0, F16) == 0  # heads not a multiple
+
+
+def test_copy_blocks_argument_checks(lib):
+    f = lib.pa_copy_blocks
+    assert f(BAD, BAD, BAD, 0, 8, 128, 16, 10, F16, None) == PA_OK
+    assert f(BAD, BAD, None, 3, 8, 128, 16, 10, F16, None) == PA_ERR_INVALID_ARG
+    assert f(BAD, BAD, BAD, -3, 8, 128, 16, 10, F16, None) == PA_ERR_INVALID_ARG
+    assert f(BAD, BAD, BAD, 3, 0, 128, 16, 10, F16, None) == PA_ERR_INVALID_ARG
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import paged_kv_cache_82_amd._binding as b
+
+    monkeypatch.setattr(b, "_lib", None)
+    monkeypatch.setattr(b, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(FileNotFoundError):
+        b.load()

@@ -1,0 +1,188 @@
+"""GPU parity of the C ABI (pa_write_kv, pa_copy_blocks, pa_decode) against the CPU oracle on
+small and edge-case inputs. Bit-exact for the indexing kernels; attention within max-abs 1e-5
+for fp32 and |gpu - ref| <= 2e-2 + 1e-2 |ref| for fp16/bf16 (fp32 accumulation)."""
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+from gpu_harness import DevStep, assert_attention_close, to_host
+from workloads import config1, config5, make_step, to_float64, to_storage
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(a):
+    return a.view(np.uint8)
+
+
+def _run_and_check(step, partition_tokens=0, check_pools=True, what=""):
+    ref, kc, vc = oracle.run_step(step)
+    dev = DevStep(step, partition_tokens)
+    got = dev.run()
+    if check_pools:
+        assert np.array_equal(_bits(to_host(dev.k_cache, step.dtype)), _bits(kc)), what
+        assert np.array_equal(_bits(to_host(dev.v_cache, step.dtype)), _bits(vc)), what
+    assert_attention_close(got, ref, step.dtype, what)
+    return got, ref
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu-test] {request.node.name}", flush=True)
+    yield
+
+
+def test_config1_tiny_f32():
+    got, ref = _run_and_check(config1(), what="config1")
+    assert np.abs(got.astype(np.float64) - ref).max() <= 1e-5
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B", [8, 16, 32])
+def test_shapes_mha(dt, d, B):
+    step = make_step("mha", 31 + B + d, [1, 7, B, B + 1, 3 * B - 1, 200], 4, 4, d, B, dt)
+    _run_and_check(step, what=f"mha {dt} d{d} B{B}")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("g", [2, 4, 8, 16, 32])
+@pytest.mark.parametrize("d,B", [(128, 16), (64, 8), (128, 32)])
+def test_shapes_gqa(dt, g, d, B):
+    step = make_step("gqa", 41 + g, [1, 5, 16, 33, 130, 257], 2 * g, 2, d, B, dt)
+    _run_and_check(step, what=f"gqa {dt} g{g} d{d} B{B}")
+
+
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+def test_both_decode_paths_on_gqa(path, monkeypatch):
+    monkeypatch.setenv("PA_DECODE_PATH", path)
+    step = make_step("paths", 50, [3, 64, 100, 511, 700], 16, 2, 128, 16, "bf16")
+    _run_and_check(step, what=path)
+
+
+@pytest.mark.parametrize("P", [32, 64, 96, 512])
+def test_forced_split_k(P):
+    step = make_step("split", 60, [1, 31, 32, 33, 95, 400, 1000], 8, 8, 128, 16, "f16")
+    got, ref = _run_and_check(step, partition_tokens=P, what=f"P={P}")
+    single, _ = _run_and_check(step, partition_tokens=1024, check_pools=False)
+    assert_attention_close(got, to_float64(single, step.dtype), step.dtype, "split vs single")
+
+
+@pytest.mark.parametrize("P", [32, 128])
+def test_forced_split_k_gqa(P):
+    step = make_step("splitg", 61, [2, 40, 300, 900], 32, 4, 128, 16, "bf16")
+    _run_and_check(step, partition_tokens=P, what=f"gqa P={P}")
+
+
+def test_config1_split_k_every_partition_size():
+    for P in (32, 64, 96, 128, 512):
+        _run_and_check(config1(), partition_tokens=P, what=f"config1 P={P}")
+
+
+def test_empty_and_single_token_sequences():
+    step = make_step("edge", 70, [0, 1, 0, 2, 16, 17], 8, 2, 128, 16, "bf16")
+    got, ref = _run_and_check(step, what="edges")
+    assert np.array_equal(got[0].view(np.uint16), np.zeros_like(got[0].view(np.uint16)))
+    # T = 1 returns V_0 exactly (weight 1, sum 1)
+    step1 = make_step("t1", 71, [1, 1, 1], 4, 4, 64, 16, "f32")
+    dev = DevStep(step1)
+    got1 = dev.run()
+    v = step1.writes[0].v_new  # the only token of each sequence
+    assert np.array_equal(got1, v)
+
+
+def test_table_filled_to_the_last_entry():
+    # T = max_blocks_per_seq * B: the last 32-token step ends exactly at the table's end
+    step = make_step("full", 72, [48, 16], 8, 2, 128, 16, "f16")
+    assert step.block_tables.shape[1] == 3
+    _run_and_check(step, partition_tokens=32, what="full table")
+
+
+def test_large_scores_stay_finite():
+    step = make_step("big", 73, [50, 700], 8, 2, 128, 16, "bf16")
+    step.q[...] = to_storage(to_float64(step.q, "bf16") * 30.0, "bf16")
+    _run_and_check(step, what="large scores")
+
+
+def test_placement_invariance_bit_exact():
+    outs = []
+    for r in range(3):
+        step = make_step("pl", 80, [50, 7, 300, 129], 16, 2, 128, 16, "bf16",
+                         alloc_rng=np.random.default_rng(500 + r), pool_factor=2.0)
+        outs.append(DevStep(step).run())
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    outs = []
+    for r in range(3):
+        step = make_step("pl", 81, [50, 7, 300, 129], 8, 8, 128, 16, "f16",
+                         alloc_rng=np.random.default_rng(600 + r), pool_factor=2.0)
+        outs.append(DevStep(step).run())
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_block_size_change_within_tolerance():
+    ref = None
+    for B in (8, 16, 32):
+        step = make_step("bs", 82, [50, 7, 300], 8, 8, 128, B, "f16")
+        got = DevStep(step).run()
+        if ref is None:
+            ref = oracle.run_step(step)[0]
+        assert_attention_close(got, ref, "f16", f"B={B}")
+
+
+def test_repeated_calls_reuse_workspace():
+    step = make_step("rep", 83, [700, 1500, 33], 8, 8, 128, 16, "f16")
+    dev = DevStep(step, partition_tokens=128)
+    first = dev.run()
+    for _ in range(3):
+        # poison the output first: a call whose merge never ran would leave it NaN
+        dev.out.fill_(float("nan"))
+        dev.decode()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(dev.out, "f16"), first)
+
+
+def test_nondefault_stream():
+    step = make_step("strm", 84, [100, 200], 8, 2, 128, 16, "bf16")
+    ref = oracle.run_step(step)[0]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        dev = DevStep(step)
+        dev.apply_updates()
+        dev.decode()
+    s.synchronize()
+    assert_attention_close(to_host(dev.out, "bf16"), ref, "bf16", "stream")
+
+
+def test_config5_small_shared_vs_private():
+    kw = dict(prompts=3, samples=4, prompt_len=70, tail_len=20, heads=4, head_dim=128,
+              block_size=32, dtype="f16")
+    shared = config5(**kw)
+    private = config5(private=True, **kw)
+    a, _ = _run_and_check(shared, what="shared")
+    b, _ = _run_and_check(private, what="private")
+    assert np.array_equal(a, b)
+
+
+def test_config5_full():
+    shared = config5()
+    a, _ = _run_and_check(shared, what="config5 shared")
+    b = DevStep(config5(private=True)).run()
+    assert np.array_equal(a, b)
+
+
+def test_copy_blocks_and_write_leave_rest_untouched():
+    rng = np.random.default_rng(90)
+    step = make_step("cw", 90, [40, 70], 4, 4, 128, 16, "bf16", pool_factor=3.0)
+    # add copies of used blocks into free ones
+    used = set(step.block_tables[step.block_tables >= 0].tolist())
+    free = [b for b in range(step.num_blocks) if b not in used]
+    src = sorted(used)[:3]
+    dst = rng.choice(free, size=3, replace=False)
+    step.copies = np.stack([src, dst], axis=1).astype(np.int32)
+    _run_and_check(step, what="copy+write")
