@@ -1,0 +1,310 @@
+"""Benchmark of the paged decode hot path on one MI355X.
+
+One step = pa_write_kv of every sequence's new token, then pa_decode of the whole batch (all
+partitions and the fused merge), on seeded synthetic inputs already resident in HBM. The
+default workload is the 13B-shape fp16 MHA decode batch: 64 sequences, 40 heads, head dim
+128, block size 16, context lengths lognormal (median 512, sigma 1) clipped to [16, 2048],
+blocks scattered over a pool 1.2x the need. Other workloads (--workload) are for profiling.
+
+Prints one JSON line: value = algorithmic HBM bytes of the step / step time (GB/s), plus
+decode seq-tokens/s, the decode kernel's roofline (HIP-event duration on the launch stream,
+vs 8 TB/s) and the CPU oracle timed on this host.
+
+Cache honesty: the KV pools are replicated (--pool-copies, default 4, about 4.8 GB for the
+default workload) and consecutive steps use different copies, so no step finds the previous
+step's blocks in the 256 MB last-level cache.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, vendor figure
+
+WORKLOADS = {
+    "mha13b": ("config2", "13B-shape fp16 MHA decode: 64 seqs, 40 heads, d=128, B=16, "
+               "lognormal lengths (median 512) clipped to [16,2048]"),
+    "gqa": ("config3", "GQA bf16 decode: 256 seqs, 64 query / 8 KV heads, d=128, B=16, "
+            "lengths uniform in [128,4096]"),
+    "long": ("config4", "long-context bf16 split-K decode: 8 seqs, 32 heads, d=128, B=16, "
+             "lengths uniform in [32768,131072]"),
+    "shared": ("config5", "shared-prefix fp16 decode: 16 prompts x 4 samples, 32 heads, "
+               "d=128, B=32, 1297 tokens each"),
+    "tiny": ("config1", "tiny fp32 decode: 4 seqs (7,16,33,50), 8 heads, d=64, B=16"),
+    "copy": (None, "plain copy calibration: pa_copy_blocks of 4096 blocks of 256 KiB"),
+}
+
+DECODE_SOURCES = ["paged_kv_cache_82_amd/csrc/pa_decode.hip",
+                  "paged_kv_cache_82_amd/csrc/pa_device.h",
+                  "paged_kv_cache_82_amd/csrc/pa_internal.h",
+                  "paged_kv_cache_82_amd/csrc/pa_api.hip"]
+
+
+def decode_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in DECODE_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes (read + written) per decode launch from the committed rocprofv3 counter
+    summary, if it was taken on the current decode sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"pa_decode_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    src = re.search(r"decode_source_sha256_16:\s*(\w+)", text)
+    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not src or not val or src.group(1) != decode_source_hash():
+        return None
+    return float(val.group(1))
+
+
+def algorithmic_bytes(step) -> dict:
+    """Bytes the method itself must move (per decode launch and per KV write)."""
+    e = step.elem_bytes
+    S, Hq, Hkv, d, B = (step.num_seqs, step.num_q_heads, step.num_kv_heads, step.head_dim,
+                        step.block_size)
+    T = step.context_lens.astype(float)
+    kv = float(T.sum()) * 2 * Hkv * d * e
+    qo = 2.0 * S * Hq * d * e
+    idx = 4.0 * (float(sum(math.ceil(t / B) for t in T)) + S)
+    n_new = sum(len(w.slot_mapping) for w in step.writes)
+    write = 2.0 * n_new * Hkv * d * e * 2 + 4.0 * n_new
+    return {"decode": kv + qo + idx, "write": write, "tokens": float(T.sum())}
+
+
+def make_workload(name: str, poison: bool, placement: str = "random"):
+    import workloads
+
+    cfg = WORKLOADS[name][0]
+    kw = {"poison": poison}
+    if placement == "contiguous" and cfg != "config5":
+        kw["alloc_rng"] = workloads.InOrder()
+    return getattr(workloads, cfg)(**kw)
+
+
+def cpu_baseline(step, budget_s: float = 12.0) -> dict:
+    """The oracle (test infrastructure, plain C, fp64) on this host: the whole step (KV write and
+    decode of every sequence) repeated until about `budget_s` of CPU time; a bounded sample."""
+    import numpy as np
+
+    import oracle
+
+    nb = algorithmic_bytes(step)
+    # Bound the sample: whole sequences, in order, until about 1/4 of the budget per pass.
+    S = step.num_seqs
+    seqs = list(range(S))
+    t0 = time.perf_counter()
+    oracle.decode(step.q, step.k_cache, step.v_cache, step.block_tables, step.context_lens,
+                  step.scale, step.dtype, seq_list=np.asarray(seqs[:1], np.int32))
+    one = time.perf_counter() - t0
+    per_seq_est = max(one, 1e-4)
+    n = max(1, min(S, int((budget_s / 4) / per_seq_est)))
+    sample = np.asarray(seqs[:n], np.int32)
+    reps, elapsed = 0, 0.0
+    t0 = time.perf_counter()
+    while elapsed < budget_s and reps < 1000:
+        oracle.decode(step.q, step.k_cache, step.v_cache, step.block_tables, step.context_lens,
+                      step.scale, step.dtype, seq_list=sample)
+        reps += 1
+        elapsed = time.perf_counter() - t0
+    tok = float(step.context_lens[sample].sum()) * reps
+    frac = float(step.context_lens[sample].sum()) / nb["tokens"]
+    gbs = nb["decode"] * frac * reps / elapsed / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"decode of sequences 0..{n - 1} of {S} ({int(step.context_lens[sample].sum())} "
+                      f"of {int(nb['tokens'])} context tokens), fp64 oracle, {reps} passes in "
+                      f"{elapsed:.1f} s",
+            "seq_tokens_per_s": round(tok / elapsed, 1)}
+
+
+def run_copy_calibration(args):
+    import torch
+
+    import paged_kv_cache_82_amd as pa
+
+    dev = torch.device("cuda")
+    nblk, H, B, d = 8192, 32, 32, 128  # 256 KiB blocks, 2 GiB pools
+    k = torch.zeros((nblk, H, B, d), dtype=torch.float16, device=dev)
+    v = torch.zeros_like(k)
+    pairs = torch.stack([torch.arange(0, 4096), torch.arange(4096, 8192)], 1).int().to(dev)
+    for _ in range(args.warmup):
+        pa.pa_copy_blocks(k, v, pairs)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        pa.pa_copy_blocks(k, v, pairs)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    nbytes = 2 * 2 * 4096 * H * B * d * 2
+    print(json.dumps({"metric": "copy calibration", "bytes_read_per_launch": nbytes // 2,
+                      "bytes_written_per_launch": nbytes // 2, "GB_per_s": nbytes / dt / 1e9}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mha13b", choices=sorted(WORKLOADS))
+    ap.add_argument("--pool-copies", type=int, default=4)
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--placement", default="random", choices=["random", "contiguous"],
+                    help="block placement; 'contiguous' is a diagnostic of what scattering costs")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(sequences and KV heads would shard with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_82_amd as pa
+
+    if not os.path.exists(pa.lib_path()):
+        from paged_kv_cache_82_amd import build as pa_build
+
+        pa_build.build()
+    pa.load()
+    if args.workload == "copy":
+        return run_copy_calibration(args)
+
+    t_gen = time.perf_counter()
+    step = make_workload(args.workload, poison=False, placement=args.placement)
+    t_gen = time.perf_counter() - t_gen
+    dev = torch.device("cuda")
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[step.dtype]
+
+    def up(a, dt=None):
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    ncopy = max(1, args.pool_copies)
+    kc0, vc0 = up(step.k_cache, step.dtype), up(step.v_cache, step.dtype)
+    pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(ncopy - 1)]
+    q = up(step.q, step.dtype)
+    bt, cl = up(step.block_tables), up(step.context_lens)
+    copies = up(step.copies)
+    writes = [(up(w.k_new, step.dtype), up(w.v_new, step.dtype), up(w.slot_mapping))
+              for w in step.writes]
+    out = torch.empty_like(q)
+    P = args.partition_tokens
+    ws_bytes = pa.pa_decode_workspace_size(step.num_seqs, step.num_q_heads, step.num_kv_heads,
+                                           step.head_dim, step.block_size, step.max_context_len,
+                                           P, tdt)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    scale = float(step.scale)
+    maxT = step.max_context_len
+    torch.cuda.synchronize()
+
+    def one_step(i, ev=None):
+        kc, vc = pools[i % ncopy]
+        if len(step.copies):
+            pa.pa_copy_blocks(kc, vc, copies)
+        for kn, vn, sm in writes:
+            pa.pa_write_kv(kc, vc, kn, vn, sm)
+        if ev is not None:
+            ev[0].record()
+        pa.pa_decode(out, q, kc, vc, bt, cl, scale, maxT, ws, P)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+    # Timed region, part 1: K steps (KV write + decode), events around each decode launch.
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_event_us = float(np.mean([a.elapsed_time(b) for a, b in events])) * 1e3
+    # Part 2: K decode launches back to back (rotating pool copies) between two events on the
+    # launch stream; the average is the decode kernel's launch duration for the roofline (an
+    # event right before each launch would also time the dispatch gap after the KV write).
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        kc, vc = pools[i % ncopy]
+        pa.pa_decode(out, q, kc, vc, bt, cl, scale, maxT, ws, P)
+    e1.record()
+    torch.cuda.synchronize()
+    dec_s = e0.elapsed_time(e1) / 1e3 / args.steps
+
+    nb = algorithmic_bytes(step)
+    ms_per_step = wall / args.steps * 1e3
+    step_bytes = nb["decode"] + nb["write"]
+    value = step_bytes / (wall / args.steps) / 1e9
+    achieved = nb["decode"] / dec_s / 1e9
+    traffic = measured_traffic(args.workload)
+    res = {
+        "metric": "paged decode attention: achieved HBM GB/s (% of peak) + seq-tokens/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": step.dtype,
+        "accumulate": "f32",
+        "data": "synthetic (seeded N(0,1) K/V/q; lengths and placement as described)",
+        "config": {
+            "workload": WORKLOADS[args.workload][1],
+            "num_seqs": step.num_seqs, "num_q_heads": step.num_q_heads,
+            "num_kv_heads": step.num_kv_heads, "head_dim": step.head_dim,
+            "block_size": step.block_size, "num_blocks": step.num_blocks,
+            "context_tokens": int(nb["tokens"]), "max_context_len": maxT,
+            "partition_tokens": P or "auto", "pool_copies": ncopy,
+            "placement": args.placement,
+            "parallelism": "single GPU",
+        },
+        "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
+        "seq_tokens_per_s": round(nb["tokens"] / (wall / args.steps), 1),
+        "decode_seq_tokens_per_s": round(nb["tokens"] / dec_s, 1),
+        "roofline": {
+            "kernel": ("pa_decode: decode kernel (every sequence in one partition, no merge)"
+                       if ws_bytes == 0 else
+                       "pa_decode: decode kernel + partition-merge kernel (split sequences)"),
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": nb["decode"],
+            "avg_launch_us": round(dec_s * 1e6, 3),
+            "step_event_decode_us": round(step_event_us, 3),
+        },
+        "bytes_per_step": step_bytes,
+        "input_generation_s": round(t_gen, 2),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(step)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

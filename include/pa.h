@@ -87,9 +87,10 @@ pa_status pa_write_kv(void *k_cache, void *v_cache, const void *k_new, const voi
 /*
  * pa_decode_workspace_size — bytes of device workspace pa_decode needs for these sizes.
  * The workspace holds per-partition partial results (running max, running sum and partial
- * output, fp32) plus one int32 arrival counter per (sequence, query-head group).
+ * output, fp32) of every (sequence, query head).
  * partition_tokens: 0 = let the library choose (the same choice pa_decode makes for the same
- * arguments); > 0 must be a multiple of 32.
+ * arguments); > 0 must be a multiple of 32 and at most 64*4*block_size tokens (fp32 and
+ * single-head groups) or 8192 tokens (grouped heads).
  * Returns 0 when no workspace is needed (every sequence fits one partition) and for invalid
  * sizes.
  */
@@ -111,13 +112,12 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
  * §3.2 returns zeros when a sequence has no pages). Tail slots of the last block (t >= T) and
  * blocks the table does not reach never influence the result, whatever they hold.
  * Long contexts are split into partitions of partition_tokens tokens processed by separate
- * workgroups; each writes its (max, sum, partial output) to `workspace` and the last one to
- * finish for a (sequence, head group) merges them with the same log-sum-exp rescaling.
+ * workgroups; each writes its (max, sum, partial output) to `workspace` and a second kernel
+ * on the same stream merges them with the same log-sum-exp rescaling.
  * max_context_len: a host-known upper bound on context_lens (sizes the grid; no device read).
- * workspace: device buffer of >= pa_decode_workspace_size(...) bytes, 256-byte aligned, ZERO-
- * FILLED before its first use; every call leaves its counter words zero again on completion,
- * so one workspace is reused across calls that are ordered on one stream. Calls that overlap
- * in time must not share a workspace.
+ * workspace: device buffer of >= pa_decode_workspace_size(...) bytes, 256-byte aligned, any
+ * contents (NULL when that size is 0). One workspace serves any number of calls ordered on
+ * one stream; calls that may overlap in time must not share one.
  */
 pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
                     const int32_t *block_tables, const int32_t *context_lens, float scale,

@@ -37,6 +37,12 @@ def load(path: str | None = None) -> ctypes.CDLL:
         if _lib is not None:
             return _lib
         p = path or _LIB_PATH
+        # PyTorch ships its own HIP runtime whose soname equals the system one but which torch
+        # requests by another file name. Importing torch first makes libpa bind to that single
+        # runtime; loading libpa first would put two HIP runtimes in the process, and torch's
+        # streams and allocations would be foreign to the one libpa launches on.
+        import torch  # noqa: F401
+
         if not os.path.exists(p):
             raise FileNotFoundError(
                 f"{p} is missing: build it first (python -m paged_kv_cache_82_amd.build)")
@@ -108,7 +114,8 @@ def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, bloc
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
               workspace=None, partition_tokens=0, stream=None) -> None:
     """out, q [S, Hq, d]; pools [N, Hkv, B, d]; block_tables int32 [S, M]; context_lens int32
-    [S]; workspace: a zero-initialised uint8 tensor of >= pa_decode_workspace_size bytes."""
+    [S]; workspace: a device uint8 tensor of >= pa_decode_workspace_size bytes (any contents;
+    None when that size is 0)."""
     S, Hq, d = q.shape
     N, Hkv, B, _ = k_cache.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -39,20 +39,27 @@ bool choose_path(pa_dtype dt, int num_q_heads, int num_kv_heads, int head_dim, i
   return pa::decode_supported(p, (int)dt, head_dim, block_size);
 }
 
-// Tokens per partition. A workgroup covers P tokens of one (sequence, head unit); long
-// contexts are split so the grid has enough workgroups to fill 256 compute units several
-// times over and no single workgroup carries a long tail. 0 = automatic.
-int choose_partition(int num_seqs, int units_per_seq, int max_context_len, int requested) {
+// Tokens per partition. A workgroup covers P tokens of one (sequence, head unit); each extra
+// partition costs a partial-state write, a read in the merge kernel and a short-lived
+// workgroup, so sequences are split only when there are too few (sequence, head) units to fill
+// the GPU: with at least kManyUnits units every sequence stays whole; otherwise partitions of
+// 2048 tokens (halved while the grid would be smaller than kManyUnits workgroups, down to
+// 256). Measured on MI355X: unsplit 13B-shape and GQA batches ran 25-35% faster than with
+// 512-token partitions; long contexts peaked at 2048. 0 = automatic.
+constexpr int kManyUnits = 1024;
+
+int choose_partition(int num_seqs, int units_per_seq, int max_context_len, int cap,
+                     int requested) {
   if (requested > 0) return requested;
-  int P = 512;
   const int64_t units = (int64_t)num_seqs * units_per_seq;
-  // expected workgroups if lengths average half the maximum
-  int64_t est = units * (max_context_len / (2 * P) > 1 ? max_context_len / (2 * P) : 1);
-  while (est < 2048 && P > 128) {
-    P /= 2;
-    est *= 2;
-  }
-  return P;
+  const int whole = ((max_context_len + 31) / 32) * 32;
+  if (whole <= 0) return 32;
+  if (units >= kManyUnits && whole <= cap) return whole;
+  int P = 2048 < cap ? 2048 : cap;
+  // workgroups if lengths average half the maximum
+  auto est = [&](int p) { return units * ((max_context_len / 2 + p - 1) / p); };
+  while (P > 256 && est(P) < kManyUnits) P /= 2;
+  return P < whole ? P : whole;
 }
 
 int parts_for(int max_context_len, int P) {
@@ -106,9 +113,11 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
     return 0;
   DecodePath path;
   if (!choose_path(dt, num_q_heads, num_kv_heads, head_dim, block_size, &path)) return 0;
+  const int cap = pa::max_partition_tokens(path, block_size);
+  if (partition_tokens > cap) return 0;
   const int P = choose_partition(num_seqs,
                                  pa::decode_units_per_seq(path, num_q_heads, num_kv_heads),
-                                 max_context_len, partition_tokens);
+                                 max_context_len, cap, partition_tokens);
   return pa::workspace_layout(num_seqs, num_q_heads, head_dim, parts_for(max_context_len, P))
       .total;
 }
@@ -131,6 +140,8 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   DecodePath path;
   if (!choose_path(dt, num_q_heads, num_kv_heads, head_dim, block_size, &path))
     return PA_ERR_UNSUPPORTED;
+  const int cap = pa::max_partition_tokens(path, block_size);
+  if (partition_tokens > cap) return PA_ERR_INVALID_ARG;
   if (num_seqs == 0) return PA_OK;
   if (max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
@@ -141,7 +152,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
 
   const int P = choose_partition(num_seqs,
                                  pa::decode_units_per_seq(path, num_q_heads, num_kv_heads),
-                                 max_context_len, partition_tokens);
+                                 max_context_len, cap, partition_tokens);
   const int max_parts = parts_for(max_context_len, P);
   const pa::WorkspaceLayout L =
       pa::workspace_layout(num_seqs, num_q_heads, head_dim, max_parts);
@@ -168,7 +179,6 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.part_m = L.total ? (float*)(ws + L.m_off) : nullptr;
   a.part_l = L.total ? (float*)(ws + L.l_off) : nullptr;
   a.part_o = L.total ? (float*)(ws + L.o_off) : nullptr;
-  a.counters = L.total ? (int*)(ws + L.cnt_off) : nullptr;
   return from_hip(pa::launch_decode(path, (int)dt, head_dim, block_size, a, (hipStream_t)stream));
 }
 

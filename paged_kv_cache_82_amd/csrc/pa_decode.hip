@@ -14,8 +14,13 @@
 //   - every wave keeps its own running state; states are merged across lanes, then across
 //     waves through LDS, with the same rescaling as the equation;
 //   - when a sequence needs more than one partition, each workgroup stores its partial
-//     (max, sum, unnormalised output) and bumps an arrival counter; the last arrival merges
-//     all partials (split-K with the merge fused into the same launch, no spin-waits).
+//     (max, sum, unnormalised output) and a second, small kernel merges the partials of each
+//     (sequence, query head) with the same rescaling (split-K). Merging across workgroups in
+//     the same launch would need device-scope release/acquire fences, which on gfx950 write
+//     back and invalidate the whole L2 of an XCD; the kernel boundary is far cheaper.
+//   - each wave's physical block ids are read once into one register (lane k = k-th block)
+//     and broadcast with readlane, and the next block's K/V loads are issued before the
+//     current block is consumed (two register buffers).
 // Scores are kept in the base-2 exponent domain: s' = s * log2(e), exp(s - m) = 2^(s' - m').
 //
 // Two kernels:
@@ -46,13 +51,17 @@ __device__ __forceinline__ int64_t clamp_block(int32_t phys, int64_t n) {
   return phys < 0 ? 0 : (phys >= n ? n - 1 : (int64_t)phys);
 }
 
-// After a workgroup has merged its partition into (fm, fl, fo[nh][D]) in LDS: either store the
-// final output (single partition) or store the partial and, if this workgroup is the last of
-// its (sequence, head unit) to arrive, merge every partition's partial into the output.
+// Wave index inside the workgroup as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+// After a workgroup has merged its partition into (fm, fl, fo[nh][D]) in LDS: store the final
+// output when the sequence has a single partition, otherwise the partial state for the merge
+// kernel.
 template <DT dt, int D, int NT>
 __device__ void finish_partition(const DecodeArgs& a, int s, int h0, int nh, int p, int nparts,
-                                 const float* fm, const float* fl, const float* fo,
-                                 int* lds_flag) {
+                                 const float* fm, const float* fl, const float* fo) {
   const int tid = threadIdx.x;
   const int Hq = a.num_q_heads;
   if (nparts == 1) {
@@ -71,35 +80,34 @@ __device__ void finish_partition(const DecodeArgs& a, int s, int h0, int nh, int
     a.part_m[((int64_t)s * Hq + h0 + tid) * MP + p] = fm[tid];
     a.part_l[((int64_t)s * Hq + h0 + tid) * MP + p] = fl[tid];
   }
-  __threadfence();  // release this workgroup's partial to the whole device
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = atomicAdd(&a.counters[(int64_t)s * Hq + h0], 1);
-    *lds_flag = (prev == nparts - 1);
-  }
-  __syncthreads();
-  if (!*lds_flag) return;
-  __threadfence();  // acquire the other workgroups' partials
-  for (int idx = tid; idx < nh * D; idx += NT) {
-    const int hh = idx / D, dim = idx % D;
-    const int64_t base = ((int64_t)s * Hq + h0 + hh) * MP;
-    float M = kNegInf;
-    for (int pp = 0; pp < nparts; ++pp) M = fmaxf(M, a.part_m[base + pp]);
-    float acc = 0.0f, L = 0.0f;
-    for (int pp = 0; pp < nparts; ++pp) {
-      const float wgt = rescale(a.part_m[base + pp], M);
-      acc = fmaf(wgt, a.part_o[(base + pp) * D + dim], acc);
-      L = fmaf(wgt, a.part_l[base + pp], L);
-    }
-    store_elem<dt>(a.out, ((int64_t)s * Hq + h0 + hh) * D + dim, acc / L);
-  }
-  if (tid == 0) a.counters[(int64_t)s * Hq + h0] = 0;  // ready for the next call
 }
 
 template <DT dt, int D, int NT>
 __device__ void store_zeros(const DecodeArgs& a, int s, int h0, int nh) {
   for (int idx = threadIdx.x; idx < nh * D; idx += NT)
     store_elem<dt>(a.out, ((int64_t)s * a.num_q_heads + h0) * D + idx, 0.0f);
+}
+
+// Merge kernel: one workgroup of D threads per (query head, sequence) whose context spans more
+// than one partition. With M = max_p m_p and w_p = 2^(m_p - M):
+//   out = sum_p w_p o_p / sum_p w_p l_p          (the equation's rescaling, over partitions)
+template <DT dt, int D, int BS>
+__global__ __launch_bounds__(D) void merge_partitions_kernel(const DecodeArgs a) {
+  const int h = blockIdx.x, s = blockIdx.y;
+  const int T = seq_len(a, s, BS);
+  const int nparts = (T + a.partition_tokens - 1) / a.partition_tokens;
+  if (nparts <= 1) return;
+  const int64_t base = ((int64_t)s * a.num_q_heads + h) * a.max_parts;
+  float M = kNegInf;
+  for (int p = 0; p < nparts; ++p) M = fmaxf(M, a.part_m[base + p]);
+  float acc = 0.0f, L = 0.0f;
+  const int dim = threadIdx.x;
+  for (int p = 0; p < nparts; ++p) {
+    const float wgt = rescale(a.part_m[base + p], M);
+    acc = fmaf(wgt, a.part_o[(base + p) * D + dim], acc);
+    L = fmaf(wgt, a.part_l[base + p], L);
+  }
+  store_elem<dt>(a.out, ((int64_t)s * a.num_q_heads + h) * D + dim, acc / L);
 }
 
 // ---- VALU kernel ------------------------------------------------------------------------
@@ -165,14 +173,17 @@ __device__ __forceinline__ void valu_block(const float (&qf)[ValuCfg<dt, D, BS, 
   m = mn;
 }
 
-template <DT dt, int D, int BS, int NW>
+// Maximum blocks (VALU) or 32-token steps (MFMA) one wave handles in one partition: their
+// physical ids sit one per lane of a single register.
+constexpr int kMaxPerWave = 64;
+
+template <DT dt, int D, int BS, int NW, int NBUF>
 __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a) {
   using C = ValuCfg<dt, D, BS, NW>;
   constexpr int E = C::E, VEC = C::VEC, R = C::R, TPI = C::TPI, NL = C::NL, NT = C::NT;
   __shared__ float lds_o[NW][D];
   __shared__ float lds_m[NW], lds_l[NW];
   __shared__ float lds_fm[1], lds_fl[1];
-  __shared__ int lds_flag;
 
   const int p = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int T = seq_len(a, s, BS);
@@ -187,7 +198,8 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
   const int t0 = p * P;
   const int t1 = (T < t0 + P) ? T : t0 + P;
   const int jb0 = t0 / BS, jb1 = (t1 + BS - 1) / BS;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id();
   const int c = lane % R, r = lane / R;
 
   float qf[VEC];
@@ -205,25 +217,55 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
 #pragma unroll
   for (int e = 0; e < VEC; ++e) o[e] = 0.0f;
 
+  // This wave takes blocks jb0 + w + k*NW, k < nb; lane k holds the k-th physical id.
+  const int nb = (jb1 - jb0 - w + NW - 1) / NW;
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  int my_id = 0;
+  if (lane < nb) my_id = bt[jb0 + w + lane * NW];
   const char* kbase = (const char*)a.k_cache;
   const char* vbase = (const char*)a.v_cache;
-  constexpr int64_t row_bytes = (int64_t)D * E;
-  for (int j = jb0 + w; j < jb1; j += NW) {
-    const int64_t phys = clamp_block(bt[j], a.num_blocks);
-    const int64_t tile = (phys * a.num_kv_heads + kvh) * BS * row_bytes;
-    u32x4 kr[NL], vr[NL];
+  constexpr int row_bytes = D * E;
+  // Per-lane byte offset inside a (block, head) tile: loop-invariant and 32-bit, so loads take
+  // the form (wave-uniform 64-bit tile base) + (per-lane 32-bit offset).
+  const uint32_t lane_off = (uint32_t)(r * row_bytes + c * 16);
+  auto fetch = [&](int k, u32x4* kr, u32x4* vr) {
+    const int32_t id = __builtin_amdgcn_readlane(my_id, k);
+    const int64_t tile =
+        (clamp_block(id, a.num_blocks) * a.num_kv_heads + kvh) * (int64_t)(BS * row_bytes);
+    const char* kt = kbase + tile;
+    const char* vt = vbase + tile;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const int64_t off = tile + (int64_t)(i * TPI + r) * row_bytes + c * 16;
-      kr[i] = load16(kbase + off);
-      vr[i] = load16(vbase + off);
+      kr[i] = load16(kt + lane_off + i * TPI * row_bytes);
+      vr[i] = load16(vt + lane_off + i * TPI * row_bytes);
     }
-    const int tok0 = j * BS;
+    __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the consume that follows
+  };
+  auto consume = [&](int k, const u32x4* kr, const u32x4* vr) {
+    const int tok0 = (jb0 + w + k * NW) * BS;
     if (tok0 + BS <= t1)
       valu_block<dt, D, BS, NW, false>(qf, kr, vr, tok0, t1, r, m, l, o);
     else
       valu_block<dt, D, BS, NW, true>(qf, kr, vr, tok0, t1, r, m, l, o);
+  };
+  // A ring of NBUF register buffers: the loads of the next NBUF-1 blocks are in flight while
+  // one block is consumed. Prefetches are unconditional (past the end they re-read the final
+  // block, a cache hit) so that the compiler's wait before each consume only covers the
+  // oldest buffer.
+  if (nb > 0) {
+    u32x4 kbuf[NBUF][NL], vbuf[NBUF][NL];
+#pragma unroll
+    for (int u = 0; u + 1 < NBUF; ++u) fetch(u < nb ? u : nb - 1, kbuf[u], vbuf[u]);
+    for (int k = 0; k < nb; k += NBUF) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
+        if (k + u >= nb) break;
+        const int ahead = k + u + NBUF - 1;
+        fetch(ahead < nb ? ahead : nb - 1, kbuf[(u + NBUF - 1) % NBUF],
+              vbuf[(u + NBUF - 1) % NBUF]);
+        consume(k + u, kbuf[u], vbuf[u]);
+      }
+    }
   }
 
   // Merge the TPI row states of this wave (lanes with equal c), then the waves.
@@ -267,7 +309,7 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
     }
   }
   __syncthreads();
-  finish_partition<dt, D, NT>(a, s, h, 1, p, nparts, lds_fm, lds_fl, fo, &lds_flag);
+  finish_partition<dt, D, NT>(a, s, h, 1, p, nparts, lds_fm, lds_fl, fo);
 }
 
 // ---- MFMA kernel (grouped query heads) -----------------------------------------------------
@@ -315,8 +357,16 @@ __device__ __forceinline__ uint32_t vfrag_elem(const typename VFrag<D>::T& f, in
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-template <DT dt, int D, int BS, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a) {
+// One 32-token step of one wave: loads of tile u hold K rows of tokens 16u + hh (KC chunks)
+// and V rows of tokens 16u + 4*gq + i (i < 4).
+template <int D, int KC>
+struct StepRegs {
+  u32x4 k[2][KC];
+  typename VFrag<D>::T v[2][4];
+};
+
+template <DT dt, int D, int BS, int NW, int NBUF, int MINB>
+__global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const DecodeArgs a) {
   static_assert(dt != DT::F32, "MFMA path takes 16-bit inputs");
   static_assert(BS <= 32 && 32 % BS == 0, "a 32-token step spans whole blocks");
   using M = MfmaT<dt>;
@@ -330,7 +380,6 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
   __shared__ float lds_o[NW][16][D];
   __shared__ float lds_m[NW][16], lds_l[NW][16];
   __shared__ float lds_fm[16], lds_fl[16];
-  __shared__ int lds_flag;
 
   const int p = blockIdx.x, unit = blockIdx.y, s = blockIdx.z;
   const int Hq = a.num_q_heads;
@@ -351,7 +400,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
   const int t1 = (T < t0 + P) ? T : t0 + P;
   const int st0 = t0 / 32, st1 = (t1 + 31) / 32;
   const int jlast = (t1 - 1) / BS;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id();
   const int hh = lane & 15, gq = lane >> 4;
 
   // Q^T operand: column hh = query head h0 + hh, k = head dims 32*kk + 8*gq + e.
@@ -370,41 +420,69 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
   for (int mt = 0; mt < MT; ++mt) oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = kNegInf, lsum = 0.0f;
 
+  // This wave takes steps st0 + w + k*NW, k < ns; lane k holds the NBS physical ids of step k.
+  const int ns = (st1 - st0 - w + NW - 1) / NW;
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  int my_id[NBS];
+#pragma unroll
+  for (int b = 0; b < NBS; ++b) {
+    my_id[b] = 0;
+    if (lane < ns) {
+      int j = (st0 + w + lane * NW) * 32 / BS + b;
+      j = (j < jlast) ? j : jlast;  // never read the table past this partition's last block
+      my_id[b] = bt[j];
+    }
+  }
   const char* kbase = (const char*)a.k_cache;
   const char* vbase = (const char*)a.v_cache;
   const int64_t Hkv = a.num_kv_heads;
 
-  for (int st = st0 + w; st < st1; st += NW) {
-    const int tau0 = st * 32;
-    int64_t ph[NBS];
+  // Loop-invariant per-lane byte offsets inside a (block, head) tile. Token tk of a step lives
+  // in the step's block tk / BS at row tk % BS; for BS >= 16 the block of tile u is the same
+  // for every lane, so loads are (wave-uniform tile base) + (32-bit lane offset).
+  constexpr int RB = D * E;  // bytes per token row
+  const uint32_t koff = (uint32_t)((hh % BS) * RB + 8 * gq * E);
+  const uint32_t voff = (uint32_t)(((4 * gq) % BS) * RB + MT * hh * E);
+  const int64_t tile_bytes = (int64_t)BS * RB;
+  auto fetch = [&](int k, StepRegs<D, KC>& R) {
+    const char* kt[NBS];
+    const char* vt[NBS];
 #pragma unroll
     for (int b = 0; b < NBS; ++b) {
-      int j = tau0 / BS + b;
-      j = (j < jlast) ? j : jlast;  // never read the table past this partition's last block
-      ph[b] = clamp_block(bt[j], a.num_blocks);
+      const int64_t tile =
+          (clamp_block(__builtin_amdgcn_readlane(my_id[b], k), a.num_blocks) * Hkv + kvh) *
+          tile_bytes;
+      kt[b] = kbase + tile;
+      vt[b] = vbase + tile;
     }
-    // K operand of tile u: row hh = token tau0 + 16u + hh, k = dims 32*kk + 8*gq + e.
-    u32x4 kreg[2][KC];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int tk = 16 * u + hh;
-      const int64_t row = (ph[tk / BS] * Hkv + kvh) * BS + (tk % BS);
-      const char* rp = kbase + row * D * E + 8 * gq * E;
+      const char* rp;
+      if constexpr (BS >= 16) {
+        rp = kt[(16 * u) / BS] + koff + ((16 * u) % BS) * RB;
+      } else {  // BS == 8: lanes hh < 8 and hh >= 8 read different blocks
+        rp = kt[2 * u + (hh >> 3)] + koff;
+      }
 #pragma unroll
-      for (int kk = 0; kk < KC; ++kk) kreg[u][kk] = load16(rp + 32 * kk * E);
+      for (int kk = 0; kk < KC; ++kk) R.k[u][kk] = load16(rp + 32 * kk * E);
     }
-    // V rows of tokens 16u + 4*gq + i (i < 4): head dims MT*hh .. MT*hh + MT - 1.
-    typename VF::T vreg[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tk = 16 * u + 4 * gq + i;
-        const int64_t row = (ph[tk / BS] * Hkv + kvh) * BS + (tk % BS);
-        vreg[u][i] = VF::load(vbase + (row * D + MT * hh) * E);
+        const char* rp;
+        if constexpr (BS >= 16) {
+          rp = vt[(16 * u) / BS] + voff + ((16 * u) % BS + i) * RB;
+        } else {  // token 16u + 4gq + i sits in block 2u + gq/2 at row 4*(gq&1) + i
+          rp = vt[2 * u + (gq >> 1)] + voff + i * RB;
+        }
+        R.v[u][i] = VF::load(rp);
       }
+    __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the consume that follows
+  };
 
+  auto consume = [&](int k, StepRegs<D, KC>& R) {
+    const int tau0 = (st0 + w + k * NW) * 32;
     // S^T = K Q^T: sacc[u][i] = score of token tau0 + 16u + 4*gq + i for head hh.
     f32x4 sacc[2];
 #pragma unroll
@@ -412,7 +490,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
       sacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KC; ++kk)
-        sacc[u] = M::mma(__builtin_bit_cast(vec8, kreg[u][kk]), qop[kk], sacc[u]);
+        sacc[u] = M::mma(__builtin_bit_cast(vec8, R.k[u][kk]), qop[kk], sacc[u]);
     }
     const bool tail = tau0 + 32 > t1;
     float sc[8];
@@ -448,7 +526,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (tau0 + 16 * u + 4 * gq + i >= t1) vreg[u][i] = typename VF::T{};  // select
+          if (tau0 + 16 * u + 4 * gq + i >= t1) R.v[u][i] = typename VF::T{};  // select
     }
     // O^T += V^T P^T with k element e <-> token 16*(e/4) + 4*gq + (e%4).
 #pragma unroll
@@ -457,13 +535,28 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
 #pragma unroll
       for (int q2 = 0; q2 < 4; ++q2) {
         const int e0 = 2 * q2, e1 = 2 * q2 + 1;
-        const uint32_t lo = vfrag_elem<D>(vreg[e0 / 4][e0 % 4], mt);
-        const uint32_t hi = vfrag_elem<D>(vreg[e1 / 4][e1 % 4], mt);
+        const uint32_t lo = vfrag_elem<D>(R.v[e0 / 4][e0 % 4], mt);
+        const uint32_t hi = vfrag_elem<D>(R.v[e1 / 4][e1 % 4], mt);
         vw[q2] = lo | (hi << 16);
       }
       oacc[mt] = M::mma(__builtin_bit_cast(vec8, vw), pop, oacc[mt]);
     }
     m = mn;
+  };
+
+  if (ns > 0) {  // ring of NBUF register buffers, unconditional prefetch (see the VALU kernel)
+    StepRegs<D, KC> rb[NBUF];
+#pragma unroll
+    for (int u = 0; u + 1 < NBUF; ++u) fetch(u < ns ? u : ns - 1, rb[u]);
+    for (int k = 0; k < ns; k += NBUF) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
+        if (k + u >= ns) break;
+        const int ahead = k + u + NBUF - 1;
+        fetch(ahead < ns ? ahead : ns - 1, rb[(u + NBUF - 1) % NBUF]);
+        consume(k + u, rb[u]);
+      }
+    }
   }
 
   // Sum the per-lane partial sums over the four lane groups of each head.
@@ -502,12 +595,17 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
     fo[idx] = acc;
   }
   __syncthreads();
-  finish_partition<dt, D, NT>(a, s, h0, nh, p, nparts, lds_fm, lds_fl, fo, &lds_flag);
+  finish_partition<dt, D, NT>(a, s, h0, nh, p, nparts, lds_fm, lds_fl, fo);
 }
 
 // ---- host launchers -----------------------------------------------------------------------
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;          // waves per workgroup
+// Prefetch depth and occupancy, measured on MI355X (13B-shape fp16 MHA and GQA bf16 batches):
+// more blocks in flight per wave beat more waves per SIMD up to these depths.
+constexpr int kValuBuffers = 4;    // VALU kernel: blocks in registers (NBUF-1 in flight)
+constexpr int kMfmaBuffers = 3;    // MFMA kernel: 32-token steps in registers
+constexpr int kMfmaMinBlocks = 1;  // MFMA kernel: workgroups per CU the registers must allow
 
 WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_parts) {
   WorkspaceLayout L{};
@@ -517,8 +615,7 @@ WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int head_dim, in
   L.m_off = 0;
   L.l_off = up(L.m_off + sh * max_parts * sizeof(float));
   L.o_off = up(L.l_off + sh * max_parts * sizeof(float));
-  L.cnt_off = up(L.o_off + sh * max_parts * (size_t)head_dim * sizeof(float));
-  L.total = up(L.cnt_off + sh * sizeof(int));
+  L.total = up(L.o_off + sh * max_parts * (size_t)head_dim * sizeof(float));
   return L;
 }
 
@@ -528,21 +625,36 @@ int decode_units_per_seq(DecodePath path, int num_q_heads, int num_kv_heads) {
   return num_kv_heads * ((g + 15) / 16);
 }
 
+int max_partition_tokens(DecodePath path, int block_size) {
+  // every wave's block (or step) ids must fit one register: kMaxPerWave per wave
+  return path == DecodePath::Valu ? kMaxPerWave * kWaves * block_size : kMaxPerWave * kWaves * 32;
+}
+
+// Launches report their own status (hipLaunchKernel), never a stale error left by an earlier,
+// unrelated runtime call.
 template <DT dt, int D, int BS>
 static hipError_t launch_t(DecodePath path, const DecodeArgs& a, hipStream_t stream) {
   const dim3 block(kWaves * 64);
   const dim3 grid((unsigned)a.max_parts,
                   (unsigned)decode_units_per_seq(path, a.num_q_heads, a.num_kv_heads),
                   (unsigned)a.num_seqs);
+  DecodeArgs args_copy = a;
+  void* args[] = {&args_copy};
+  const void* fn = nullptr;
   if (path == DecodePath::Mfma) {
     if constexpr (dt != DT::F32) {
-      hipLaunchKernelGGL((decode_mfma_kernel<dt, D, BS, kWaves>), grid, block, 0, stream, a);
-      return hipGetLastError();
+      fn = (const void*)decode_mfma_kernel<dt, D, BS, kWaves, kMfmaBuffers, kMfmaMinBlocks>;
+    } else {
+      return hipErrorInvalidValue;
     }
-    return hipErrorInvalidValue;
+  } else {
+    fn = (const void*)decode_valu_kernel<dt, D, BS, kWaves, kValuBuffers>;
   }
-  hipLaunchKernelGGL((decode_valu_kernel<dt, D, BS, kWaves>), grid, block, 0, stream, a);
-  return hipGetLastError();
+  hipError_t e = hipLaunchKernel(fn, grid, block, args, 0, stream);
+  if (e != hipSuccess || a.max_parts <= 1) return e;
+  return hipLaunchKernel((const void*)merge_partitions_kernel<dt, D, BS>,
+                         dim3((unsigned)a.num_q_heads, (unsigned)a.num_seqs), dim3(D), args, 0,
+                         stream);
 }
 
 template <DT dt, int D>

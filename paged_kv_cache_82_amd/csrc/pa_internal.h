@@ -27,12 +27,11 @@ struct DecodeArgs {
   float* part_m;         // [S][Hq][max_parts]   running maxima (base-2 domain)
   float* part_l;         // [S][Hq][max_parts]   running sums
   float* part_o;         // [S][Hq][max_parts][D] unnormalised partial outputs
-  int* counters;         // [S][Hq] arrivals per (sequence, head unit); zero between calls
 };
 
 // Workspace layout for a given problem: byte offsets of each region.
 struct WorkspaceLayout {
-  size_t m_off, l_off, o_off, cnt_off, total;
+  size_t m_off, l_off, o_off, total;
 };
 WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_parts);
 
@@ -43,6 +42,8 @@ hipError_t launch_decode(DecodePath path, int dt, int head_dim, int block_size,
                          const DecodeArgs& a, hipStream_t stream);
 bool decode_supported(DecodePath path, int dt, int head_dim, int block_size);
 int decode_units_per_seq(DecodePath path, int num_q_heads, int num_kv_heads);
+// Largest partition (tokens) a launch supports: a wave keeps its block ids in one register.
+int max_partition_tokens(DecodePath path, int block_size);
 
 hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                            const int32_t* slot_mapping, int n_tokens, int num_kv_heads,

@@ -74,10 +74,11 @@ hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, cons
   const int chunks = row_bytes / 16;
   const int64_t total = (int64_t)n_tokens * num_kv_heads * chunks;
   const int64_t grid = (total + 255) / 256;
-  hipLaunchKernelGGL(write_kv_kernel, dim3((unsigned)grid), dim3(256), 0, stream, k_cache,
-                     v_cache, k_new, v_new, slot_mapping, n_tokens, num_kv_heads, chunks,
-                     block_size, num_blocks * block_size);
-  return hipGetLastError();
+  int64_t num_slots = num_blocks * block_size;
+  void* args[] = {&k_cache, &v_cache, &k_new, &v_new, &slot_mapping, &n_tokens, &num_kv_heads,
+                  (void*)&chunks, &block_size, &num_slots};
+  return hipLaunchKernel((const void*)write_kv_kernel, dim3((unsigned)grid), dim3(256), args, 0,
+                         stream);
 }
 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int n_pairs,
@@ -89,9 +90,12 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs
   // grid.y is limited to 65535: launch pairs in batches of at most that many.
   for (int first = 0; first < n_pairs; first += 65535) {
     const int n = (n_pairs - first < 65535) ? (n_pairs - first) : 65535;
-    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)gx, (unsigned)n, 2), dim3(256), 0,
-                       stream, k_cache, v_cache, pairs + 2 * (int64_t)first, chunks, num_blocks);
-    hipError_t e = hipGetLastError();
+    const int32_t* batch = pairs + 2 * (int64_t)first;
+    int64_t chunks_per_block = chunks;
+    void* args[] = {&k_cache, &v_cache, (void*)&batch, &chunks_per_block, &num_blocks};
+    const hipError_t e = hipLaunchKernel((const void*)copy_blocks_kernel,
+                                         dim3((unsigned)gx, (unsigned)n, 2), dim3(256), args, 0,
+                                         stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

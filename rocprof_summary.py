@@ -1,0 +1,104 @@
+"""Summarise rocprofv3 CSV output into the short text files kept under profiles/.
+
+  python rocprof_summary.py trace  <kernel_stats.csv> <out.txt> --command "<command>"
+  python rocprof_summary.py pmc    <workload> <out.txt> --fetch <csv> --write <csv>
+                                   --copy-fetch <csv> --copy-write <csv> --command "<command>"
+
+`trace` keeps the kernel table (calls, average/min/max duration) of a --kernel-trace --stats
+run. `pmc` turns FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the decode kernel into HBM
+bytes per launch, each scaled by what the same counter reads for the plain copy kernel
+(pa_copy_blocks moving 4096 blocks of 256 KiB: 2 GiB read and 2 GiB written per launch), and
+records the hash of the decode sources so bench.py only reports the figure while those sources
+are unchanged.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+COPY_BYTES = 2 * 4096 * 32 * 32 * 128 * 2 // 2  # read (= written) bytes per copy launch
+
+
+def kernel_avgs(path: str) -> dict:
+    agg = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in agg.items()}
+
+
+def pick(avgs: dict, needle: str) -> tuple:
+    hits = [(k, v) for k, v in avgs.items() if needle in k]
+    if len(hits) != 1:
+        raise SystemExit(f"expected one kernel matching {needle!r}, found {[h[0] for h in hits]}")
+    return hits[0]
+
+
+def do_trace(args) -> str:
+    rows = list(csv.DictReader(open(args.stats)))
+    lines = [f"command: {args.command}", "", "kernel | calls | avg us | min us | max us | % time"]
+    for r in rows:
+        lines.append(f"{r['Name'][:110]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.2f}")
+    return "\n".join(lines) + "\n"
+
+
+def do_pmc(args) -> str:
+    import bench
+
+    fetch = kernel_avgs(args.fetch)
+    write = kernel_avgs(args.write)
+    cf = pick(kernel_avgs(args.copy_fetch), "copy_blocks_kernel")[1]
+    cw = pick(kernel_avgs(args.copy_write), "copy_blocks_kernel")[1]
+    f_factor = COPY_BYTES / (cf * 1024)
+    w_factor = COPY_BYTES / (cw * 1024)
+    name, fk = pick(fetch, "decode_")
+    _, wk = pick(write, "decode_")
+    rd = fk * 1024 * f_factor
+    wr = wk * 1024 * w_factor
+    step = bench.make_workload(args.workload, poison=False)
+    alg = bench.algorithmic_bytes(step)["decode"]
+    lines = [
+        f"command: {args.command}",
+        f"kernel: {name}",
+        f"FETCH_SIZE_KiB_per_dispatch: {fk:.1f}",
+        f"WRITE_SIZE_KiB_per_dispatch: {wk:.1f}",
+        f"copy_kernel_FETCH_SIZE_KiB: {cf:.1f}  (known read {COPY_BYTES} B -> factor {f_factor:.4f})",
+        f"copy_kernel_WRITE_SIZE_KiB: {cw:.1f}  (known write {COPY_BYTES} B -> factor {w_factor:.4f})",
+        f"hbm_read_bytes_per_launch: {rd:.6g}",
+        f"hbm_write_bytes_per_launch: {wr:.6g}",
+        f"hbm_bytes_per_launch: {rd + wr:.6g}",
+        f"algorithmic_bytes_per_launch: {alg:.6g}",
+        f"traffic_over_algorithmic: {(rd + wr) / alg:.4f}",
+        f"decode_source_sha256_16: {bench.decode_source_hash()}",
+    ]
+    return "\n".join(lines) + "\n"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("stats")
+    t.add_argument("out")
+    t.add_argument("--command", required=True)
+    p = sub.add_parser("pmc")
+    p.add_argument("workload")
+    p.add_argument("out")
+    for k in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--command"):
+        p.add_argument(k, required=True)
+    args = ap.parse_args()
+    text = do_trace(args) if args.mode == "trace" else do_pmc(args)
+    with open(args.out, "w") as f:
+        f.write(text)
+    print(text)
+
+
+if __name__ == "__main__":
+    main()

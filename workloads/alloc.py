@@ -27,6 +27,15 @@ class PoolExhausted(MemoryError):
     """No free physical block is left."""
 
 
+class InOrder:
+    """Stands in for a Generator in BlockAllocator: hands out block ids in increasing order
+    (contiguous placement; used to measure what scattering costs)."""
+
+    @staticmethod
+    def permutation(n):
+        return np.arange(n)
+
+
 class BlockAllocator:
     """Free list (LIFO) and reference counts over `num_blocks` physical blocks.
 
