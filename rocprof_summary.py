@@ -22,7 +22,8 @@ import sys
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-COPY_BYTES = 2 * 4096 * 32 * 32 * 128 * 2 // 2  # read (= written) bytes per copy launch
+# bytes read (= written) per copy launch: 4096 pairs x (K block + V block) of 32*32*128 fp16
+COPY_BYTES = 4096 * 2 * 32 * 32 * 128 * 2
 
 
 def kernel_avgs(path: str) -> dict:
