@@ -15,7 +15,8 @@
  *   block_tables       int32 [num_seqs][max_blocks_per_seq]; entry j of row s is the physical
  *                      block that holds tokens j*B .. j*B+B-1 of sequence s ([PA-summary]
  *                      "Key idea: virtual memory for the KV cache"; [PA-tutorial] §2.1 PageTable).
- *                      Entries at or beyond ceil(context_lens[s]/B) are never read.
+ *                      Entries at or beyond ceil(context_lens[s]/B) never affect the result
+ *                      (they may be read, never beyond max_blocks_per_seq).
  *   context_lens       int32 [num_seqs]; T_s, the number of cached tokens of sequence s.
  *   slot_mapping       int32 [n_tokens]; slot = physical_block*block_size + offset_in_block
  *                      ([PA-tutorial] §3.1 append_kv: page = pos // page_size, offset =
@@ -86,7 +87,7 @@ pa_status pa_write_kv(void *k_cache, void *v_cache, const void *k_new, const voi
 
 /*
  * pa_decode_workspace_size — bytes of device workspace pa_decode needs for these sizes.
- * The workspace holds per-partition partial results (running max, running sum and partial
+ * The workspace holds the per-partition partial results (running max, running sum and partial
  * output, fp32) of every (sequence, query head).
  * partition_tokens: 0 = let the library choose (the same choice pa_decode makes for the same
  * arguments); > 0 must be a multiple of 32 and at most 64*4*block_size tokens (fp32 and
@@ -116,8 +117,8 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
  * on the same stream merges them with the same log-sum-exp rescaling.
  * max_context_len: a host-known upper bound on context_lens (sizes the grid; no device read).
  * workspace: device buffer of >= pa_decode_workspace_size(...) bytes, 256-byte aligned, any
- * contents (NULL when that size is 0). One workspace serves any number of calls ordered on
- * one stream; calls that may overlap in time must not share one.
+ * contents (may be NULL when that size is 0). One workspace serves any number of calls
+ * ordered on one stream; calls that may overlap in time must not share one.
  */
 pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
                     const int32_t *block_tables, const int32_t *context_lens, float scale,

@@ -114,8 +114,8 @@ def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, bloc
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
               workspace=None, partition_tokens=0, stream=None) -> None:
     """out, q [S, Hq, d]; pools [N, Hkv, B, d]; block_tables int32 [S, M]; context_lens int32
-    [S]; workspace: a device uint8 tensor of >= pa_decode_workspace_size bytes (any contents;
-    None when that size is 0)."""
+    [S]; workspace: a device uint8 tensor of >= pa_decode_workspace_size bytes (any
+    contents; None when that size is 0)."""
     S, Hq, d = q.shape
     N, Hkv, B, _ = k_cache.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -185,9 +185,25 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
   __shared__ float lds_m[NW], lds_l[NW];
   __shared__ float lds_fm[1], lds_fl[1];
 
-  const int p = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
-  const int T = seq_len(a, s, BS);
+  const int p = blockIdx.x, h = blockIdx.y;
+  const int s = blockIdx.z;
   const int P = a.partition_tokens;
+  const int jb0 = p * (P / BS);
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id();
+  const int c = lane % R, r = lane / R;
+  // Issued before the context length is known, so the id, query and length loads overlap:
+  // lane k takes the id of this wave's k-th block of the partition (when inside the table).
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  int my_id = 0;
+  {
+    const int j = jb0 + w + lane * NW;
+    if (lane < (P / BS + NW - 1) / NW && j < a.max_blocks_per_seq) my_id = bt[j];
+  }
+  const u32x4 qraw =
+      load16((const char*)a.q + (((int64_t)s * a.num_q_heads + h) * D + c * VEC) * E);
+
+  const int T = seq_len(a, s, BS);
   const int nparts = (T + P - 1) / P;
   if (T == 0) {
     if (p == 0) store_zeros<dt, D, NT>(a, s, h, 1);
@@ -197,17 +213,11 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
   const int kvh = h / (a.num_q_heads / a.num_kv_heads);
   const int t0 = p * P;
   const int t1 = (T < t0 + P) ? T : t0 + P;
-  const int jb0 = t0 / BS, jb1 = (t1 + BS - 1) / BS;
-  const int lane = threadIdx.x & 63;
-  const int w = wave_id();
-  const int c = lane % R, r = lane / R;
+  const int jb1 = (t1 + BS - 1) / BS;
 
   float qf[VEC];
   {
-    const char* qp =
-        (const char*)a.q + (((int64_t)s * a.num_q_heads + h) * D + c * VEC) * E;
-    const u32x4 raw = load16(qp);
-    const uint32_t wq[4] = {raw[0], raw[1], raw[2], raw[3]};
+    const uint32_t wq[4] = {qraw[0], qraw[1], qraw[2], qraw[3]};
 #pragma unroll
     for (int e = 0; e < VEC; ++e) qf[e] = elem_of<dt>(wq, e) * a.scale_log2;
   }
@@ -219,9 +229,6 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
 
   // This wave takes blocks jb0 + w + k*NW, k < nb; lane k holds the k-th physical id.
   const int nb = (jb1 - jb0 - w + NW - 1) / NW;
-  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  int my_id = 0;
-  if (lane < nb) my_id = bt[jb0 + w + lane * NW];
   const char* kbase = (const char*)a.k_cache;
   const char* vbase = (const char*)a.v_cache;
   constexpr int row_bytes = D * E;
@@ -381,29 +388,30 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
   __shared__ float lds_m[NW][16], lds_l[NW][16];
   __shared__ float lds_fm[16], lds_fl[16];
 
-  const int p = blockIdx.x, unit = blockIdx.y, s = blockIdx.z;
+  const int p = blockIdx.x, unit = blockIdx.y;
+  const int s = blockIdx.z;
   const int Hq = a.num_q_heads;
   const int g = Hq / a.num_kv_heads;
   const int ntile = (g + 15) / 16;
   const int kvh = unit / ntile, ht = unit % ntile;
   const int h0 = kvh * g + ht * 16;
   const int nh = (g - ht * 16 < 16) ? g - ht * 16 : 16;
-  const int T = seq_len(a, s, BS);
   const int P = a.partition_tokens;
-  const int nparts = (T + P - 1) / P;
-  if (T == 0) {
-    if (p == 0) store_zeros<dt, D, NT>(a, s, h0, nh);
-    return;
-  }
-  if (p >= nparts) return;
-  const int t0 = p * P;
-  const int t1 = (T < t0 + P) ? T : t0 + P;
-  const int st0 = t0 / 32, st1 = (t1 + 31) / 32;
-  const int jlast = (t1 - 1) / BS;
+  const int st0 = p * (P / 32);
   const int lane = threadIdx.x & 63;
   const int w = wave_id();
   const int hh = lane & 15, gq = lane >> 4;
 
+  // Issued before the context length is known, so the id, query and length loads overlap:
+  // lane k takes the NBS block ids of this wave's k-th 32-token step (when inside the table).
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  int my_id[NBS];
+#pragma unroll
+  for (int b = 0; b < NBS; ++b) {
+    my_id[b] = 0;
+    const int j = (st0 + w + lane * NW) * (32 / BS) + b;
+    if (lane < (P / 32 + NW - 1) / NW && j < a.max_blocks_per_seq) my_id[b] = bt[j];
+  }
   // Q^T operand: column hh = query head h0 + hh, k = head dims 32*kk + 8*gq + e.
   vec8 qop[KC];
 #pragma unroll
@@ -415,6 +423,17 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
     qop[kk] = __builtin_bit_cast(vec8, raw);
   }
 
+  const int T = seq_len(a, s, BS);
+  const int nparts = (T + P - 1) / P;
+  if (T == 0) {
+    if (p == 0) store_zeros<dt, D, NT>(a, s, h0, nh);
+    return;
+  }
+  if (p >= nparts) return;
+  const int t1 = (T < (p + 1) * P) ? T : (p + 1) * P;
+  const int st1 = (t1 + 31) / 32;
+  const int jlast = (t1 - 1) / BS;  // last block of this partition
+
   f32x4 oacc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -422,17 +441,6 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
 
   // This wave takes steps st0 + w + k*NW, k < ns; lane k holds the NBS physical ids of step k.
   const int ns = (st1 - st0 - w + NW - 1) / NW;
-  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  int my_id[NBS];
-#pragma unroll
-  for (int b = 0; b < NBS; ++b) {
-    my_id[b] = 0;
-    if (lane < ns) {
-      int j = (st0 + w + lane * NW) * 32 / BS + b;
-      j = (j < jlast) ? j : jlast;  // never read the table past this partition's last block
-      my_id[b] = bt[j];
-    }
-  }
   const char* kbase = (const char*)a.k_cache;
   const char* vbase = (const char*)a.v_cache;
   const int64_t Hkv = a.num_kv_heads;
@@ -447,11 +455,14 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
   auto fetch = [&](int k, StepRegs<D, KC>& R) {
     const char* kt[NBS];
     const char* vt[NBS];
+    const int jfirst = (st0 + w + k * NW) * (32 / BS);
 #pragma unroll
     for (int b = 0; b < NBS; ++b) {
-      const int64_t tile =
-          (clamp_block(__builtin_amdgcn_readlane(my_id[b], k), a.num_blocks) * Hkv + kvh) *
-          tile_bytes;
+      // a block past this partition's last one holds no valid token: read the step's first
+      // block instead (its tokens are masked), never an id beyond the sequence's blocks
+      const int32_t id = (jfirst + b <= jlast) ? __builtin_amdgcn_readlane(my_id[b], k)
+                                               : __builtin_amdgcn_readlane(my_id[0], k);
+      const int64_t tile = (clamp_block(id, a.num_blocks) * Hkv + kvh) * tile_bytes;
       kt[b] = kbase + tile;
       vt[b] = vbase + tile;
     }
