@@ -41,6 +41,8 @@ WORKLOADS = {
                "d=128, B=32, 1297 tokens each"),
     "tiny": ("config1", "tiny fp32 decode: 4 seqs (7,16,33,50), 8 heads, d=64, B=16"),
     "copy": (None, "plain copy calibration: pa_copy_blocks of 4096 blocks of 256 KiB"),
+    "swap": (None, "preemption swap: pa_swap_blocks of 2048 blocks of 160 KiB (40 heads, B=16, "
+             "d=128, fp16) device -> pinned host and back"),
 }
 
 DECODE_SOURCES = ["paged_kv_cache_82_amd/csrc/pa_decode.hip",
@@ -153,6 +155,42 @@ def run_copy_calibration(args):
                       "bytes_written_per_launch": nbytes // 2, "GB_per_s": nbytes / dt / 1e9}))
 
 
+def run_swap(args):
+    """Swap-out (device -> pinned host) and swap-in (host -> device) rates of pa_swap_blocks.
+    The bound is the host link, not HBM."""
+    import torch
+
+    import paged_kv_cache_82_amd as pa
+
+    dev = torch.device("cuda")
+    n, H, B, d = 2048, 40, 16, 128
+    k = torch.randn((n, H, B, d), device=dev).half()
+    v = torch.randn((n, H, B, d), device=dev).half()
+    hk = torch.empty((n, H, B, d), dtype=torch.float16).pin_memory()
+    hv = torch.empty_like(hk).pin_memory()
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(0))
+    out_pairs = torch.stack([perm, torch.arange(n)], 1).int().to(dev)
+    in_pairs = torch.stack([torch.arange(n), perm], 1).int().to(dev)
+    nbytes = 2 * n * H * B * d * 2
+    res = {}
+    for name, fn in (("out", lambda: pa.pa_swap_blocks(hk, hv, k, v, out_pairs)),
+                     ("in", lambda: pa.pa_swap_blocks(k, v, hk, hv, in_pairs))):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        dt = e0.elapsed_time(e1) / 1e3 / args.steps
+        res[f"swap_{name}_GB_per_s"] = round(nbytes / dt / 1e9, 2)
+        res[f"swap_{name}_ms"] = round(dt * 1e3, 4)
+    print(json.dumps({"metric": "pa_swap_blocks device<->pinned host", "bytes_per_call": nbytes,
+                      **res}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,6 +224,8 @@ def main():
     pa.load()
     if args.workload == "copy":
         return run_copy_calibration(args)
+    if args.workload == "swap":
+        return run_swap(args)
 
     t_gen = time.perf_counter()
     step = make_workload(args.workload, poison=False, placement=args.placement)

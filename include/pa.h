@@ -141,6 +141,26 @@ pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *block_pair
                          int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
                          pa_dtype dt, void *stream);
 
+/*
+ * pa_swap_blocks — move whole blocks between two block pools, e.g. out of the GPU pool into a
+ * pinned host pool and back.
+ * [PA-summary] "vLLM: the serving system built on PagedAttention": when GPU memory runs short
+ * the scheduler can pause a lower-priority request by moving its blocks to CPU memory (or by
+ * freeing them to recompute later); the blocks come back before the request resumes, at new
+ * physical positions recorded in its block table.
+ * For each pair p < n_pairs with src = block_pairs[p][0], dst = block_pairs[p][1]:
+ *   dst_k[dst] = src_k[src] and dst_v[dst] = src_v[src], whole blocks, bit-exact.
+ * The two pools share (num_kv_heads, block_size, head_dim, dt) and have their own block counts.
+ * Each pool may be device memory or pinned host memory (hipHostMalloc, mapped into the device
+ * address space); block_pairs must be device-accessible too. Pairs with an id outside its
+ * pool are skipped; a repeated dst, or the same buffer as both src and dst pool with a dst that
+ * is also a src, is a caller error. n_pairs == 0 is a valid no-op.
+ */
+pa_status pa_swap_blocks(void *dst_k, void *dst_v, int64_t dst_num_blocks, const void *src_k,
+                         const void *src_v, int64_t src_num_blocks, const int32_t *block_pairs,
+                         int n_pairs, int num_kv_heads, int head_dim, int block_size,
+                         pa_dtype dt, void *stream);
+
 /* Static, never-null description of a status code. */
 const char *pa_status_string(pa_status s);
 

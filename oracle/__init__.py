@@ -15,7 +15,7 @@ invariants, brute force on tiny inputs, and a mutation test showing that planted
 a pin). No function is "parity unpinned".
 """
 from .core import (build, copy_blocks, decode, lib_path, num_threads, round_to, run_step,
-                   widen, write_kv)
+                   swap_blocks, widen, write_kv)
 
 __all__ = ["build", "copy_blocks", "decode", "lib_path", "num_threads", "round_to", "run_step",
-           "widen", "write_kv"]
+           "swap_blocks", "widen", "write_kv"]

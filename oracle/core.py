@@ -54,9 +54,11 @@ def _load(path: str | None = None) -> ctypes.CDLL:
         lib.oracle_decode.argtypes = [P, P, P, P, P, P, D, I, I, I, I, I, I, I64, I, P, I]
         lib.oracle_write_kv.argtypes = [P, P, P, P, P, I, I, I, I, I64, I]
         lib.oracle_copy_blocks.argtypes = [P, P, P, I, I, I, I, I64, I]
+        lib.oracle_swap_blocks.argtypes = [P, P, I64, P, P, I64, P, I, I, I, I, I]
         lib.oracle_round.argtypes = [P, P, I64, I]
         lib.oracle_widen.argtypes = [P, P, I64, I]
         for f in (lib.oracle_decode, lib.oracle_write_kv, lib.oracle_copy_blocks,
+                  lib.oracle_swap_blocks,
                   lib.oracle_round, lib.oracle_widen, lib.oracle_num_threads):
             f.restype = I
         _libs[path] = lib
@@ -143,6 +145,20 @@ def copy_blocks(k_cache, v_cache, pairs, dtype: str, lib: str | None = None):
     rc = _load(lib).oracle_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(pr), len(pr), Hkv, d,
                                        B, N, k_cache.itemsize)
     _check(rc, "copy_blocks")
+
+
+def swap_blocks(dst_k, dst_v, src_k, src_v, pairs, dtype: str, lib: str | None = None):
+    """In-place whole-block moves between two pools: dst[pair[1]] = src[pair[0]]."""
+    for name, a in (("dst_k", dst_k), ("dst_v", dst_v), ("src_k", src_k), ("src_v", src_v)):
+        _need(a, dtype, name)
+    Nd, Hkv, B, d = dst_k.shape
+    if src_k.shape[1:] != dst_k.shape[1:]:
+        raise ValueError("pools differ in block shape")
+    pr = np.ascontiguousarray(pairs, np.int32).reshape(-1, 2)
+    rc = _load(lib).oracle_swap_blocks(_ptr(dst_k), _ptr(dst_v), Nd, _ptr(src_k), _ptr(src_v),
+                                       src_k.shape[0], _ptr(pr), len(pr), Hkv, d, B,
+                                       dst_k.itemsize)
+    _check(rc, "swap_blocks")
 
 
 def run_step(step, seq_list=None, in_place: bool = False, lib: str | None = None):

@@ -272,6 +272,33 @@ int oracle_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int n
   return 0;
 }
 
+/* ---- block swap between two pools: [PA-summary] "vLLM" (preemption moves a request's
+ * blocks to CPU memory and back) ------------------------------------------------------------ */
+
+/* dst_pool[dst] = src_pool[src] for K and V, whole blocks. Pairs with an id outside its pool
+ * are skipped; a repeated dst is an error. */
+int oracle_swap_blocks(void *dst_k, void *dst_v, int64_t dst_num_blocks, const void *src_k,
+                       const void *src_v, int64_t src_num_blocks, const int32_t *pairs,
+                       int n_pairs, int num_kv_heads, int head_dim, int block_size,
+                       int elem_bytes) {
+  if (n_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      dst_num_blocks < 0 || src_num_blocks < 0 || (elem_bytes != 2 && elem_bytes != 4))
+    return -1;
+  for (int i = 0; i < n_pairs; ++i)
+    for (int k = i + 1; k < n_pairs; ++k)
+      if (pairs[2 * i + 1] == pairs[2 * k + 1]) return -3;
+  const size_t block_bytes = (size_t)num_kv_heads * block_size * head_dim * elem_bytes;
+  for (int i = 0; i < n_pairs; ++i) {
+    const int64_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+    if (src < 0 || src >= src_num_blocks || dst < 0 || dst >= dst_num_blocks) continue;
+    memcpy((char *)dst_k + dst * block_bytes, (const char *)src_k + src * block_bytes,
+           block_bytes);
+    memcpy((char *)dst_v + dst * block_bytes, (const char *)src_v + src * block_bytes,
+           block_bytes);
+  }
+  return 0;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

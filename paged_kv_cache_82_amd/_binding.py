@@ -57,6 +57,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.pa_decode.restype = I
         lib.pa_copy_blocks.argtypes = [P, P, P, I, I, I, I, I64, I, P]
         lib.pa_copy_blocks.restype = I
+        lib.pa_swap_blocks.argtypes = [P, P, I64, P, P, I64, P, I, I, I, I, I, P]
+        lib.pa_swap_blocks.restype = I
         lib.pa_status_string.argtypes = [I]
         lib.pa_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -132,3 +134,15 @@ def pa_copy_blocks(k_cache, v_cache, block_pairs, stream=None) -> None:
     _check("pa_copy_blocks", load().pa_copy_blocks(
         _ptr(k_cache), _ptr(v_cache), _ptr(block_pairs), block_pairs.shape[0], Hkv, d, B, N,
         _dtype_code(k_cache), _stream(stream)))
+
+
+def pa_swap_blocks(dst_k, dst_v, src_k, src_v, block_pairs, stream=None) -> None:
+    """Whole-block moves between two pools [N, Hkv, B, d] (device or pinned host tensors);
+    block_pairs int32 [n, 2] of (src, dst), on the device."""
+    Nd, Hkv, B, d = dst_k.shape
+    Ns = src_k.shape[0]
+    if tuple(src_k.shape[1:]) != (Hkv, B, d) or src_k.dtype != dst_k.dtype:
+        raise ValueError("pools differ in block shape or dtype")
+    _check("pa_swap_blocks", load().pa_swap_blocks(
+        _ptr(dst_k), _ptr(dst_v), Nd, _ptr(src_k), _ptr(src_v), Ns, _ptr(block_pairs),
+        block_pairs.shape[0], Hkv, d, B, _dtype_code(dst_k), _stream(stream)))

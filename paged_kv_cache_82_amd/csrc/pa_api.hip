@@ -195,8 +195,32 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pair
   if (!k_cache || !v_cache || !block_pairs) return PA_ERR_INVALID_ARG;
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_pairs, 4))
     return PA_ERR_INVALID_ARG;
-  return from_hip(pa::launch_copy_blocks(k_cache, v_cache, block_pairs, n_pairs, block_bytes,
-                                         num_blocks, (hipStream_t)stream));
+  return from_hip(pa::launch_copy_blocks(k_cache, v_cache, num_blocks, k_cache, v_cache,
+                                         num_blocks, block_pairs, n_pairs, block_bytes,
+                                         (hipStream_t)stream));
+}
+
+pa_status pa_swap_blocks(void* dst_k, void* dst_v, int64_t dst_num_blocks, const void* src_k,
+                         const void* src_v, int64_t src_num_blocks, const int32_t* block_pairs,
+                         int n_pairs, int num_kv_heads, int head_dim, int block_size,
+                         pa_dtype dt, void* stream) {
+  if (!valid_dtype(dt)) return PA_ERR_INVALID_ARG;
+  if (n_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      dst_num_blocks <= 0 || src_num_blocks <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (pool_elems(dst_num_blocks, num_kv_heads, block_size, head_dim) < 0 ||
+      pool_elems(src_num_blocks, num_kv_heads, block_size, head_dim) < 0)
+    return PA_ERR_INVALID_ARG;
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elem_bytes(dt);
+  if (block_bytes % 16) return PA_ERR_UNSUPPORTED;
+  if (n_pairs == 0) return PA_OK;
+  if (!dst_k || !dst_v || !src_k || !src_v || !block_pairs) return PA_ERR_INVALID_ARG;
+  if (!aligned(dst_k, 16) || !aligned(dst_v, 16) || !aligned(src_k, 16) || !aligned(src_v, 16) ||
+      !aligned(block_pairs, 4))
+    return PA_ERR_INVALID_ARG;
+  return from_hip(pa::launch_copy_blocks(dst_k, dst_v, dst_num_blocks, src_k, src_v,
+                                         src_num_blocks, block_pairs, n_pairs, block_bytes,
+                                         (hipStream_t)stream));
 }
 
 }  // extern "C"

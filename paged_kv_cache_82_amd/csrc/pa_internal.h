@@ -49,7 +49,10 @@ hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, cons
                            const int32_t* slot_mapping, int n_tokens, int num_kv_heads,
                            int row_bytes, int block_size, int64_t num_blocks,
                            hipStream_t stream);
-hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int n_pairs,
-                              int64_t block_bytes, int64_t num_blocks, hipStream_t stream);
+// Whole-block copies dst[pairs[p][1]] = src[pairs[p][0]] for K and V (same or separate pools).
+hipError_t launch_copy_blocks(void* dst_k, void* dst_v, int64_t dst_num_blocks,
+                              const void* src_k, const void* src_v, int64_t src_num_blocks,
+                              const int32_t* pairs, int n_pairs, int64_t block_bytes,
+                              hipStream_t stream);
 
 }  // namespace pa

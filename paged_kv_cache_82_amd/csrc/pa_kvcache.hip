@@ -39,19 +39,21 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
 }
 
 // grid = (chunk groups, n_pairs, 2 for K|V); each thread copies kUnroll chunks spaced a
-// workgroup apart, so a workgroup covers kUnroll * 256 * 16 bytes of one block.
+// workgroup apart, so a workgroup covers kUnroll * 256 * 16 bytes of one block. Source and
+// destination pools may be the same (copy-on-write) or different (swap to/from host memory).
 constexpr int kCopyUnroll = 4;
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(
-    void* __restrict__ k_cache, void* __restrict__ v_cache, const int32_t* __restrict__ pairs,
-    int64_t chunks_per_block, int64_t num_blocks) {
+    void* dst_k, void* dst_v, int64_t dst_num_blocks,
+    const void* src_k, const void* src_v, int64_t src_num_blocks,
+    const int32_t* __restrict__ pairs, int64_t chunks_per_block) {
   const int pair = blockIdx.y;
   const int64_t src = pairs[2 * pair];
   const int64_t dst = pairs[2 * pair + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  u32x4* base = reinterpret_cast<u32x4*>(blockIdx.z == 0 ? k_cache : v_cache);
-  const u32x4* from = base + src * chunks_per_block;
-  u32x4* to = base + dst * chunks_per_block;
+  if (src < 0 || src >= src_num_blocks || dst < 0 || dst >= dst_num_blocks) return;
+  const u32x4* from =
+      reinterpret_cast<const u32x4*>(blockIdx.z == 0 ? src_k : src_v) + src * chunks_per_block;
+  u32x4* to = reinterpret_cast<u32x4*>(blockIdx.z == 0 ? dst_k : dst_v) + dst * chunks_per_block;
   const int64_t first = (int64_t)blockIdx.x * (kCopyUnroll * 256) + threadIdx.x;
   u32x4 tmp[kCopyUnroll];
 #pragma unroll
@@ -81,8 +83,10 @@ hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, cons
                          stream);
 }
 
-hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int n_pairs,
-                              int64_t block_bytes, int64_t num_blocks, hipStream_t stream) {
+hipError_t launch_copy_blocks(void* dst_k, void* dst_v, int64_t dst_num_blocks,
+                              const void* src_k, const void* src_v, int64_t src_num_blocks,
+                              const int32_t* pairs, int n_pairs, int64_t block_bytes,
+                              hipStream_t stream) {
   if (n_pairs == 0) return hipSuccess;
   const int64_t chunks = block_bytes / 16;
   const int64_t per_wg = kCopyUnroll * 256;
@@ -92,7 +96,8 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs
     const int n = (n_pairs - first < 65535) ? (n_pairs - first) : 65535;
     const int32_t* batch = pairs + 2 * (int64_t)first;
     int64_t chunks_per_block = chunks;
-    void* args[] = {&k_cache, &v_cache, (void*)&batch, &chunks_per_block, &num_blocks};
+    void* args[] = {&dst_k, &dst_v, &dst_num_blocks, (void*)&src_k, (void*)&src_v,
+                    &src_num_blocks, (void*)&batch, &chunks_per_block};
     const hipError_t e = hipLaunchKernel((const void*)copy_blocks_kernel,
                                          dim3((unsigned)gx, (unsigned)n, 2), dim3(256), args, 0,
                                          stream);

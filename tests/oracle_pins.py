@@ -19,6 +19,8 @@ mutation test). What pins what:
                  prefix blocks vs private copies ([PA-summary] "Memory sharing: copy-on-write")
   write / copy   vs numpy fancy-index assignment, everything else untouched, invalid inputs
                  rejected
+  swap           moves between two pools vs numpy assignment, a round trip out and back in
+                 restores the contents ([PA-summary] "vLLM": preemption by swapping to CPU)
 """
 from __future__ import annotations
 
@@ -378,6 +380,36 @@ def pin_copy_blocks_vs_numpy(lib):
         except ValueError:
             continue
         raise AssertionError(f"overlapping pairs accepted: {bad}")
+
+
+def pin_swap_blocks_vs_numpy(lib):
+    rng = np.random.default_rng(23)
+    for dt in ("f16", "f32"):
+        H, B, d = 2, 4, 8
+        dev_k = to_storage(rng.standard_normal((9, H, B, d)), dt)
+        dev_v = to_storage(rng.standard_normal((9, H, B, d)), dt)
+        host_k = to_storage(rng.standard_normal((5, H, B, d)), dt)
+        host_v = to_storage(rng.standard_normal((5, H, B, d)), dt)
+        out_pairs = np.array([[3, 0], [8, 4], [1, 2], [2, 77]], np.int32)  # last one skipped
+        ek, ev = host_k.copy(), host_v.copy()
+        for s_, t in out_pairs[:3]:
+            ek[t] = dev_k[s_]
+            ev[t] = dev_v[s_]
+        oracle.swap_blocks(host_k, host_v, dev_k, dev_v, out_pairs, dt, lib=lib)
+        assert np.array_equal(host_k.view(np.uint8), ek.view(np.uint8))
+        assert np.array_equal(host_v.view(np.uint8), ev.view(np.uint8))
+        # and back into other device blocks: the round trip restores the contents
+        back = np.array([[0, 5], [4, 6], [2, 7]], np.int32)
+        oracle.swap_blocks(dev_k, dev_v, host_k, host_v, back, dt, lib=lib)
+        for (s_, _), (_, t) in zip(out_pairs[:3], back):
+            assert np.array_equal(dev_k[t].view(np.uint8), dev_k[s_].view(np.uint8)) or s_ == t
+    try:
+        oracle.swap_blocks(host_k, host_v, dev_k, dev_v, np.array([[0, 1], [2, 1]], np.int32),
+                           dt, lib=lib)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("repeated destination accepted")
 
 
 def pin_allocator_tables(lib):

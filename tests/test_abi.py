@@ -19,6 +19,13 @@ F32, F16, BF16 = 0, 1, 2
 
 @pytest.fixture(scope="module")
 def lib():
+    """The library, for calls that must fail their host-side checks. The fake pointers below
+    are never valid device memory, so these tests refuse to run where a GPU is visible: a call
+    that wrongly passed its checks would launch on them."""
+    import torch
+
+    if torch.cuda.device_count() > 0:  # counts devices without initialising the runtime
+        pytest.skip("host-side argument checks run only where no GPU is visible")
     if not os.path.exists(pa.lib_path()):
         pa_build.build()
     return pa.load()
@@ -33,7 +40,7 @@ def declared_functions():
 
 def test_header_declares_the_calls():
     assert declared_functions() == ["pa_copy_blocks", "pa_decode", "pa_decode_workspace_size",
-                                    "pa_status_string", "pa_write_kv"]
+                                    "pa_status_string", "pa_swap_blocks", "pa_write_kv"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -124,6 +131,15 @@ def test_copy_blocks_argument_checks(lib):
     assert f(BAD, BAD, None, 3, 8, 128, 16, 10, F16, None) == PA_ERR_INVALID_ARG
     assert f(BAD, BAD, BAD, -3, 8, 128, 16, 10, F16, None) == PA_ERR_INVALID_ARG
     assert f(BAD, BAD, BAD, 3, 0, 128, 16, 10, F16, None) == PA_ERR_INVALID_ARG
+
+
+def test_swap_blocks_argument_checks(lib):
+    f = lib.pa_swap_blocks
+    assert f(BAD, BAD, 8, BAD, BAD, 8, BAD, 0, 8, 128, 16, F16, None) == PA_OK
+    assert f(BAD, BAD, 8, None, BAD, 8, BAD, 2, 8, 128, 16, F16, None) == PA_ERR_INVALID_ARG
+    assert f(BAD, BAD, 0, BAD, BAD, 8, BAD, 2, 8, 128, 16, F16, None) == PA_ERR_INVALID_ARG
+    assert f(BAD, BAD, 8, BAD, BAD, 8, BAD, 2, 8, 128, 16, 7, None) == PA_ERR_INVALID_ARG
+    assert f(V(0x1008), BAD, 8, BAD, BAD, 8, BAD, 2, 8, 128, 16, F16, None) == PA_ERR_INVALID_ARG
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

@@ -186,3 +186,70 @@ def test_copy_blocks_and_write_leave_rest_untouched():
     dst = rng.choice(free, size=3, replace=False)
     step.copies = np.stack([src, dst], axis=1).astype(np.int32)
     _run_and_check(step, what="copy+write")
+
+
+def test_swap_out_and_in_restores_attention():
+    """Preempt a sequence: its blocks go to a pinned host pool, the device blocks are reused
+    (clobbered), the blocks come back at new device positions, the table is repointed, and the
+    attention output is bit-identical to the one before the swap."""
+    step = make_step("swap", 95, [70, 300, 45], 8, 8, 128, 16, "f16", pool_factor=2.5)
+    dev = DevStep(step)
+    before = dev.run()
+    s = 1
+    nblk = (int(step.context_lens[s]) + 15) // 16
+    blocks = step.block_tables[s, :nblk].astype(np.int32)
+    H, B, d = 8, 16, 128
+    host_k = torch.empty((nblk + 3, H, B, d), dtype=torch.float16).pin_memory()
+    host_v = torch.empty_like(host_k).pin_memory()
+    host_k.fill_(float("nan"))
+    host_v.fill_(float("nan"))
+    out_pairs = np.stack([blocks, np.arange(nblk, dtype=np.int32) + 2], 1).astype(np.int32)
+    import paged_kv_cache_82_amd as pa
+    pa.pa_swap_blocks(host_k, host_v, dev.k_cache, dev.v_cache,
+                      torch.from_numpy(out_pairs).cuda())
+    torch.cuda.synchronize()
+    # host side against the oracle's move from the same device pool
+    kc, vc = to_host(dev.k_cache, "f16"), to_host(dev.v_cache, "f16")
+    ek = np.full((nblk + 3, H, B, d), np.nan, np.float16)
+    ev = ek.copy()
+    oracle.swap_blocks(ek, ev, kc, vc, out_pairs, "f16")
+    assert np.array_equal(host_k.numpy().view(np.uint16), ek.view(np.uint16))
+    assert np.array_equal(host_v.numpy().view(np.uint16), ev.view(np.uint16))
+    # the device blocks are reused by someone else
+    idx = torch.from_numpy(blocks.astype(np.int64)).cuda()
+    dev.k_cache.index_fill_(0, idx, float("nan"))
+    dev.v_cache.index_fill_(0, idx, float("nan"))
+    # swap back into free blocks
+    used = set(step.block_tables[step.block_tables >= 0].tolist())
+    free = np.array([b for b in range(step.num_blocks) if b not in used][:nblk], np.int32)
+    in_pairs = np.stack([np.arange(nblk, dtype=np.int32) + 2, free], 1).astype(np.int32)
+    pa.pa_swap_blocks(dev.k_cache, dev.v_cache, host_k, host_v,
+                      torch.from_numpy(in_pairs).cuda())
+    bt = step.block_tables.copy()
+    bt[s, :nblk] = free
+    dev.block_tables.copy_(torch.from_numpy(bt))
+    dev.decode()
+    torch.cuda.synchronize()
+    after = to_host(dev.out, "f16")
+    assert np.array_equal(after.view(np.uint16), before.view(np.uint16))
+
+
+def test_swap_between_device_pools_vs_oracle():
+    rng = np.random.default_rng(96)
+    for dt in ("bf16", "f32"):
+        src = make_step("sw2", 96, [100, 50], 4, 4, 64, 32, dt, poison=False)
+        dev = DevStep(src)
+        dst_k = torch.zeros((7,) + tuple(dev.k_cache.shape[1:]), dtype=dev.k_cache.dtype,
+                            device="cuda")
+        dst_v = torch.zeros_like(dst_k)
+        pairs = np.array([[1, 6], [0, 0], [3, 2], [99, 1], [2, 77]], np.int32)  # 2 skipped
+        import paged_kv_cache_82_amd as pa
+        pa.pa_swap_blocks(dst_k, dst_v, dev.k_cache, dev.v_cache, torch.from_numpy(pairs).cuda())
+        torch.cuda.synchronize()
+        ek = to_host(dst_k, dt).copy()
+        ev = to_host(dst_v, dt).copy()
+        ek[...] = 0
+        ev[...] = 0
+        oracle.swap_blocks(ek, ev, src.k_cache, src.v_cache, pairs, dt)
+        assert np.array_equal(to_host(dst_k, dt).view(np.uint8), ek.view(np.uint8))
+        assert np.array_equal(to_host(dst_v, dt).view(np.uint8), ev.view(np.uint8))

@@ -39,6 +39,7 @@ MUTANTS = [
     ("write_v_missing", "memcpy((char *)v_cache + dst, (const char *)v_new + src, row_bytes);",
      ";"),
     ("copy_v_missing", "memcpy((char *)v_cache + dst * block_bytes", "(void)(v_cache + dst * block_bytes"),
+    ("swap_wrong_src", "(const char *)src_k + src * block_bytes", "(const char *)src_k + dst * block_bytes"),
 ]
 
 _RUNNER = """
