@@ -14,8 +14,8 @@ Every function here is pinned by tests/test_oracle_pins.py (closed forms, librar
 invariants, brute force on tiny inputs, and a mutation test showing that planted mistakes fail
 a pin). No function is "parity unpinned".
 """
-from .core import (build, copy_blocks, decode, lib_path, num_threads, round_to, run_step,
-                   swap_blocks, widen, write_kv)
+from .core import (build, copy_blocks, decode, lib_path, num_threads, prefill, round_to,
+                   run_prefill_step, run_step, swap_blocks, widen, write_kv)
 
-__all__ = ["build", "copy_blocks", "decode", "lib_path", "num_threads", "round_to", "run_step",
-           "swap_blocks", "widen", "write_kv"]
+__all__ = ["build", "copy_blocks", "decode", "lib_path", "num_threads", "prefill", "round_to",
+           "run_prefill_step", "run_step", "swap_blocks", "widen", "write_kv"]

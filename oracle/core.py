@@ -52,12 +52,13 @@ def _load(path: str | None = None) -> ctypes.CDLL:
         lib = ctypes.CDLL(path)
         P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
         lib.oracle_decode.argtypes = [P, P, P, P, P, P, D, I, I, I, I, I, I, I64, I, P, I]
+        lib.oracle_prefill.argtypes = [P, P, P, P, P, P, P, D, I, I, I, I, I, I, I, I64, I]
         lib.oracle_write_kv.argtypes = [P, P, P, P, P, I, I, I, I, I64, I]
         lib.oracle_copy_blocks.argtypes = [P, P, P, I, I, I, I, I64, I]
         lib.oracle_swap_blocks.argtypes = [P, P, I64, P, P, I64, P, I, I, I, I, I]
         lib.oracle_round.argtypes = [P, P, I64, I]
         lib.oracle_widen.argtypes = [P, P, I64, I]
-        for f in (lib.oracle_decode, lib.oracle_write_kv, lib.oracle_copy_blocks,
+        for f in (lib.oracle_decode, lib.oracle_prefill, lib.oracle_write_kv, lib.oracle_copy_blocks,
                   lib.oracle_swap_blocks,
                   lib.oracle_round, lib.oracle_widen, lib.oracle_num_threads):
             f.restype = I
@@ -124,6 +125,33 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, dtype: str,
     return out
 
 
+def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, dtype: str,
+            lib: str | None = None) -> np.ndarray:
+    """Causal multi-query attention in float64, shape [num_q_tokens, Hq, d].
+
+    Query rows query_start[s] .. query_start[s+1]-1 are the last n_s tokens of sequence s
+    (n_s <= context_lens[s]); query i of the sequence attends to positions 0 .. T-n_s+i."""
+    for name, a in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(a, dtype, name)
+    Nq, Hq, d = q.shape
+    N, Hkv, B, d2 = k_cache.shape
+    if d2 != d or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    bt = np.ascontiguousarray(block_tables, np.int32)
+    cl = np.ascontiguousarray(context_lens, np.int32)
+    qs = np.ascontiguousarray(query_start, np.int32)
+    S = len(cl)
+    if len(qs) != S + 1:
+        raise ValueError("query_start must have num_seqs + 1 entries")
+    out = np.zeros((Nq, Hq, d), np.float64)
+    rc = _load(lib).oracle_prefill(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(cl), _ptr(qs),
+        float(scale), S, Nq, Hq, Hkv, d, B, bt.shape[1] if bt.ndim == 2 else 0, N,
+        _CODE[dtype])
+    _check(rc, "prefill")
+    return out
+
+
 def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, dtype: str, lib: str | None = None):
     """In-place slot-mapped write of new keys/values into the pools."""
     for name, a in (("k_cache", k_cache), ("v_cache", v_cache), ("k_new", k_new),
@@ -159,6 +187,18 @@ def swap_blocks(dst_k, dst_v, src_k, src_v, pairs, dtype: str, lib: str | None =
                                        src_k.shape[0], _ptr(pr), len(pr), Hkv, d, B,
                                        dst_k.itemsize)
     _check(rc, "swap_blocks")
+
+
+def run_prefill_step(step, in_place: bool = False, lib: str | None = None):
+    """Apply a PrefillStep's KV writes (the chunk's new tokens) to the pools, then run causal
+    multi-query attention. Returns (out64, k_cache, v_cache)."""
+    kc = step.k_cache if in_place else step.k_cache.copy()
+    vc = step.v_cache if in_place else step.v_cache.copy()
+    for w in step.writes:
+        write_kv(kc, vc, w.k_new, w.v_new, w.slot_mapping, step.dtype, lib)
+    out = prefill(step.q, kc, vc, step.block_tables, step.context_lens, step.query_start,
+                  step.scale, step.dtype, lib)
+    return out, kc, vc
 
 
 def run_step(step, seq_list=None, in_place: bool = False, lib: str | None = None):

@@ -1,5 +1,6 @@
 /*
- * pa_oracle.c — plain, slow CPU oracle for paged decode attention, KV write and block copy.
+ * pa_oracle.c — plain, slow CPU oracle for paged decode attention, causal multi-query (prefill)
+ * attention over the same pool, KV write, block copy and block swap.
  *
  * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's CPU-baseline
  * leg load this library. The product (libpa) neither links nor calls it, and the two share no
@@ -21,7 +22,9 @@
  *     valid_len in [PA-tutorial] §3.2);
  *   - query head h uses KV head h / (Hq/Hkv) (grouped heads are not on the pages);
  *   - T == 0 gives a zero output ([PA-tutorial] §3.2 returns zeros without pages);
- *   - a block-table entry that the sequence needs but that is outside the pool is an error.
+ *   - a block-table entry that the sequence needs but that is outside the pool is an error;
+ *   - multi-query attention: the n query tokens of a sequence are its last n cached tokens and
+ *     query i sees positions 0 .. T-n+i (the causal rule; a decode step is n = 1).
  *
  * Element types: 0 = IEEE binary32, 1 = IEEE binary16, 2 = bfloat16 (the upper half of a
  * binary32). Every input element is widened exactly to double.
@@ -111,14 +114,14 @@ int oracle_round(double *dst, const double *src, int64_t n, int dtype) {
 
 /* ---- decode attention ------------------------------------------------------------------- */
 
-/* One (sequence, query head): gather, score, softmax, weighted sum. `kbuf` and `vbuf` hold
- * at least T*d doubles. Returns 0 or a negative error. */
-static int decode_one(double *out, const void *q, const void *k_cache, const void *v_cache,
-                      const int32_t *block_tables, const int32_t *context_lens, double scale,
+/* One query vector (row `qtok` of q, query head h) attending to the first T tokens of sequence
+ * s: gather, score, softmax, weighted sum. `kbuf` and `vbuf` hold at least T*d doubles.
+ * Returns 0 or a negative error. */
+static int attend_one(double *out, const void *q, int64_t qtok, const void *k_cache,
+                      const void *v_cache, const int32_t *block_tables, int T, double scale,
                       int s, int h, int num_q_heads, int num_kv_heads, int d, int B,
                       int max_blocks_per_seq, int64_t num_blocks, int dtype, double *kbuf,
                       double *vbuf, double *score) {
-  const int T = context_lens[s];
   const int group = num_q_heads / num_kv_heads;
   const int kv = h / group;
   for (int c = 0; c < d; ++c) out[c] = 0.0;
@@ -140,7 +143,7 @@ static int decode_one(double *out, const void *q, const void *k_cache, const voi
   }
 
   /* Scores s_t = scale * q . K_t. */
-  const int64_t qrow = ((int64_t)s * num_q_heads + h) * d;
+  const int64_t qrow = (qtok * num_q_heads + h) * d;
   for (int t = 0; t < T; ++t) {
     double acc = 0.0;
     for (int c = 0; c < d; ++c) acc += load_elem(q, qrow + c, dtype) * kbuf[(int64_t)t * d + c];
@@ -201,9 +204,79 @@ int oracle_decode(double *out, const void *q, const void *k_cache, const void *v
       const int i = (int)(p / num_q_heads);
       const int h = (int)(p % num_q_heads);
       const int s = seq_list ? seq_list[i] : i;
-      int e = decode_one(out + p * head_dim, q, k_cache, v_cache, block_tables, context_lens,
-                         scale, s, h, num_q_heads, num_kv_heads, head_dim, block_size,
-                         max_blocks_per_seq, num_blocks, dtype, kbuf, vbuf, score);
+      int e = attend_one(out + p * head_dim, q, s, k_cache, v_cache, block_tables,
+                         context_lens[s], scale, s, h, num_q_heads, num_kv_heads, head_dim,
+                         block_size, max_blocks_per_seq, num_blocks, dtype, kbuf, vbuf, score);
+      if (e) {
+#pragma omp atomic write
+        err = e;
+      }
+    }
+    free(kbuf);
+    free(vbuf);
+    free(score);
+  }
+  return err;
+}
+
+/* ---- multi-query (prefill / chunked-prefill) attention ---------------------------------------
+ *
+ * [PA-summary] "The PagedAttention algorithm" runs the block-table walk for each query vector.
+ * When a sequence receives n new tokens at once (a prompt, or a chunk of one), those n tokens
+ * are the last n of its T cached tokens, and each of them is a query vector. Reading (the
+ * pages give no mask explicitly): query i (0 <= i < n) sits at position T - n + i and attends
+ * to the tokens at positions 0 .. T - n + i, itself included -- the causal rule of
+ * autoregressive attention, under which a decode step is the case n = 1.
+ *
+ * q, out rows: query tokens of sequence s are rows query_start[s] .. query_start[s+1]-1 of
+ * q [num_q_tokens][num_q_heads][head_dim]; out is double [num_q_tokens][num_q_heads][head_dim]
+ * (rows no sequence owns are left untouched). query_start is non-decreasing, query_start[0]
+ * >= 0, query_start[num_seqs] <= num_q_tokens, and n_s <= context_lens[s] (error -1 otherwise).
+ */
+int oracle_prefill(double *out, const void *q, const void *k_cache, const void *v_cache,
+                   const int32_t *block_tables, const int32_t *context_lens,
+                   const int32_t *query_start, double scale, int num_seqs, int num_q_tokens,
+                   int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                   int max_blocks_per_seq, int64_t num_blocks, int dtype) {
+  if (num_seqs < 0 || num_q_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || block_size <= 0 || max_blocks_per_seq < 0 || num_blocks < 0 ||
+      dtype < 0 || dtype > 2 || num_q_heads % num_kv_heads != 0)
+    return -1;
+  if (num_seqs > 0 && (query_start[0] < 0 || query_start[num_seqs] > num_q_tokens)) return -1;
+  int max_T = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int n = query_start[s + 1] - query_start[s];
+    if (n < 0 || context_lens[s] < 0 || n > context_lens[s]) return -1;
+    if (context_lens[s] > max_T) max_T = context_lens[s];
+  }
+  /* one work item per (sequence, query token, query head) */
+  const int64_t rows = num_seqs > 0 ? (int64_t)query_start[num_seqs] - query_start[0] : 0;
+  const int64_t items = rows * num_q_heads;
+  int err = 0;
+#pragma omp parallel
+  {
+    double *kbuf = (double *)malloc(sizeof(double) * ((size_t)max_T * head_dim + 1));
+    double *vbuf = (double *)malloc(sizeof(double) * ((size_t)max_T * head_dim + 1));
+    double *score = (double *)malloc(sizeof(double) * ((size_t)max_T + 1));
+    if (!kbuf || !vbuf || !score) {
+#pragma omp atomic write
+      err = -4;
+    }
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t it = 0; it < items; ++it) {
+      if (!kbuf || !vbuf || !score) continue;
+      const int64_t qtok = query_start[0] + it / num_q_heads;
+      const int h = (int)(it % num_q_heads);
+      int s = 0; /* the sequence that owns row qtok */
+      while (query_start[s + 1] <= qtok) ++s;
+      const int T = context_lens[s];
+      const int n = query_start[s + 1] - query_start[s];
+      const int i = (int)(qtok - query_start[s]);
+      const int visible = T - n + i + 1; /* positions 0 .. T-n+i */
+      int e = attend_one(out + qtok * (int64_t)num_q_heads * head_dim + (int64_t)h * head_dim,
+                         q, qtok, k_cache, v_cache, block_tables, visible, scale, s, h,
+                         num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                         num_blocks, dtype, kbuf, vbuf, score);
       if (e) {
 #pragma omp atomic write
         err = e;

@@ -21,6 +21,12 @@ mutation test). What pins what:
                  rejected
   swap           moves between two pools vs numpy assignment, a round trip out and back in
                  restores the contents ([PA-summary] "vLLM": preemption by swapping to CPU)
+  prefill        causal multi-query attention ([PA-summary] "The PagedAttention algorithm" runs
+                 the block-table walk for each query vector) vs torch SDPA (float64, CPU) with
+                 an explicit mask (query i of a chunk of n sees positions <= T-n+i), and with
+                 is_causal=True when the chunk is the whole context; the last query of a chunk
+                 equals the decode oracle; keys/values after a query's position never change
+                 it while its own position's do; placement and block-size invariance
 """
 from __future__ import annotations
 
@@ -32,7 +38,7 @@ import torch
 
 import oracle
 from workloads import (BlockAllocator, Sequence, append_tokens, block_tables_array, config5,
-                       make_step, to_float64, to_storage)
+                       make_prefill_step, make_step, to_float64, to_storage)
 from oracle import blockwise
 
 RTOL = 1e-12
@@ -426,6 +432,109 @@ def pin_allocator_tables(lib):
     assert len(used) == len(set(used))
     bt = block_tables_array(seqs)
     assert bt.shape == (5, 5) and (bt[0, 1:] == -1).all()
+
+
+# ---- multi-query (prefill / chunked-prefill) attention ----------------------------------------
+
+PREFILL_TINY = [
+    # (context lengths, query lengths, Hq, Hkv, d, B, dtype)
+    ([7, 16, 33, 50, 5], [7, 3, 16, 1, 0], 4, 2, 16, 8, "f16"),
+    ([9, 12], [9, 12], 2, 2, 8, 4, "f32"),
+    ([20, 1, 6], [5, 1, 2], 8, 2, 8, 3, "bf16"),
+    ([40, 17], [40, 9], 4, 1, 16, 16, "f32"),
+    ([3, 8], [2, 8], 2, 2, 4, 1, "f16"),
+]
+
+
+def _sdpa_prefill_ref(step, s, is_causal=False):
+    """Standard attention (torch SDPA, float64 CPU) of the query chunk of sequence s on its
+    logical K/V, query i seeing positions 0 .. T-n+i."""
+    T = int(step.context_lens[s])
+    a, b = int(step.query_start[s]), int(step.query_start[s + 1])
+    n = b - a
+    q = torch.from_numpy(to_float64(step.q[a:b], step.dtype)).permute(1, 0, 2)  # [Hq, n, d]
+    k = torch.from_numpy(to_float64(step.logical_k[s], step.dtype))  # [T, Hkv, d]
+    v = torch.from_numpy(to_float64(step.logical_v[s], step.dtype))
+    g = step.num_q_heads // step.num_kv_heads
+    k = k.repeat_interleave(g, dim=1).permute(1, 0, 2).contiguous()  # [Hq, T, d]
+    v = v.repeat_interleave(g, dim=1).permute(1, 0, 2).contiguous()
+    if is_causal:
+        assert n == T
+        o = torch.nn.functional.scaled_dot_product_attention(
+            q.contiguous(), k, v, is_causal=True, scale=float(step.scale))
+    else:
+        mask = torch.arange(T)[None, :] <= (T - n + torch.arange(n))[:, None]  # True = attend
+        o = torch.nn.functional.scaled_dot_product_attention(
+            q.contiguous(), k, v, attn_mask=mask, scale=float(step.scale))
+    return o.permute(1, 0, 2).numpy()  # [n, Hq, d]
+
+
+def _prefill(step, lib):
+    return oracle.run_prefill_step(step, lib=lib)[0]
+
+
+def pin_prefill_vs_sdpa_masked(lib):
+    for i, (T, n, Hq, Hkv, d, B, dt) in enumerate(PREFILL_TINY):
+        step = make_prefill_step("pf", 300 + i, T, n, Hq, Hkv, d, B, dt, keep_logical=True)
+        out = _prefill(step, lib)
+        for s in range(len(T)):
+            a, b = step.query_start[s], step.query_start[s + 1]
+            if b > a:
+                _close(out[a:b], _sdpa_prefill_ref(step, s), what=f"prefill case {i} seq {s}")
+
+
+def pin_prefill_whole_prompt_is_causal(lib):
+    # n == T: the chunk is the whole context; SDPA's own causal mask (top-left aligned, which
+    # equals bottom-right alignment when n == T) is the reference
+    for i, (T, Hq, Hkv, d, B, dt) in enumerate([([9, 12, 1], 2, 2, 8, 4, "f32"),
+                                                  ([33, 16], 8, 2, 16, 16, "bf16")]):
+        step = make_prefill_step("pc", 320 + i, T, T, Hq, Hkv, d, B, dt, keep_logical=True)
+        out = _prefill(step, lib)
+        for s in range(len(T)):
+            a, b = step.query_start[s], step.query_start[s + 1]
+            _close(out[a:b], _sdpa_prefill_ref(step, s, is_causal=True), what=f"causal {i}/{s}")
+
+
+def pin_prefill_last_query_is_decode(lib):
+    step = make_prefill_step("pd", 330, [7, 16, 33, 50], [7, 3, 16, 1], 8, 2, 16, 8, "f16")
+    out, kc, vc = oracle.run_prefill_step(step, lib=lib)
+    last = step.query_start[1:] - 1
+    q_dec = np.ascontiguousarray(step.q[last])  # [S, Hq, d]
+    dec = oracle.decode(q_dec, kc, vc, step.block_tables, step.context_lens, step.scale,
+                        step.dtype, lib=lib)
+    _close(out[last], dec, what="last query vs decode")
+
+
+def pin_prefill_future_tokens_ignored(lib):
+    # Sequence 0: T = 20 with a chunk of n = 6 (positions 14..19). Changing the stored key and
+    # value at position 16 must leave queries 0, 1 (positions 14, 15) bit-identical and change
+    # queries 2.. (positions 16..19).
+    step = make_prefill_step("pfut", 340, [20, 9], [6, 4], 2, 1, 8, 4, "f32")
+    out, kc, vc = oracle.run_prefill_step(step, lib=lib)
+    pos = 16
+    phys = step.block_tables[0, pos // 4]
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[phys, :, pos % 4] += np.float32(3.0)
+    vc2[phys, :, pos % 4] -= np.float32(5.0)
+    out2 = oracle.prefill(step.q, kc2, vc2, step.block_tables, step.context_lens,
+                          step.query_start, step.scale, step.dtype, lib=lib)
+    assert np.array_equal(out2[0:2], out[0:2]), "a query saw a later position"
+    assert np.array_equal(out2[6:], out[6:]), "another sequence changed"
+    for i in range(2, 6):
+        assert np.abs(out2[i] - out[i]).max() > 1e-6, f"query {i} did not see position {pos}"
+
+
+def pin_prefill_placement_and_block_size(lib):
+    outs = []
+    for r in range(3):
+        step = make_prefill_step("ppl", 350, [50, 7, 33], [20, 7, 1], 8, 2, 16, 8, "bf16",
+                                 alloc_rng=np.random.default_rng(2000 + r), pool_factor=2.5)
+        outs.append(_prefill(step, lib))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    for B in (1, 3, 16, 64):
+        step = make_prefill_step("ppl", 350, [50, 7, 33], [20, 7, 1], 8, 2, 16, B, "bf16")
+        _close(_prefill(step, lib), outs[0], what=f"prefill block size {B}")
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -3,8 +3,10 @@
 The pins themselves live in oracle_pins.py. The mutation test compiles copies of the oracle
 with one plausible mistake each (wrong head group, wrong offset or block index, dropped scale,
 flipped exponent sign, keys used as values, no normalisation, no max shift, wrong fp16
-exponent bias, wrong bf16 precision, a write or copy that misses data) and checks that every
-copy fails at least one pin, so the pins would catch such a mistake in the oracle.
+exponent bias, wrong bf16 precision, a write or copy that misses data, a causal mask that is off
+by one, starts at the chunk or is missing, the chunk's first query used for every row) and
+checks that every copy fails at least one pin, so the pins would catch such a mistake in the
+oracle.
 """
 import os
 import subprocess
@@ -40,6 +42,11 @@ MUTANTS = [
      ";"),
     ("copy_v_missing", "memcpy((char *)v_cache + dst * block_bytes", "(void)(v_cache + dst * block_bytes"),
     ("swap_wrong_src", "(const char *)src_k + src * block_bytes", "(const char *)src_k + dst * block_bytes"),
+    ("causal_off_by_one", "const int visible = T - n + i + 1;", "const int visible = T - n + i;"),
+    ("causal_from_chunk_start", "const int visible = T - n + i + 1;", "const int visible = i + 1;"),
+    ("causal_whole_context", "const int visible = T - n + i + 1;", "const int visible = T;"),
+    ("prefill_first_query_row", "q, qtok, k_cache, v_cache, block_tables, visible,",
+     "q, query_start[s], k_cache, v_cache, block_tables, visible,"),
 ]
 
 _RUNNER = """

@@ -107,3 +107,34 @@ def test_config2_config3_metadata_small():
         assert st.k_cache.shape[1] == H
         nblk = (st.block_tables >= 0).sum(axis=1)
         assert (nblk == (st.context_lens + 15) // 16).all()
+
+
+def test_prefill_step_layout():
+    from workloads import make_prefill_step
+
+    st = make_prefill_step("p", 9, [7, 16, 33, 5], [7, 3, 16, 0], 4, 2, 8, 8, "f16")
+    assert list(st.query_start) == [0, 7, 10, 26, 26]
+    assert st.q.shape == (26, 4, 8) and st.num_q_tokens == 26 and st.max_query_len == 16
+    w = st.writes[0]
+    assert len(w.slot_mapping) == 26 and len(set(w.slot_mapping.tolist())) == 26
+    # the chunk's tokens go to positions T-n .. T-1 of each sequence, still poison before
+    k = 0
+    for s, (T, n) in enumerate(zip(st.context_lens, st.query_lens)):
+        for i in range(n):
+            j, off = divmod(int(T - n + i), 8)
+            assert w.slot_mapping[k] == st.block_tables[s, j] * 8 + off
+            assert np.isnan(st.k_cache[st.block_tables[s, j], :, off, :].astype(np.float32)).all()
+            k += 1
+    with pytest.raises(ValueError):
+        make_prefill_step("bad", 9, [4], [5], 2, 2, 8, 8, "f16")
+
+
+def test_prefill_workloads_shapes():
+    from workloads.configs import prefill_gqa, prefill_mha13b
+
+    a = prefill_mha13b(poison=False)
+    assert a.num_seqs == 16 and a.num_q_tokens == 16 * 512 and a.max_context_len <= 2048
+    assert (a.context_lens >= 512).all() and a.dtype == "f16" and a.num_q_heads == 40
+    b = prefill_gqa(poison=False)
+    assert b.num_q_tokens == 16 * 1024 and b.max_context_len <= 4096
+    assert (b.num_q_heads, b.num_kv_heads, b.dtype) == (64, 8, "bf16")

@@ -184,6 +184,158 @@ def make_step(name: str, seed: int, lengths, num_q_heads: int, num_kv_heads: int
     return step
 
 
+# ---- multi-query (prefill / chunked-prefill) steps --------------------------------------------
+
+
+@dataclass
+class PrefillStep:
+    """One chunked-prefill iteration: sequence s already holds its first T_s - n_s tokens; the
+    step writes its next n_s tokens through the slot mapping and runs causal attention for
+    those n_s query tokens (query i of s sees positions 0 .. T_s - n_s + i)."""
+
+    name: str
+    seed: int
+    dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    k_cache: np.ndarray  # [N, Hkv, B, d], state before the step
+    v_cache: np.ndarray
+    q: np.ndarray  # [num_q_tokens, Hq, d], sequences one after another
+    block_tables: np.ndarray  # int32 [S, max_blocks]
+    context_lens: np.ndarray  # int32 [S], T_s after the step's write
+    query_start: np.ndarray  # int32 [S + 1]
+    writes: list = field(default_factory=list)
+    scale: np.float32 = np.float32(0)
+    logical_k: list | None = None
+    logical_v: list | None = None
+    notes: dict = field(default_factory=dict)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.context_lens.shape[0])
+
+    @property
+    def num_q_tokens(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def query_lens(self) -> np.ndarray:
+        return np.diff(self.query_start)
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.query_lens.max()) if self.num_seqs else 0
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.k_cache.shape[0])
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.context_lens.size else 0
+
+    @property
+    def elem_bytes(self) -> int:
+        return ELEM_BYTES[self.dtype]
+
+
+def make_prefill_step(name: str, seed: int, context_lens, query_lens, num_q_heads: int,
+                      num_kv_heads: int, head_dim: int, block_size: int, dtype: str,
+                      num_blocks: int | None = None, pool_factor: float = 1.2,
+                      poison: bool = True, keep_logical: bool = False,
+                      alloc_rng: np.random.Generator | None = None,
+                      scale: float | None = None) -> PrefillStep:
+    """Sequence s ends with T_s = context_lens[s] tokens of which the last n_s = query_lens[s]
+    arrive in this step (keys/values written through the slot mapping, queries in q)."""
+    check_dtype(dtype)
+    T_all = [int(t) for t in context_lens]
+    n_all = [int(n) for n in query_lens]
+    if len(T_all) != len(n_all) or any(n < 0 or n > t for t, n in zip(T_all, n_all)):
+        raise ValueError("need 0 <= query_lens[s] <= context_lens[s]")
+    S, Hkv, d, B = len(T_all), num_kv_heads, head_dim, block_size
+    if num_q_heads % num_kv_heads:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    need = sum(math.ceil(t / B) for t in T_all)
+    if num_blocks is None:
+        num_blocks = max(1, math.ceil(pool_factor * need))
+    if alloc_rng is None:
+        alloc_rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(3,)))
+    alloc = BlockAllocator(num_blocks, alloc_rng)
+    fill = nan_value(dtype) if poison else 0
+    k_cache = full((num_blocks, Hkv, B, d), fill, dtype)
+    v_cache = full((num_blocks, Hkv, B, d), fill, dtype)
+
+    seqs = [Sequence(B) for _ in range(S)]
+    for s in range(S):
+        append_tokens(alloc, seqs[s], T_all[s] - n_all[s])
+
+    def prior(s):
+        T, n = T_all[s], n_all[s]
+        kk = logical_kv(seed, s, T, Hkv, d, dtype, 0)
+        vv = logical_kv(seed, s, T, Hkv, d, dtype, 1)
+        _scatter(k_cache, seqs[s].table, kk[: T - n], 0, B)
+        _scatter(v_cache, seqs[s].table, vv[: T - n], 0, B)
+        return kk, vv
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        res = list(ex.map(prior, range(S)))
+
+    k_new, v_new, slots = [], [], []
+    for s in range(S):
+        T, n = T_all[s], n_all[s]
+        sl, pairs = append_tokens(alloc, seqs[s], n)
+        assert not pairs
+        slots.extend(sl)
+        k_new.append(res[s][0][T - n:])
+        v_new.append(res[s][1][T - n:])
+    shape = (0, Hkv, d)
+    write = KVWrite(
+        np.concatenate(k_new) if k_new else np.empty(shape, STORAGE[dtype]),
+        np.concatenate(v_new) if v_new else np.empty(shape, STORAGE[dtype]),
+        np.asarray(slots, dtype=np.int32),
+    )
+    qs = [to_storage(_normal(seed, (4, s), (n_all[s], num_q_heads, d)), dtype) for s in range(S)]
+    q = np.concatenate(qs) if qs else np.empty((0, num_q_heads, d), STORAGE[dtype])
+    step = PrefillStep(
+        name=name, seed=seed, dtype=dtype, num_q_heads=num_q_heads, num_kv_heads=Hkv,
+        head_dim=d, block_size=B, k_cache=k_cache, v_cache=v_cache,
+        q=np.ascontiguousarray(q), block_tables=block_tables_array(seqs),
+        context_lens=np.asarray(T_all, np.int32),
+        query_start=np.concatenate([[0], np.cumsum(n_all)]).astype(np.int32),
+        writes=[write],
+        scale=np.float32(1.0 / math.sqrt(d) if scale is None else scale),
+    )
+    if keep_logical:
+        step.logical_k = [r[0] for r in res]
+        step.logical_v = [r[1] for r in res]
+    step.notes["blocks_needed"] = need
+    return step
+
+
+def prefill_mha13b(**kw) -> PrefillStep:
+    """Chunked prefill, 13B shape, fp16 MHA: 16 sequences, 40 heads, d=128, B=16; each appends a
+    512-token chunk to a cached prefix of lognormal length (median 512, sigma 1) clipped to
+    [0, 1536], so T <= 2048."""
+    rng = np.random.default_rng(6)
+    prefix = np.clip(np.rint(rng.lognormal(math.log(512.0), 1.0, size=16)), 0, 1536)
+    n = np.full(16, 512)
+    return make_prefill_step("prefill-mha13b-f16", 6, prefix + n, n, 40, 40, 128, 16, "f16", **kw)
+
+
+def prefill_gqa(**kw) -> PrefillStep:
+    """Chunked prefill, GQA bf16: 16 sequences, 64 query heads over 8 KV heads, d=128, B=16;
+    each appends a 1024-token chunk to a cached prefix of length uniform in [0, 3072]."""
+    prefix = np.random.default_rng(7).integers(0, 3072 + 1, size=16)
+    n = np.full(16, 1024)
+    return make_prefill_step("prefill-gqa-bf16", 7, prefix + n, n, 64, 8, 128, 16, "bf16", **kw)
+
+
 # ---- the five workloads ---------------------------------------------------------------------
 
 
