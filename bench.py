@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, vendor figure
+PEAK_MFMA_TFLOPS_16 = 2500.0  # MI355X dense fp16/bf16 matrix peak, vendor figure
 
 WORKLOADS = {
     "mha13b": ("config2", "13B-shape fp16 MHA decode: 64 seqs, 40 heads, d=128, B=16, "
@@ -40,6 +41,11 @@ WORKLOADS = {
     "shared": ("config5", "shared-prefix fp16 decode: 16 prompts x 4 samples, 32 heads, "
                "d=128, B=32, 1297 tokens each"),
     "tiny": ("config1", "tiny fp32 decode: 4 seqs (7,16,33,50), 8 heads, d=64, B=16"),
+    "prefill-mha13b": ("prefill_mha13b", "chunked prefill, 13B shape fp16 MHA: 16 seqs, 40 heads, "
+                       "d=128, B=16, 512-token chunks after lognormal (median 512) prefixes "
+                       "clipped to [0,1536]"),
+    "prefill-gqa": ("prefill_gqa", "chunked prefill, GQA bf16: 16 seqs, 64 query / 8 KV heads, "
+                    "d=128, B=16, 1024-token chunks after prefixes uniform in [0,3072]"),
     "copy": (None, "plain copy calibration: pa_copy_blocks of 4096 blocks of 256 KiB"),
     "swap": (None, "preemption swap: pa_swap_blocks of 2048 blocks of 160 KiB (40 heads, B=16, "
              "d=128, fp16) device -> pinned host and back"),
@@ -130,6 +136,156 @@ def cpu_baseline(step, budget_s: float = 12.0) -> dict:
                       f"of {int(nb['tokens'])} context tokens), fp64 oracle, {reps} passes in "
                       f"{elapsed:.1f} s",
             "seq_tokens_per_s": round(tok / elapsed, 1)}
+
+
+def prefill_flops(step) -> float:
+    """Algorithmic flops of one pa_prefill launch: every (query row, query head, visible token)
+    costs 2d for q.K and 2d for p.V."""
+    qs = step.query_start
+    total = 0
+    for s in range(step.num_seqs):
+        n = int(qs[s + 1] - qs[s])
+        T = int(step.context_lens[s])
+        total += n * (T - n) + n * (n + 1) // 2  # sum over i of (T - n + i + 1)
+    return float(total) * step.num_q_heads * 4.0 * step.head_dim
+
+
+def prefill_cpu_baseline(step, budget_s: float = 12.0) -> dict:
+    """The oracle on this host, on a bounded sample: the chunks of the first sequences, as many
+    as fit about a quarter of the budget per pass, repeated until the budget is spent."""
+    import numpy as np
+
+    import oracle
+    from workloads.configs import PrefillStep
+
+    def sub(nseq):
+        qs = step.query_start
+        return PrefillStep(
+            name=step.name, seed=step.seed, dtype=step.dtype, num_q_heads=step.num_q_heads,
+            num_kv_heads=step.num_kv_heads, head_dim=step.head_dim, block_size=step.block_size,
+            k_cache=step.k_cache, v_cache=step.v_cache, q=step.q[: qs[nseq]],
+            block_tables=step.block_tables[:nseq], context_lens=step.context_lens[:nseq],
+            query_start=qs[: nseq + 1], scale=step.scale)
+
+    def run(st):
+        return oracle.prefill(st.q, st.k_cache, st.v_cache, st.block_tables, st.context_lens,
+                              st.query_start, st.scale, st.dtype)
+
+    t0 = time.perf_counter()
+    run(sub(1))
+    one = max(time.perf_counter() - t0, 1e-4)
+    n = max(1, min(step.num_seqs, int((budget_s / 4) / one)))
+    st = sub(n)
+    reps, elapsed = 0, 0.0
+    t0 = time.perf_counter()
+    while elapsed < budget_s and reps < 1000:
+        run(st)
+        reps += 1
+        elapsed = time.perf_counter() - t0
+    fl = prefill_flops(st) * reps
+    return {"value": round(fl / elapsed / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"causal attention of the chunks of sequences 0..{n - 1} of "
+                      f"{step.num_seqs} ({int(st.query_start[-1])} of {step.num_q_tokens} query "
+                      f"tokens), fp64 oracle, {reps} passes in {elapsed:.1f} s"}
+
+
+def run_prefill(args):
+    """One step = pa_write_kv of every sequence's chunk, then pa_prefill. The bound is the
+    matrix cores (about 2d flops per byte of K/V per query row): the roofline is the dense
+    fp16/bf16 MFMA peak."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_82_amd as pa
+    import workloads
+
+    t_gen = time.perf_counter()
+    step = getattr(workloads, WORKLOADS[args.workload][0])(poison=False)
+    t_gen = time.perf_counter() - t_gen
+    dev = torch.device("cuda")
+
+    def up(a, dt=None):
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    ncopy = max(1, args.pool_copies)
+    kc0, vc0 = up(step.k_cache, step.dtype), up(step.v_cache, step.dtype)
+    pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(ncopy - 1)]
+    q = up(step.q, step.dtype)
+    bt, cl, qs = up(step.block_tables), up(step.context_lens), up(step.query_start)
+    writes = [(up(w.k_new, step.dtype), up(w.v_new, step.dtype), up(w.slot_mapping))
+              for w in step.writes]
+    out = torch.empty_like(q)
+    scale, maxn, maxT = float(step.scale), step.max_query_len, step.max_context_len
+
+    def attend(i):
+        kc, vc = pools[i % ncopy]
+        pa.pa_prefill(out, q, kc, vc, bt, cl, qs, scale, maxn, maxT)
+
+    def one_step(i):
+        kc, vc = pools[i % ncopy]
+        for kn, vn, sm in writes:
+            pa.pa_write_kv(kc, vc, kn, vn, sm)
+        attend(i)
+
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < args.prewarm_s:
+        for i in range(4):
+            one_step(i)
+        torch.cuda.synchronize()
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(args.warmup + i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        attend(i)
+    e1.record()
+    torch.cuda.synchronize()
+    att_s = e0.elapsed_time(e1) / 1e3 / args.steps
+    fl = prefill_flops(step)
+    n_new = step.num_q_tokens
+    res = {
+        "metric": "paged prefill attention: achieved TFLOP/s (% of MFMA peak) + query tokens/s",
+        "value": round(fl / (wall / args.steps) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": step.dtype, "accumulate": "f32",
+        "data": "synthetic (seeded N(0,1) K/V/q; lengths and placement as described)",
+        "config": {
+            "workload": WORKLOADS[args.workload][1],
+            "num_seqs": step.num_seqs, "num_q_heads": step.num_q_heads,
+            "num_kv_heads": step.num_kv_heads, "head_dim": step.head_dim,
+            "block_size": step.block_size, "num_blocks": step.num_blocks,
+            "query_tokens": n_new, "context_tokens": int(step.context_lens.sum()),
+            "max_context_len": maxT, "pool_copies": ncopy, "parallelism": "single GPU",
+        },
+        "query_tokens_per_s": round(n_new / (wall / args.steps), 1),
+        "roofline": {
+            "kernel": "pa_prefill: prefill_mfma_kernel",
+            "bound": "mfma",
+            "achieved": round(fl / att_s / 1e12, 3),
+            "peak": PEAK_MFMA_TFLOPS_16,
+            "unit": "TFLOP/s",
+            "frac": round(fl / att_s / 1e12 / PEAK_MFMA_TFLOPS_16, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": fl,
+            "avg_launch_us": round(att_s * 1e6, 3),
+        },
+        "input_generation_s": round(t_gen, 2),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = prefill_cpu_baseline(step)
+    print(json.dumps(res))
 
 
 def run_copy_calibration(args):
@@ -226,6 +382,8 @@ def main():
         return run_copy_calibration(args)
     if args.workload == "swap":
         return run_swap(args)
+    if args.workload.startswith("prefill"):
+        return run_prefill(args)
 
     t_gen = time.perf_counter()
     step = make_workload(args.workload, poison=False, placement=args.placement)

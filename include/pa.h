@@ -128,6 +128,35 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v
                     size_t workspace_bytes, pa_dtype dt, void *stream);
 
 /*
+ * pa_prefill — causal multi-query (prefill / chunked-prefill) attention over the same block
+ * pool and tables.
+ * [PA-summary] "The PagedAttention algorithm": the kernel walks the block table for each query
+ * vector and merges the blocks with the log-sum-exp rescaling of the block-wise equation.
+ * Here sequence s brings n_s = query_start[s+1] - query_start[s] new tokens at once (a prompt
+ * or a chunk of one). They must already be in the pool (pa_write_kv) as the last n_s of its
+ * T_s = context_lens[s] tokens, and each is a query vector: query i (0 <= i < n_s), row
+ * query_start[s] + i of q, sits at position T_s - n_s + i and attends to positions
+ * 0 .. T_s - n_s + i (the causal rule; a decode step is the case n_s = 1):
+ *   out[r][h] = sum_{t <= p} exp(s_t - M) V_t / sum_{t <= p} exp(s_t - M),
+ *   s_t = scale * q[r][h] . K_t,  K_t = k_cache[block_tables[s][t/B]][h/g][t%B],  p = T_s-n_s+i
+ * computed in fp32 (MFMA) and rounded to nearest-even in `dt`.
+ * q, out: [num_q_tokens][num_q_heads][head_dim], 16-byte aligned; rows that belong to no
+ * sequence are left untouched.
+ * query_start: int32 [num_seqs + 1], device, non-decreasing, within [0, num_q_tokens].
+ * max_query_len: host-known bound on every n_s; max_context_len: on every T_s (they size the
+ * grid; no device read on the host). n_s > T_s or n_s > max_query_len is a caller error: only
+ * min(n_s, T_s, max_query_len) rows are computed.
+ * Supported: dt f16 or bf16 (PA_ERR_UNSUPPORTED for f32), head_dim 64 or 128, block_size 8,
+ * 16 or 32. No workspace. Device indices are clamped as for pa_decode.
+ */
+pa_status pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
+                     const int32_t *block_tables, const int32_t *context_lens,
+                     const int32_t *query_start, float scale, int num_seqs, int num_q_tokens,
+                     int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                     int max_blocks_per_seq, int64_t num_blocks, int max_query_len,
+                     int max_context_len, pa_dtype dt, void *stream);
+
+/*
  * pa_copy_blocks — copy-on-write of shared blocks.
  * [PA-summary] "Memory sharing: copy-on-write for parallel decoding": when a sequence must
  * write into a block it shares with others, only that block is copied to a new physical block

@@ -5,7 +5,9 @@ this package is its thin Python binding. Importing it never falls back to any ot
 path: if the library is missing, calls raise.
 """
 from ._binding import (PAError, lib_path, load, pa_copy_blocks, pa_decode,
-                       pa_decode_workspace_size, pa_status_string, pa_swap_blocks, pa_write_kv)
+                       pa_decode_workspace_size, pa_prefill, pa_status_string, pa_swap_blocks,
+                       pa_write_kv)
 
 __all__ = ["PAError", "lib_path", "load", "pa_copy_blocks", "pa_decode",
-           "pa_decode_workspace_size", "pa_status_string", "pa_swap_blocks", "pa_write_kv"]
+           "pa_decode_workspace_size", "pa_prefill", "pa_status_string", "pa_swap_blocks",
+           "pa_write_kv"]

@@ -55,6 +55,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.pa_decode_workspace_size.restype = SZ
         lib.pa_decode.argtypes = [P, P, P, P, P, P, F, I, I, I, I, I, I, I64, I, I, P, SZ, I, P]
         lib.pa_decode.restype = I
+        lib.pa_prefill.argtypes = [P, P, P, P, P, P, P, F, I, I, I, I, I, I, I, I64, I, I, I, P]
+        lib.pa_prefill.restype = I
         lib.pa_copy_blocks.argtypes = [P, P, P, I, I, I, I, I64, I, P]
         lib.pa_copy_blocks.restype = I
         lib.pa_swap_blocks.argtypes = [P, P, I64, P, P, I64, P, I, I, I, I, I, P]
@@ -126,6 +128,23 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_c
         _ptr(context_lens), float(scale), S, Hq, Hkv, d, B, block_tables.shape[1], N,
         int(max_context_len), int(partition_tokens), _ptr(workspace), ws_bytes,
         _dtype_code(q), _stream(stream)))
+
+
+def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+               max_query_len, max_context_len, stream=None) -> None:
+    """Causal multi-query attention. out, q [Nq, Hq, d]; pools [N, Hkv, B, d]; block_tables
+    int32 [S, M]; context_lens int32 [S]; query_start int32 [S + 1] (rows of q per sequence);
+    max_query_len / max_context_len: host-known bounds on the per-sequence counts."""
+    Nq, Hq, d = q.shape
+    N, Hkv, B, _ = k_cache.shape
+    S = context_lens.shape[0]
+    if query_start.shape[0] != S + 1:
+        raise ValueError("query_start must have num_seqs + 1 entries")
+    _check("pa_prefill", load().pa_prefill(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), _ptr(query_start), float(scale), S, Nq, Hq, Hkv, d, B,
+        block_tables.shape[1], N, int(max_query_len), int(max_context_len), _dtype_code(q),
+        _stream(stream)))
 
 
 def pa_copy_blocks(k_cache, v_cache, block_pairs, stream=None) -> None:

@@ -182,6 +182,57 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   return from_hip(pa::launch_decode(path, (int)dt, head_dim, block_size, a, (hipStream_t)stream));
 }
 
+pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, const int32_t* context_lens,
+                     const int32_t* query_start, float scale, int num_seqs, int num_q_tokens,
+                     int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                     int max_blocks_per_seq, int64_t num_blocks, int max_query_len,
+                     int max_context_len, pa_dtype dt, void* stream) {
+  if (!valid_dtype(dt)) return PA_ERR_INVALID_ARG;
+  if (num_seqs < 0 || num_q_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || block_size <= 0 || max_blocks_per_seq < 0 || num_blocks <= 0 ||
+      max_query_len < 0 || max_context_len < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads) return PA_ERR_INVALID_ARG;
+  if (pool_elems(num_blocks, num_kv_heads, block_size, head_dim) < 0) return PA_ERR_INVALID_ARG;
+  if ((int64_t)num_q_tokens * num_q_heads * head_dim > INT64_MAX / 8) return PA_ERR_INVALID_ARG;
+  if (!pa::prefill_supported((int)dt, head_dim, block_size)) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_q_tokens == 0 || max_query_len == 0 || max_context_len == 0)
+    return PA_OK;
+  if (max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4))
+    return PA_ERR_INVALID_ARG;
+  const int g = num_q_heads / num_kv_heads;
+  const int64_t rows = (int64_t)max_query_len * g;
+  const int per_wg = pa::prefill_rows_per_workgroup();
+  const int64_t row_tiles = (rows + per_wg - 1) / per_wg;
+  if (rows > INT32_MAX || row_tiles * num_kv_heads * (int64_t)num_seqs > INT32_MAX)
+    return PA_ERR_INVALID_ARG;  // one-dimensional grid
+
+  pa::PrefillArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_seqs = num_seqs;
+  a.num_q_tokens = num_q_tokens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_query_len = max_query_len;
+  a.max_context_len = max_context_len;
+  a.row_tiles = (int)row_tiles;
+  return from_hip(pa::launch_prefill((int)dt, head_dim, block_size, a, (hipStream_t)stream));
+}
+
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int n_pairs,
                          int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
                          pa_dtype dt, void* stream) {

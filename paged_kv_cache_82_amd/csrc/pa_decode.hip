@@ -34,6 +34,7 @@
 //     pairing M-tile row r with head dimension (D/16)*r + mt, so no LDS staging is needed.
 #include "pa_device.h"
 #include "pa_internal.h"
+#include "pa_mfma.h"
 
 namespace pa {
 
@@ -45,15 +46,6 @@ __device__ __forceinline__ int seq_len(const DecodeArgs& a, int s, int BS) {
   const int64_t cap64 = (int64_t)a.max_blocks_per_seq * BS;
   const int cap = (int)(cap64 < (int64_t)a.max_context_len ? cap64 : (int64_t)a.max_context_len);
   return T < 0 ? 0 : (T > cap ? cap : T);
-}
-
-__device__ __forceinline__ int64_t clamp_block(int32_t phys, int64_t n) {
-  return phys < 0 ? 0 : (phys >= n ? n - 1 : (int64_t)phys);
-}
-
-// Wave index inside the workgroup as a wave-uniform (scalar) value.
-__device__ __forceinline__ int wave_id() {
-  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
 // After a workgroup has merged its partition into (fm, fl, fo[nh][D]) in LDS: store the final
@@ -320,57 +312,6 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
 }
 
 // ---- MFMA kernel (grouped query heads) -----------------------------------------------------
-
-template <DT dt>
-struct MfmaT;
-template <>
-struct MfmaT<DT::BF16> {
-  using vec8 = bf16x8;
-  using scalar = __bf16;
-  static __device__ __forceinline__ f32x4 mma(vec8 a, vec8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
-template <>
-struct MfmaT<DT::F16> {
-  using vec8 = f16x8;
-  using scalar = _Float16;
-  static __device__ __forceinline__ f32x4 mma(vec8 a, vec8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-  }
-};
-
-// V row fragment of one token: D/16 consecutive head dimensions (16 bytes for D = 128,
-// 8 bytes for D = 64).
-template <int D>
-struct VFrag;
-template <>
-struct VFrag<128> {
-  using T = u32x4;
-  static constexpr int words = 4;
-  static __device__ __forceinline__ T load(const char* p) { return load16(p); }
-};
-template <>
-struct VFrag<64> {
-  using T = u32x2;
-  static constexpr int words = 2;
-  static __device__ __forceinline__ T load(const char* p) { return load8(p); }
-};
-
-// 16-bit element `e` of a V fragment, as raw bits in the low half.
-template <int D>
-__device__ __forceinline__ uint32_t vfrag_elem(const typename VFrag<D>::T& f, int e) {
-  const uint32_t w = f[e >> 1];
-  return (e & 1) ? (w >> 16) : (w & 0xffffu);
-}
-
-// One 32-token step of one wave: loads of tile u hold K rows of tokens 16u + hh (KC chunks)
-// and V rows of tokens 16u + 4*gq + i (i < 4).
-template <int D, int KC>
-struct StepRegs {
-  u32x4 k[2][KC];
-  typename VFrag<D>::T v[2][4];
-};
 
 template <DT dt, int D, int BS, int NW, int NBUF, int MINB>
 __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const DecodeArgs a) {

@@ -69,6 +69,19 @@ __device__ __forceinline__ void store_elem(void* base, int64_t idx, float x) {
   }
 }
 
+// ---- indices ----------------------------------------------------------------------------
+
+// A physical block id clamped into the pool [0, n): a bad id reads the wrong block, never
+// outside the pool.
+__device__ __forceinline__ int64_t clamp_block(int32_t phys, int64_t n) {
+  return phys < 0 ? 0 : (phys >= n ? n - 1 : (int64_t)phys);
+}
+
+// Wave index inside the workgroup as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 // ---- loads ------------------------------------------------------------------------------
 
 __device__ __forceinline__ u32x4 load16(const void* p) {

@@ -45,6 +45,33 @@ int decode_units_per_seq(DecodePath path, int num_q_heads, int num_kv_heads);
 // Largest partition (tokens) a launch supports: a wave keeps its block ids in one register.
 int max_partition_tokens(DecodePath path, int block_size);
 
+// Arguments of the multi-query (prefill / chunked-prefill) kernel.
+struct PrefillArgs {
+  void* out;                   // [num_q_tokens][Hq][D]
+  const void* q;               // [num_q_tokens][Hq][D]
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start;  // [num_seqs + 1]
+  float scale_log2;
+  int num_seqs;
+  int num_q_tokens;
+  int num_q_heads;
+  int num_kv_heads;
+  int max_blocks_per_seq;
+  int64_t num_blocks;
+  int max_query_len;
+  int max_context_len;
+  int row_tiles;               // workgroup row tiles per (sequence, KV head)
+};
+
+bool prefill_supported(int dt, int head_dim, int block_size);
+// Query rows (query token x grouped head) one workgroup covers.
+int prefill_rows_per_workgroup();
+hipError_t launch_prefill(int dt, int head_dim, int block_size, const PrefillArgs& a,
+                          hipStream_t stream);
+
 hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                            const int32_t* slot_mapping, int n_tokens, int num_kv_heads,
                            int row_bytes, int block_size, int64_t num_blocks,

@@ -78,3 +78,54 @@ def assert_attention_close(gpu: np.ndarray, ref64: np.ndarray, dtype: str, what:
         raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; "
                              f"max abs err {err.max():.3g}; first bad {idx.tolist()}")
     return float(err.max())
+
+
+class DevPrefill:
+    """A PrefillStep's arrays on the GPU plus an output; run() writes the chunk's keys/values
+    (pa_write_kv) and runs pa_prefill."""
+
+    def __init__(self, step, device="cuda"):
+        self.step = step
+        dt = step.dtype
+        self.k_cache = to_dev(step.k_cache, dt, device)
+        self.v_cache = to_dev(step.v_cache, dt, device)
+        self.q = to_dev(step.q, dt, device)
+        self.block_tables = to_dev(step.block_tables, None, device)
+        self.context_lens = to_dev(step.context_lens, None, device)
+        self.query_start = to_dev(step.query_start, None, device)
+        self.writes = [(to_dev(w.k_new, dt, device), to_dev(w.v_new, dt, device),
+                        to_dev(w.slot_mapping, None, device)) for w in step.writes]
+        self.out = torch.zeros_like(self.q)
+
+    def apply_updates(self):
+        for kn, vn, sm in self.writes:
+            pa.pa_write_kv(self.k_cache, self.v_cache, kn, vn, sm)
+
+    def attend(self):
+        st = self.step
+        pa.pa_prefill(self.out, self.q, self.k_cache, self.v_cache, self.block_tables,
+                      self.context_lens, self.query_start, float(st.scale), st.max_query_len,
+                      st.max_context_len)
+        return self.out
+
+    def run(self):
+        self.apply_updates()
+        self.attend()
+        torch.cuda.synchronize()
+        return to_host(self.out, self.step.dtype)
+
+
+def prefill_rows_reference(step, kc, vc, rows):
+    """Oracle outputs (float64 [len(rows), Hq, d]) of the listed query rows, each evaluated as a
+    single query over its visible prefix (positions 0 .. T-n+i) with the decode oracle on the
+    pools after the chunk's write. Test infrastructure: lets full-size checks sample rows."""
+    import oracle
+
+    qs = step.query_start
+    seq = np.searchsorted(qs, rows, side="right") - 1
+    T = step.context_lens[seq]
+    n = qs[seq + 1] - qs[seq]
+    visible = (T - n + (rows - qs[seq]) + 1).astype(np.int32)
+    q_rows = np.ascontiguousarray(step.q[rows])
+    tables = np.ascontiguousarray(step.block_tables[seq])
+    return oracle.decode(q_rows, kc, vc, tables, visible, step.scale, step.dtype)

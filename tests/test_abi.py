@@ -40,7 +40,8 @@ def declared_functions():
 
 def test_header_declares_the_calls():
     assert declared_functions() == ["pa_copy_blocks", "pa_decode", "pa_decode_workspace_size",
-                                    "pa_status_string", "pa_swap_blocks", "pa_write_kv"]
+                                    "pa_prefill", "pa_status_string", "pa_swap_blocks",
+                                    "pa_write_kv"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -112,6 +113,32 @@ def test_decode_argument_checks(lib, monkeypatch):
     # the MFMA path does not take fp32
     monkeypatch.setenv("PA_DECODE_PATH", "mfma")
     assert call(dt=F32) == PA_ERR_UNSUPPORTED
+
+
+def test_prefill_argument_checks(lib):
+    f = lib.pa_prefill
+    args = [BAD, BAD, BAD, BAD, BAD, BAD, BAD, 0.125, 4, 64, 8, 2, 128, 16, 8, 64, 32, 100, F16,
+            None]
+    names = ["out", "q", "k", "v", "bt", "cl", "qs", "scale", "S", "Nq", "Hq", "Hkv", "d", "B",
+             "M", "N", "maxn", "maxT", "dt", "stream"]
+
+    def call(**kw):
+        a = list(args)
+        for k, val in kw.items():
+            a[names.index(k)] = val
+        return f(*a)
+
+    assert call(S=0) == PA_OK and call(Nq=0) == PA_OK and call(maxn=0) == PA_OK
+    assert call(qs=None) == PA_ERR_INVALID_ARG
+    assert call(out=V(0x1008)) == PA_ERR_INVALID_ARG  # q/out rows need 16-byte alignment
+    assert call(Hq=8, Hkv=3) == PA_ERR_INVALID_ARG
+    assert call(dt=F32) == PA_ERR_UNSUPPORTED  # MFMA path: 16-bit inputs only
+    assert call(d=96) == PA_ERR_UNSUPPORTED
+    assert call(B=64) == PA_ERR_UNSUPPORTED
+    assert call(M=0) == PA_ERR_INVALID_ARG
+    assert call(maxn=-1) == PA_ERR_INVALID_ARG
+    assert call(N=1 << 62) == PA_ERR_INVALID_ARG
+    assert call(maxn=1 << 30, Hq=64, Hkv=8) == PA_ERR_INVALID_ARG  # grid too large
 
 
 def test_workspace_size(lib):

@@ -1,0 +1,147 @@
+"""GPU parity of pa_prefill (causal multi-query attention over the paged pool) against the CPU
+oracle, through the C ABI: |gpu - ref| <= 2e-2 + 1e-2 |ref| elementwise (16-bit inputs, fp32
+accumulation), the chunk's KV write bit-exact. Shapes span several row tiles with ragged
+tails, contexts that need more than one register of block ids, every supported head size,
+block size and group size, empty chunks, whole prompts and single-token chunks."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+from gpu_harness import (DevPrefill, DevStep, assert_attention_close, prefill_rows_reference,
+                         to_host)
+from workloads import make_prefill_step, make_step, to_float64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu-test] {request.node.name}", flush=True)
+    yield
+
+
+def _bits(a):
+    return a.view(np.uint8)
+
+
+def _check(step, what=""):
+    ref, kc, vc = oracle.run_prefill_step(step)
+    dev = DevPrefill(step)
+    got = dev.run()
+    assert np.array_equal(_bits(to_host(dev.k_cache, step.dtype)), _bits(kc)), what
+    assert np.array_equal(_bits(to_host(dev.v_cache, step.dtype)), _bits(vc)), what
+    owned = np.zeros(step.num_q_tokens, bool)
+    owned[step.query_start[0]:step.query_start[-1]] = True
+    assert_attention_close(got[owned], ref[owned], step.dtype, what)
+    return got, ref
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B", [8, 16, 32])
+def test_prefill_shapes_mha(dt, d, B):
+    # whole prompts, chunks after a cached prefix, a single-token chunk, an empty chunk; 300
+    # query rows span three row tiles of 128 with a ragged tail
+    T = [40, 300, 77, 1, 65, 9]
+    n = [40, 300, 20, 1, 1, 0]
+    step = make_prefill_step("pmha", 400 + B + d, T, n, 4, 4, d, B, dt)
+    _check(step, f"mha {dt} d{d} B{B}")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("g", [2, 4, 8, 16])
+@pytest.mark.parametrize("d,B", [(128, 16), (64, 8), (128, 32)])
+def test_prefill_shapes_gqa(dt, g, d, B):
+    T = [33, 130, 257, 5]
+    n = [33, 50, 17, 5]
+    step = make_prefill_step("pgqa", 420 + g, T, n, 2 * g, 2, d, B, dt)
+    _check(step, f"gqa {dt} g{g} d{d} B{B}")
+
+
+def test_prefill_long_context_rotates_block_ids():
+    # positions past 64 and 128 steps of 32 tokens: the kernel loads block ids 64 steps at a
+    # time; rows of one wave straddle a 32-token step boundary
+    T = [4500, 2100, 70]
+    n = [100, 37, 70]
+    step = make_prefill_step("plong", 430, T, n, 8, 2, 128, 16, "bf16")
+    _check(step, "long")
+
+
+def test_prefill_single_token_matches_decode():
+    # n = 1 for every sequence is a decode step: both kernels against the oracle, and each other
+    lengths = [1, 7, 100, 513, 1500]
+    pstep = make_prefill_step("p1", 440, lengths, [1] * len(lengths), 16, 2, 128, 16, "f16")
+    got_p, _ = _check(pstep, "prefill n=1")
+    dstep = make_step("d1", 440, lengths, 16, 2, 128, 16, "f16")
+    dstep.q[...] = pstep.q  # same query vectors
+    dref, _, _ = oracle.run_step(dstep)
+    got_d = DevStep(dstep).run()
+    assert_attention_close(got_d, dref, "f16", "decode")
+    assert_attention_close(got_p, to_float64(got_d, "f16"), "f16", "prefill vs decode")
+
+
+def test_prefill_placement_invariance_bit_exact():
+    outs = []
+    for r in range(3):
+        step = make_prefill_step("ppl", 450, [300, 41, 129], [200, 41, 3], 16, 2, 128, 16,
+                                 "bf16", alloc_rng=np.random.default_rng(700 + r),
+                                 pool_factor=2.0)
+        outs.append(DevPrefill(step).run())
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_prefill_large_scores_stay_finite():
+    step = make_prefill_step("pbig", 460, [90, 300], [90, 64], 8, 2, 128, 16, "bf16")
+    from workloads import to_storage
+
+    step.q[...] = to_storage(to_float64(step.q, "bf16") * 30.0, "bf16")
+    _check(step, "large scores")
+
+
+def test_prefill_rows_outside_sequences_untouched():
+    # query_start need not start at 0 nor end at num_q_tokens: rows no sequence owns keep
+    # their contents
+    step = make_prefill_step("pown", 470, [20, 30], [8, 12], 4, 4, 64, 16, "f16")
+    pad = 3
+    Nq = step.num_q_tokens
+    q = np.zeros((Nq + 2 * pad,) + step.q.shape[1:], step.q.dtype)
+    q[pad:pad + Nq] = step.q
+    step.q = q
+    step.query_start = step.query_start + pad
+    dev = DevPrefill(step)
+    dev.out.fill_(7.0)
+    got = dev.run()
+    assert (got[:pad] == 7.0).all() and (got[pad + Nq:] == 7.0).all()
+    ref, _, _ = oracle.run_prefill_step(step)
+    assert_attention_close(got[pad:pad + Nq], ref[pad:pad + Nq], "f16", "offset rows")
+
+
+@pytest.mark.parametrize("name", ["prefill_mha13b", "prefill_gqa"])
+def test_prefill_full_size_sampled_rows(name):
+    # the benchmark's workloads at full size, in the benchmark's launch configuration; the
+    # oracle checks 96 sampled rows (first, last and random rows of every sequence)
+    import workloads.configs as cfg
+
+    step = getattr(cfg, name)()
+    dev = DevPrefill(step)
+    got = dev.run()
+    kc = to_host(dev.k_cache, step.dtype)
+    vc = to_host(dev.v_cache, step.dtype)
+    ref_pool = step.k_cache.copy(), step.v_cache.copy()
+    for w in step.writes:
+        oracle.write_kv(ref_pool[0], ref_pool[1], w.k_new, w.v_new, w.slot_mapping, step.dtype)
+    assert np.array_equal(_bits(kc), _bits(ref_pool[0])) and np.array_equal(_bits(vc), _bits(ref_pool[1]))
+    rng = np.random.default_rng(480)
+    qs = step.query_start
+    rows = set()
+    for s in range(step.num_seqs):
+        if qs[s + 1] > qs[s]:
+            rows.update({int(qs[s]), int(qs[s + 1] - 1)})
+    rows.update(rng.integers(0, step.num_q_tokens, size=96 - len(rows)).tolist())
+    rows = np.array(sorted(rows))
+    ref = prefill_rows_reference(step, kc, vc, rows)
+    assert_attention_close(got[rows], ref, step.dtype, name)
+    assert np.isfinite(to_float64(got, step.dtype)).all()
