@@ -47,6 +47,8 @@ WORKLOADS = {
     "prefill-gqa": ("prefill_gqa", "chunked prefill, GQA bf16: 16 seqs, 64 query / 8 KV heads, "
                     "d=128, B=16, 1024-token chunks after prefixes uniform in [0,3072]"),
     "copy": (None, "plain copy calibration: pa_copy_blocks of 4096 blocks of 256 KiB"),
+    "sharing": (None, "KV memory accounting on the host block manager (no GPU): prompt sharing "
+                "in parallel sampling and beam search, paged vs contiguous waste"),
     "swap": (None, "preemption swap: pa_swap_blocks of 2048 blocks of 160 KiB (40 heads, B=16, "
              "d=128, fp16) device -> pinned host and back"),
 }
@@ -347,6 +349,24 @@ def run_swap(args):
                       **res}))
 
 
+def run_sharing(args):
+    """Block-manager accounting only (host code, no GPU): synthetic lognormal lengths."""
+    from paged_kv_cache_82_amd import sharing
+
+    t0 = time.perf_counter()
+    res = {
+        "metric": "KV memory saved by block sharing / wasted by allocation (host block manager)",
+        "block_size": 16,
+        "parallel_sampling": [sharing.parallel_sampling(n) for n in (2, 4, 6)],
+        "beam_search": [sharing.beam_search(k) for k in (2, 4, 6)],
+        "waste": sharing.waste(),
+        "data": "synthetic lognormal lengths (prompt median 160, output median 300 / 200 for "
+                "beams, sigma 0.8; waste: median 400, sigma 0.9, max 2048); random beam parents",
+    }
+    res["seconds"] = round(time.perf_counter() - t0, 2)
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -362,6 +382,8 @@ def main():
                     help="block placement; 'contiguous' is a diagnostic of what scattering costs")
     args = ap.parse_args()
 
+    if args.workload == "sharing":
+        return run_sharing(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(sequences and KV heads would shard with no exchange; see the design notes).",

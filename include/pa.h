@@ -65,7 +65,8 @@ typedef enum {
   PA_ERR_INVALID_ARG = 1,
   PA_ERR_UNSUPPORTED = 2,
   PA_ERR_WORKSPACE = 3,
-  PA_ERR_HIP = 4
+  PA_ERR_HIP = 4,
+  PA_ERR_NO_BLOCKS = 5 /* host block manager: the free list cannot cover the request */
 } pa_status;
 
 /*

@@ -80,6 +80,7 @@ const char* pa_status_string(pa_status s) {
     case PA_ERR_UNSUPPORTED: return "unsupported dtype/head_dim/block_size combination";
     case PA_ERR_WORKSPACE: return "workspace too small";
     case PA_ERR_HIP: return "HIP runtime error at launch";
+    case PA_ERR_NO_BLOCKS: return "not enough free blocks";
   }
   return "unknown status";
 }
