@@ -14,13 +14,20 @@
 // (pa_mfma.h): S^T = K Q^T with tokens on rows and query rows on columns, then
 // O^T += V^T P^T. Work decomposition (chosen for MI355X, not on the pages):
 //   - query rows are (query token, grouped head) pairs, head fastest, so one KV tile feeds all
-//     query heads of its group; a wave owns NCT tiles of 16 rows and reuses every K/V step it
-//     loads for all of them; a workgroup of NW waves covers NW * NCT * 16 consecutive rows;
-//   - a wave walks the 32-token steps of positions 0 .. (its last row's position), keeping a
-//     ring of NBUF steps of K/V in registers (the loads of the next step are in flight while
-//     one is consumed); only steps that reach past the wave's first position apply the mask;
-//   - physical block ids come 64 steps at a time into one register (lane k = step k) and are
-//     broadcast with readlane; the next 64 are loaded while the current ones are used;
+//     query heads of its group; a workgroup of NW waves covers NW * NCT * 16 consecutive rows
+//     as 16-row column tiles dealt round-robin to the waves (so every wave reaches about the
+//     same causal depth);
+//   - the workgroup walks its context in stages of KT = 32 * NSUB tokens: every thread loads
+//     a few 16-byte chunks of the stage's K and V rows (through the block table) and writes
+//     them to an LDS tile, double-buffered, with the loads of the stage after next in flight
+//     while a stage is consumed; one barrier per stage;
+//   - LDS rows are XOR-swizzled in 16-byte chunks so that the MFMA operand reads (16 rows at
+//     one column for K, one row for V) and the stage writes hit distinct banks;
+//   - each wave reads a 32-token substep's K and V fragments once from LDS and uses them for
+//     all its column tiles; a tile is skipped for substeps past its last position and masked
+//     only where the substep reaches past its first;
+//   - physical block ids come 64 at a time into one register per wave (lane k = block k) and
+//     are broadcast with readlane;
 //   - workgroups are ordered so that the row tiles of one (sequence, KV head) run on one XCD
 //     (workgroups are dealt round-robin over the 8 XCDs) and share that XCD's L2, heaviest
 //     (latest) tiles first.
@@ -35,8 +42,11 @@ namespace {
 
 constexpr int kPrefillWaves = 4;     // waves per workgroup
 constexpr int kPrefillColTiles = 2;  // 16-row column tiles per wave
-constexpr int kPrefillBuffers = 2;   // 32-token K/V steps held in registers
+constexpr int kPrefillSubsteps = 1;  // 32-token substeps per LDS stage
 constexpr int kXcds = 8;             // MI355X: workgroups are dealt round-robin over 8 XCDs
+// A score may exceed the reference maximum by this much (base 2) before the running state is
+// rescaled: weights stay below 2^8 = 256, well inside fp16/bf16 and fp32 sums.
+constexpr float kSlack = 8.0f;
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) {
   return x < lo ? lo : (x > hi ? hi : x);
@@ -44,19 +54,28 @@ __device__ __forceinline__ int clampi(int x, int lo, int hi) {
 
 }  // namespace
 
-template <DT dt, int D, int BS, int NW, int NCT, int NBUF>
-__global__ __launch_bounds__(NW * 64, 1) void prefill_mfma_kernel(const PrefillArgs a) {
+template <DT dt, int D, int BS, int NW, int NCT, int NSUB>
+__global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillArgs a) {
   static_assert(dt != DT::F32, "MFMA path takes 16-bit inputs");
-  static_assert(BS <= 32 && 32 % BS == 0, "a 32-token step spans whole blocks");
   using M = MfmaT<dt>;
   using vec8 = typename M::vec8;
   using VF = VFrag<D>;
   constexpr int E = 2;
-  constexpr int KC = D / 32;  // q.K MFMAs per 16-token tile
-  constexpr int MT = D / 16;  // p.V M-tiles; row r of tile mt is head dimension MT*r + mt
-  constexpr int NBS = 32 / BS;
+  constexpr int KC = D / 32;        // q.K MFMAs per 16-token tile
+  constexpr int MT = D / 16;        // p.V M-tiles; row r of tile mt is head dimension MT*r + mt
+  constexpr int RB = D * E;         // bytes per token row
+  constexpr int CPR = RB / 16;      // 16-byte chunks per row
+  constexpr int KT = 32 * NSUB;     // tokens per stage
+  constexpr int BPS = KT / BS;      // blocks per stage
+  constexpr int NT = NW * 64;
+  constexpr int CPT = KT * CPR / NT;  // chunks per thread per tensor per stage
+  constexpr int RPW = 64 / CPR;     // rows one wave-wide chunk load covers
   constexpr int ROWS_W = 16 * NCT;
   constexpr int ROWS = NW * ROWS_W;
+  constexpr int TILE = KT * RB;     // LDS bytes per tensor per stage
+  static_assert(KT * CPR % NT == 0, "a stage splits evenly over the threads");
+  static_assert(BS % RPW == 0 && 64 % BPS == 0, "a wave-wide load stays in one block");
+  __shared__ __attribute__((aligned(16))) char lds[2][2][TILE];  // [buffer][K, V]
 
   // Workgroup -> (row tile, KV head, sequence). Linear id L runs on XCD L % 8; renumber so
   // that each XCD takes a contiguous range of tiles (whole (sequence, KV head) groups).
@@ -83,43 +102,31 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_mfma_kernel(const PrefillA
   const int Hq = a.num_q_heads;
   const int g = Hq / Hkv;
   const int nrows = n * g;
+  const int W0 = tile * ROWS;  // first row of the workgroup
+  if (W0 >= nrows) return;     // uniform over the workgroup: no barrier is skipped
+  const int base_pos = T - n;  // position of the chunk's first query token
+  const int p_hi_wg = base_pos + ((W0 + ROWS < nrows ? W0 + ROWS : nrows) - 1) / g;
+  const int nstages = (p_hi_wg + KT) / KT;  // stages covering positions 0 .. p_hi_wg
+  const int jlast = p_hi_wg / BS;           // last block the workgroup reads
 
   const int lane = threadIdx.x & 63;
   const int w = wave_id();
   const int hh = lane & 15, gq = lane >> 4;
-  const int R0 = tile * ROWS + w * ROWS_W;  // first row of this wave
-  if (R0 >= nrows) return;                  // no barrier below: idle waves leave at once
-  const int base_pos = T - n;               // position of the chunk's first query token
-  const int R_last = (R0 + ROWS_W < nrows ? R0 + ROWS_W : nrows) - 1;
-  const int p_lo = base_pos + R0 / g;       // smallest position among this wave's rows
-  const int p_hi = base_pos + R_last / g;   // largest
-  const int ns = (p_hi + 32) / 32;          // 32-token steps covering positions 0 .. p_hi
-  const int jlast = p_hi / BS;              // last block any row of this wave reads
 
-  // Block ids: lane k of ids_cur holds the NBS ids of step 64*chunk + k.
-  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  auto load_ids = [&](int chunk, int (&ids)[NBS]) {
-#pragma unroll
-    for (int b = 0; b < NBS; ++b) {
-      const int j = (chunk * 64 + lane) * NBS + b;
-      ids[b] = (j <= jlast) ? bt[j] : 0;  // jlast < max_blocks_per_seq since T <= cap
-    }
-  };
-  int ids_cur[NBS], ids_nxt[NBS];
-  int cur_chunk = 0;
-  load_ids(0, ids_cur);
-  load_ids(1, ids_nxt);
-
-  // Query columns: column hh of tile c is row R = R0 + 16c + hh = (token R / g, head R % g).
-  int pos[NCT];  // position of the column's query token; -1 for rows past the chunk
+  // Column tiles of this wave: tile c is workgroup column tile w + NW*c.
+  int pos[NCT];                // position of this lane's query row; -1 past the chunk
+  int t_lo[NCT], t_hi[NCT];    // first / last position of the tile's rows (uniform); -1 if empty
   vec8 qop[NCT][KC];
 #pragma unroll
   for (int c = 0; c < NCT; ++c) {
-    const int R = R0 + 16 * c + hh;
+    const int Rt = W0 + 16 * (w + NW * c);  // first row of the tile
+    const int R = Rt + hh;
     const bool valid = R < nrows;
     const int i = valid ? R / g : 0;
     const int head = kvh * g + (valid ? R % g : 0);
     pos[c] = valid ? base_pos + i : -1;
+    t_lo[c] = Rt < nrows ? base_pos + Rt / g : -1;
+    t_hi[c] = Rt < nrows ? base_pos + ((Rt + 16 < nrows ? Rt + 16 : nrows) - 1) / g : -1;
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) {
       u32x4 raw = {0u, 0u, 0u, 0u};
@@ -129,6 +136,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_mfma_kernel(const PrefillA
       qop[c][kk] = __builtin_bit_cast(vec8, raw);
     }
   }
+  int p_hi_w = -1;  // last position any tile of this wave needs
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) p_hi_w = t_hi[c] > p_hi_w ? t_hi[c] : p_hi_w;
 
   f32x4 oacc[NCT][MT];
   float m[NCT], lsum[NCT];
@@ -140,144 +150,162 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_mfma_kernel(const PrefillA
     for (int mt = 0; mt < MT; ++mt) oacc[c][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // Block ids: lane k of ids_cur holds block 64*id_chunk + k of the sequence.
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  auto load_ids = [&](int chunk) {
+    const int j = chunk * 64 + lane;
+    return (j <= jlast) ? bt[j] : 0;  // jlast < max_blocks_per_seq since T <= cap
+  };
+  int id_chunk = 0;
+  int ids_cur = load_ids(0);
+  int ids_nxt = load_ids(1);
+
+  // Stage loads: thread chunk k (k < CPT) of a tensor is flat chunk tid + NT*k of the stage,
+  // row r = flat / CPR, column chunk flat % CPR.
   const char* kbase = (const char*)a.k_cache;
   const char* vbase = (const char*)a.v_cache;
-  constexpr int RB = D * E;  // bytes per token row
-  const uint32_t koff = (uint32_t)((hh % BS) * RB + 8 * gq * E);
-  const uint32_t voff = (uint32_t)(((4 * gq) % BS) * RB + MT * hh * E);
   const int64_t tile_bytes = (int64_t)BS * RB;
-
-  auto fetch = [&](int k, StepRegs<D, KC>& Rg) {
-    const bool cur = (k >> 6) == cur_chunk;  // wave-uniform
-    const int kl = k & 63;
-    const int id0 = cur ? __builtin_amdgcn_readlane(ids_cur[0], kl)
-                        : __builtin_amdgcn_readlane(ids_nxt[0], kl);
-    const char* kt[NBS];
-    const char* vt[NBS];
+  u32x4 gk[CPT], gv[CPT];
+  auto issue_loads = [&](int st) {
+    const int jfirst = st * BPS;  // a stage never straddles two id chunks (64 % BPS == 0)
+    if ((jfirst >> 6) != id_chunk) {
+      ids_cur = ids_nxt;
+      id_chunk = jfirst >> 6;
+      ids_nxt = load_ids(id_chunk + 1);
+    }
 #pragma unroll
-    for (int b = 0; b < NBS; ++b) {
-      const int idb = cur ? __builtin_amdgcn_readlane(ids_cur[b], kl)
-                          : __builtin_amdgcn_readlane(ids_nxt[b], kl);
-      // a block past the last one this wave needs holds only positions no row sees: read the
-      // step's first block instead (its V is zeroed and its scores masked in consume)
-      const int32_t id = (k * NBS + b <= jlast) ? idb : id0;
+    for (int k = 0; k < CPT; ++k) {
+      const int flat = threadIdx.x + NT * k;
+      const int r = flat / CPR, cc = flat % CPR;
+      const int jb = ((64 * w + NT * k) / CPR) / BS;  // block of this wave's rows (uniform)
+      int j = jfirst + jb;
+      j = j < jlast ? j : jlast;  // past the last needed block: stand-in rows, masked later
+      const int32_t id = __builtin_amdgcn_readlane(ids_cur, j & 63);
       const int64_t t = (clamp_block(id, a.num_blocks) * Hkv + kvh) * tile_bytes;
-      kt[b] = kbase + t;
-      vt[b] = vbase + t;
+      const uint32_t off = (uint32_t)((r % BS) * RB + cc * 16);
+      gk[k] = load16(kbase + t + off);
+      gv[k] = load16(vbase + t + off);
     }
+  };
+  // Swizzled LDS byte offset of chunk cc of row r.
+  auto lds_off = [](int r, int cc) {
+    constexpr int RPL = 16 / CPR;  // rows per 256-byte line of banks
+    return r * RB + ((cc ^ ((r / RPL) % CPR)) * 16);
+  };
+  auto store_stage = [&](int st, int buf) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const char* rp;
-      if constexpr (BS >= 16) {
-        rp = kt[(16 * u) / BS] + koff + ((16 * u) % BS) * RB;
-      } else {  // BS == 8: lanes hh < 8 and hh >= 8 read different blocks
-        rp = kt[2 * u + (hh >> 3)] + koff;
-      }
-#pragma unroll
-      for (int kk = 0; kk < KC; ++kk) Rg.k[u][kk] = load16(rp + 32 * kk * E);
+    for (int k = 0; k < CPT; ++k) {
+      const int flat = threadIdx.x + NT * k;
+      const int r = flat / CPR, cc = flat % CPR;
+      u32x4 vv = gv[k];
+      if (st * KT + r > p_hi_wg) vv = u32x4{0u, 0u, 0u, 0u};  // stand-in / tail rows: V = 0
+      *reinterpret_cast<u32x4*>(&lds[buf][0][lds_off(r, cc)]) = gk[k];
+      *reinterpret_cast<u32x4*>(&lds[buf][1][lds_off(r, cc)]) = vv;
     }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const char* rp;
-        if constexpr (BS >= 16) {
-          rp = vt[(16 * u) / BS] + voff + ((16 * u) % BS + i) * RB;
-        } else {  // token 16u + 4gq + i sits in block 2u + gq/2 at row 4*(gq&1) + i
-          rp = vt[2 * u + (gq >> 1)] + voff + i * RB;
-        }
-        Rg.v[u][i] = VF::load(rp);
-      }
-    __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the consume that follows
   };
 
-  auto consume = [&](int k, StepRegs<D, KC>& Rg) {
-    const int tau0 = k * 32;
-    if (tau0 + 31 > p_hi) {  // tokens after the wave's last position: zero V (select)
+  issue_loads(0);
+  store_stage(0, 0);
+  if (nstages > 1) issue_loads(1);
+  __syncthreads();
+
+  for (int st = 0; st < nstages; ++st) {
+    const int buf = st & 1;
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (tau0 + 16 * u + 4 * gq + i > p_hi) Rg.v[u][i] = typename VF::T{};
-    }
-    const bool masked = tau0 + 31 > p_lo;
-    // V^T operand of M-tile mt, k element e <-> token 16*(e/4) + 4*gq + (e%4); shared by
-    // every column tile
-    u32x4 vw[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) {
-        const int e0 = 2 * q2, e1 = 2 * q2 + 1;
-        const uint32_t lo = vfrag_elem<D>(Rg.v[e0 / 4][e0 % 4], mt);
-        const uint32_t hi = vfrag_elem<D>(Rg.v[e1 / 4][e1 % 4], mt);
-        vw[mt][q2] = lo | (hi << 16);
-      }
-#pragma unroll
-    for (int c = 0; c < NCT; ++c) {
-      f32x4 sacc[2];
+    for (int u2 = 0; u2 < NSUB; ++u2) {
+      const int tau0 = st * KT + 32 * u2;
+      if (tau0 > p_hi_w) break;  // uniform: every tile of this wave is done
+      const int rbase = 32 * u2;
+      u32x4 kf[2][KC];
+      typename VF::T vf[2][4];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        sacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int r = rbase + 16 * u + hh;
 #pragma unroll
         for (int kk = 0; kk < KC; ++kk)
-          sacc[u] = M::mma(__builtin_bit_cast(vec8, Rg.k[u][kk]), qop[c][kk], sacc[u]);
-      }
-      float sc[8];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
+          kf[u][kk] = *reinterpret_cast<const u32x4*>(&lds[buf][0][lds_off(r, 4 * kk + gq)]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float x = sacc[u][i] * a.scale_log2;
-          if (masked && tau0 + 16 * u + 4 * gq + i > pos[c]) x = kNegInf;  // select
-          sc[4 * u + i] = x;
+          const int rv = rbase + 16 * u + 4 * gq + i;
+          if constexpr (D == 128) {
+            vf[u][i] = *reinterpret_cast<const u32x4*>(&lds[buf][1][lds_off(rv, hh)]);
+          } else {
+            vf[u][i] = *reinterpret_cast<const u32x2*>(
+                &lds[buf][1][lds_off(rv, hh >> 1) + 8 * (hh & 1)]);
+          }
         }
-      float bm = sc[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sc[e]);
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      const float mn = fmaxf(m[c], bm);
-      const bool empty = (mn == kNegInf);  // no visible token yet for this column
-      const float corr = empty ? 1.0f : fast_exp2(m[c] - mn);
-      vec8 pop;
-      float ps = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pe = empty ? 0.0f : fast_exp2(sc[e] - mn);
-        ps += pe;
-        pop[e] = (typename M::scalar)pe;
       }
-      lsum[c] = fmaf(lsum[c], corr, ps);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) oacc[c][mt] *= corr;
+      // V^T operand of M-tile mt, k element e <-> token 16*(e/4) + 4*gq + (e%4)
+      u32x4 vw[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        oacc[c][mt] = M::mma(__builtin_bit_cast(vec8, vw[mt]), pop, oacc[c][mt]);
-      m[c] = mn;
-    }
-  };
-
-  {  // ring of NBUF register buffers, unconditional prefetch (past the end: the last step)
-    StepRegs<D, KC> rb[NBUF];
 #pragma unroll
-    for (int u = 0; u + 1 < NBUF; ++u) fetch(u < ns ? u : ns - 1, rb[u]);
-    for (int k = 0; k < ns; k += NBUF) {
-#pragma unroll
-      for (int u = 0; u < NBUF; ++u) {
-        const int kk = k + u;
-        if (kk >= ns) break;
-        if ((kk & 63) == 0 && kk > 0) {  // next 64 steps: rotate the id registers
-#pragma unroll
-          for (int b = 0; b < NBS; ++b) ids_cur[b] = ids_nxt[b];
-          cur_chunk = kk >> 6;
-          load_ids(cur_chunk + 1, ids_nxt);
+        for (int q2 = 0; q2 < 4; ++q2) {
+          const int e0 = 2 * q2, e1 = 2 * q2 + 1;
+          const uint32_t lo = vfrag_elem<D>(vf[e0 / 4][e0 % 4], mt);
+          const uint32_t hi = vfrag_elem<D>(vf[e1 / 4][e1 % 4], mt);
+          vw[mt][q2] = lo | (hi << 16);
         }
-        const int ahead = kk + NBUF - 1;
-        fetch(ahead < ns ? ahead : ns - 1, rb[(u + NBUF - 1) % NBUF]);
-        consume(kk, rb[u]);
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) {
+        if (tau0 > t_hi[c]) continue;  // uniform: no row of this tile sees the substep
+        const bool masked = tau0 + 31 > t_lo[c];
+        f32x4 sacc[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          sacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < KC; ++kk)
+            sacc[u] = M::mma(__builtin_bit_cast(vec8, kf[u][kk]), qop[c][kk], sacc[u]);
+        }
+        // Scaled scores (base 2), masked by select. The weights are taken against a reference
+        // maximum m[c] that is raised only when some score exceeds it by more than kSlack:
+        // weights stay below 2^kSlack, and the running sum and output use the same reference,
+        // so the normalised result is the same as with the exact running maximum.
+        float sc[8];
+        float lm = kNegInf;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float x = sacc[u][i] * a.scale_log2;
+            if (masked && tau0 + 16 * u + 4 * gq + i > pos[c]) x = kNegInf;  // select
+            sc[4 * u + i] = x;
+            lm = fmaxf(lm, x);
+          }
+        if (__builtin_amdgcn_ballot_w64(lm > m[c] + kSlack)) {  // uniform, rare after warm-up
+          float bm = fmaxf(lm, __shfl_xor(lm, 16));
+          bm = fmaxf(bm, __shfl_xor(bm, 32));
+          const float mn = fmaxf(m[c], bm);
+          const float corr = (m[c] == kNegInf) ? (mn == kNegInf ? 1.0f : 0.0f)
+                                               : fast_exp2(m[c] - mn);
+          lsum[c] *= corr;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) oacc[c][mt] *= corr;
+          m[c] = mn;
+        }
+        // m[c] is -inf only while no row of the column has a visible token (then every x is
+        // -inf too): use 0 as the reference so that the weights are exp2(-inf) = 0
+        const float mref = (m[c] == kNegInf) ? 0.0f : m[c];
+        vec8 pop;
+        float ps = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pe = fast_exp2(sc[e] - mref);
+          ps += pe;
+          pop[e] = (typename M::scalar)pe;
+        }
+        lsum[c] += ps;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          oacc[c][mt] = M::mma(__builtin_bit_cast(vec8, vw[mt]), pop, oacc[c][mt]);
       }
     }
+    if (st + 1 < nstages) {
+      store_stage(st + 1, buf ^ 1);  // that buffer was last read before the previous barrier
+      if (st + 2 < nstages) issue_loads(st + 2);
+    }
+    __syncthreads();
   }
 
   // Normalise and store. oacc[c][mt][i] is O[column hh][dim MT*(4*gq + i) + mt]: for fixed i
@@ -288,7 +316,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_mfma_kernel(const PrefillA
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     if (pos[c] < 0) continue;
-    const int R = R0 + 16 * c + hh;
+    const int R = W0 + 16 * (w + NW * c) + hh;
     const int i = R / g;
     const int head = kvh * g + R % g;
     char* orow = (char*)a.out + ((int64_t)(q0 + i) * Hq + head) * D * E;
@@ -329,7 +357,7 @@ static hipError_t launch_pf(const PrefillArgs& a, hipStream_t stream) {
   void* args[] = {&args_copy};
   return hipLaunchKernel(
       (const void*)prefill_mfma_kernel<dt, D, BS, kPrefillWaves, kPrefillColTiles,
-                                       kPrefillBuffers>,
+                                       kPrefillSubsteps>,
       dim3((unsigned)total), dim3(kPrefillWaves * 64), args, 0, stream);
 }
 
