@@ -24,8 +24,8 @@
 //   - LDS rows are XOR-swizzled in 16-byte chunks so that the MFMA operand reads (16 rows at
 //     one column for K, one row for V) and the stage writes hit distinct banks;
 //   - each wave reads a 32-token substep's K and V fragments once from LDS and uses them for
-//     all its column tiles; a tile is skipped for substeps past its last position and masked
-//     only where the substep reaches past its first;
+//     all its column tiles (their MFMA chains interleave); a tile is masked only where the
+//     substep reaches past its first position;
 //   - physical block ids come 64 at a time into one register per wave (lane k = block k) and
 //     are broadcast with readlane;
 //   - workgroups are ordered so that the row tiles of one (sequence, KV head) run on one XCD
@@ -246,35 +246,47 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
           const uint32_t hi = vfrag_elem<D>(vf[e1 / 4][e1 % 4], mt);
           vw[mt][q2] = lo | (hi << 16);
         }
+      // S^T = K Q^T for every column tile: 2*NCT independent accumulation chains. A tile whose
+      // rows all precede the substep is computed too and masked out entirely (straight-line
+      // code; this happens only in the last substeps of the diagonal).
+      f32x4 sacc[NCT][2];
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) sacc[c][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk)
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            sacc[c][u] = M::mma(__builtin_bit_cast(vec8, kf[u][kk]), qop[c][kk], sacc[c][u]);
+      // Scaled scores (base 2), masked by select. The weights are taken against a reference
+      // maximum m[c] that is raised only when some score exceeds it by more than kSlack:
+      // weights stay below 2^kSlack, and the running sum and output use the same reference,
+      // so the normalised result is the same as with the exact running maximum.
+      float sc[NCT][8];
+      float lm[NCT];
+      bool raise = false;
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
-        if (tau0 > t_hi[c]) continue;  // uniform: no row of this tile sees the substep
-        const bool masked = tau0 + 31 > t_lo[c];
-        f32x4 sacc[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          sacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kk = 0; kk < KC; ++kk)
-            sacc[u] = M::mma(__builtin_bit_cast(vec8, kf[u][kk]), qop[c][kk], sacc[u]);
-        }
-        // Scaled scores (base 2), masked by select. The weights are taken against a reference
-        // maximum m[c] that is raised only when some score exceeds it by more than kSlack:
-        // weights stay below 2^kSlack, and the running sum and output use the same reference,
-        // so the normalised result is the same as with the exact running maximum.
-        float sc[8];
-        float lm = kNegInf;
+        const bool masked = tau0 + 31 > t_lo[c];  // uniform
+        lm[c] = kNegInf;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float x = sacc[u][i] * a.scale_log2;
+            float x = sacc[c][u][i] * a.scale_log2;
             if (masked && tau0 + 16 * u + 4 * gq + i > pos[c]) x = kNegInf;  // select
-            sc[4 * u + i] = x;
-            lm = fmaxf(lm, x);
+            sc[c][4 * u + i] = x;
+            lm[c] = fmaxf(lm[c], x);
           }
-        if (__builtin_amdgcn_ballot_w64(lm > m[c] + kSlack)) {  // uniform, rare after warm-up
-          float bm = fmaxf(lm, __shfl_xor(lm, 16));
+        raise = raise || (lm[c] > m[c] + kSlack);
+      }
+      if (__builtin_amdgcn_ballot_w64(raise)) {  // uniform; rare once the maxima settle
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) {
+          float bm = fmaxf(lm[c], __shfl_xor(lm[c], 16));
           bm = fmaxf(bm, __shfl_xor(bm, 32));
           const float mn = fmaxf(m[c], bm);
           const float corr = (m[c] == kNegInf) ? (mn == kNegInf ? 1.0f : 0.0f)
@@ -284,22 +296,28 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
           for (int mt = 0; mt < MT; ++mt) oacc[c][mt] *= corr;
           m[c] = mn;
         }
+      }
+      vec8 pop[NCT];
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) {
         // m[c] is -inf only while no row of the column has a visible token (then every x is
         // -inf too): use 0 as the reference so that the weights are exp2(-inf) = 0
         const float mref = (m[c] == kNegInf) ? 0.0f : m[c];
-        vec8 pop;
         float ps = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pe = fast_exp2(sc[e] - mref);
+          const float pe = fast_exp2(sc[c][e] - mref);
           ps += pe;
-          pop[e] = (typename M::scalar)pe;
+          pop[c][e] = (typename M::scalar)pe;
         }
         lsum[c] += ps;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          oacc[c][mt] = M::mma(__builtin_bit_cast(vec8, vw[mt]), pop, oacc[c][mt]);
       }
+      // O^T += V^T P^T: MT * NCT independent MFMAs
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+          oacc[c][mt] = M::mma(__builtin_bit_cast(vec8, vw[mt]), pop[c], oacc[c][mt]);
     }
     if (st + 1 < nstages) {
       store_stage(st + 1, buf ^ 1);  // that buffer was last read before the previous barrier
