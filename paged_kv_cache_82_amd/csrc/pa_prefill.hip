@@ -26,8 +26,8 @@
 //   - each wave reads a 32-token substep's K and V fragments once from LDS and uses them for
 //     all its column tiles (their MFMA chains interleave); a tile is masked only where the
 //     substep reaches past its first position;
-//   - physical block ids come 64 at a time into one register per wave (lane k = block k) and
-//     are broadcast with readlane;
+//   - each wave-wide load reads rows of one block, so its physical block id is wave-uniform
+//     and comes through the scalar cache;
 //   - workgroups are ordered so that the row tiles of one (sequence, KV head) run on one XCD
 //     (workgroups are dealt round-robin over the 8 XCDs) and share that XCD's L2, heaviest
 //     (latest) tiles first.
@@ -43,6 +43,7 @@ namespace {
 constexpr int kPrefillWaves = 4;     // waves per workgroup
 constexpr int kPrefillColTiles = 2;  // 16-row column tiles per wave
 constexpr int kPrefillSubsteps = 1;  // 32-token substeps per LDS stage
+constexpr int kPrefillStages = 3;    // LDS stage buffers (stages in flight + the one consumed)
 constexpr int kXcds = 8;             // MI355X: workgroups are dealt round-robin over 8 XCDs
 // A score may exceed the reference maximum by this much (base 2) before the running state is
 // rescaled: weights stay below 2^8 = 256, well inside fp16/bf16 and fp32 sums.
@@ -54,7 +55,7 @@ __device__ __forceinline__ int clampi(int x, int lo, int hi) {
 
 }  // namespace
 
-template <DT dt, int D, int BS, int NW, int NCT, int NSUB>
+template <DT dt, int D, int BS, int NW, int NCT, int NSUB, int NBUF>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillArgs a) {
   static_assert(dt != DT::F32, "MFMA path takes 16-bit inputs");
   using M = MfmaT<dt>;
@@ -67,15 +68,14 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
   constexpr int CPR = RB / 16;      // 16-byte chunks per row
   constexpr int KT = 32 * NSUB;     // tokens per stage
   constexpr int BPS = KT / BS;      // blocks per stage
-  constexpr int NT = NW * 64;
-  constexpr int CPT = KT * CPR / NT;  // chunks per thread per tensor per stage
-  constexpr int RPW = 64 / CPR;     // rows one wave-wide chunk load covers
+  constexpr int RPL = 1024 / RB;    // rows one wave-wide 16-byte-per-lane load covers
+  constexpr int WLW = KT * RB / 1024 / NW;  // wave-wide loads per wave per tensor per stage
   constexpr int ROWS_W = 16 * NCT;
   constexpr int ROWS = NW * ROWS_W;
   constexpr int TILE = KT * RB;     // LDS bytes per tensor per stage
-  static_assert(KT * CPR % NT == 0, "a stage splits evenly over the threads");
-  static_assert(BS % RPW == 0 && 64 % BPS == 0, "a wave-wide load stays in one block");
-  __shared__ __attribute__((aligned(16))) char lds[2][2][TILE];  // [buffer][K, V]
+  static_assert(KT * RB % (1024 * NW) == 0, "a stage splits evenly over the waves");
+  static_assert(BS % RPL == 0 && 64 % BPS == 0, "a wave-wide load stays in one block");
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF][2][TILE];  // [stage][K, V]
 
   // Workgroup -> (row tile, KV head, sequence). Linear id L runs on XCD L % 8; renumber so
   // that each XCD takes a contiguous range of tiles (whole (sequence, KV head) groups).
@@ -150,67 +150,78 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
     for (int mt = 0; mt < MT; ++mt) oacc[c][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Block ids: lane k of ids_cur holds block 64*id_chunk + k of the sequence.
-  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  auto load_ids = [&](int chunk) {
-    const int j = chunk * 64 + lane;
-    return (j <= jlast) ? bt[j] : 0;  // jlast < max_blocks_per_seq since T <= cap
-  };
-  int id_chunk = 0;
-  int ids_cur = load_ids(0);
-  int ids_nxt = load_ids(1);
+  // Block ids: every wave-wide load reads rows of one block, so its id is wave-uniform and is
+  // read with a scalar load (scalar cache; counted apart from the K/V loads in flight).
+  // (The table is read-only during the kernel, so it is read through the constant address
+  // space, which lets uniform reads become scalar loads.)
+  typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+  const const_i32_ptr bt =
+      (const_i32_ptr)(a.block_tables + (int64_t)s * a.max_blocks_per_seq);
 
-  // Stage loads: thread chunk k (k < CPT) of a tensor is flat chunk tid + NT*k of the stage,
-  // row r = flat / CPR, column chunk flat % CPR.
+  // LDS rows are swizzled in 16-byte chunks: chunk cc of row r sits at physical chunk
+  // cc ^ swz(r), with swz running over the rows that share one 256-byte line of banks.
+  auto swz = [](int r) { return (r / (16 / CPR)) % CPR; };
+  auto lds_off = [&](int r, int cc) { return r * RB + ((cc ^ swz(r)) * 16); };
+
+  // Stage loads go straight from global memory into LDS (global_load_lds_dwordx4): lane L
+  // of a wave-wide load writes LDS bytes [base + 16L, base + 16L + 16), so one load fills
+  // 1 KB = RPL whole rows. Lane L carries physical chunk L % CPR of row L / CPR and fetches
+  // the logical chunk the swizzle maps there. No registers hold data in flight, so NBUF
+  // stages can be in flight.
   const char* kbase = (const char*)a.k_cache;
   const char* vbase = (const char*)a.v_cache;
   const int64_t tile_bytes = (int64_t)BS * RB;
-  u32x4 gk[CPT], gv[CPT];
-  auto issue_loads = [&](int st) {
-    const int jfirst = st * BPS;  // a stage never straddles two id chunks (64 % BPS == 0)
-    if ((jfirst >> 6) != id_chunk) {
-      ids_cur = ids_nxt;
-      id_chunk = jfirst >> 6;
-      ids_nxt = load_ids(id_chunk + 1);
-    }
+  const int row_in_load = lane / CPR;
+  const int pchunk = lane % CPR;
+  auto issue_stage = [&](int st) {
+    const int buf = st % NBUF;
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      const int flat = threadIdx.x + NT * k;
-      const int r = flat / CPR, cc = flat % CPR;
-      const int jb = ((64 * w + NT * k) / CPR) / BS;  // block of this wave's rows (uniform)
-      int j = jfirst + jb;
+    for (int k = 0; k < WLW; ++k) {
+      const int mload = w * WLW + k;           // wave-wide load index within the tensor
+      const int r = mload * RPL + row_in_load;  // row within the stage
+      const int cc = pchunk ^ swz(r);           // logical chunk landing at physical pchunk
+      int j = st * BPS + (mload * RPL) / BS;    // the load's rows share one block (uniform)
       j = j < jlast ? j : jlast;  // past the last needed block: stand-in rows, masked later
-      const int32_t id = __builtin_amdgcn_readlane(ids_cur, j & 63);
+      const int32_t id = bt[j];   // jlast < max_blocks_per_seq since T <= cap
       const int64_t t = (clamp_block(id, a.num_blocks) * Hkv + kvh) * tile_bytes;
       const uint32_t off = (uint32_t)((r % BS) * RB + cc * 16);
-      gk[k] = load16(kbase + t + off);
-      gv[k] = load16(vbase + t + off);
+      // (explicit void pointers: with char pointers clang's host pass drops the kernel stub)
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + t + off),
+                                       (void*)&lds[buf][0][mload * 1024], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vbase + t + off),
+                                       (void*)&lds[buf][1][mload * 1024], 16, 0, 0);
     }
   };
-  // Swizzled LDS byte offset of chunk cc of row r.
-  auto lds_off = [](int r, int cc) {
-    constexpr int RPL = 16 / CPR;  // rows per 256-byte line of banks
-    return r * RB + ((cc ^ ((r / RPL) % CPR)) * 16);
-  };
-  auto store_stage = [&](int st, int buf) {
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      const int flat = threadIdx.x + NT * k;
-      const int r = flat / CPR, cc = flat % CPR;
-      u32x4 vv = gv[k];
-      if (st * KT + r > p_hi_wg) vv = u32x4{0u, 0u, 0u, 0u};  // stand-in / tail rows: V = 0
-      *reinterpret_cast<u32x4*>(&lds[buf][0][lds_off(r, cc)]) = gk[k];
-      *reinterpret_cast<u32x4*>(&lds[buf][1][lds_off(r, cc)]) = vv;
+  // This wave's loads of stage st are done once at most `later` stages' loads are outstanding.
+  auto wait_stage = [&](int later) {
+    // s_waitcnt: vmcnt in bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max
+    constexpr int per = 2 * WLW;
+    switch (later) {
+#define PA_WAIT_CASE(n) \
+  case n: __builtin_amdgcn_s_waitcnt(((n * per) & 15) | (((n * per) >> 4) << 14) | 0x0F70); break;
+      PA_WAIT_CASE(0)
+      PA_WAIT_CASE(1)
+      PA_WAIT_CASE(2)
+      PA_WAIT_CASE(3)
+#undef PA_WAIT_CASE
+      default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
     }
   };
 
-  issue_loads(0);
-  store_stage(0, 0);
-  if (nstages > 1) issue_loads(1);
-  __syncthreads();
+  const int prolog = nstages < NBUF - 1 ? nstages : NBUF - 1;
+  for (int st = 0; st < prolog; ++st) issue_stage(st);
 
   for (int st = 0; st < nstages; ++st) {
-    const int buf = st & 1;
+    const int later = (nstages - 1 - st) < (NBUF - 2) ? (nstages - 1 - st) : (NBUF - 2);
+    wait_stage(later);
+    // Every wave's loads of stage st have landed and stage st-1 is consumed. A bare barrier:
+    // a fence here would also wait for the later stages' loads still in flight. The empty asm
+    // keeps the compiler from moving LDS accesses across it.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (st + NBUF - 1 < nstages) issue_stage(st + NBUF - 1);  // into stage st-1's buffer
+    const int buf = st % NBUF;
 #pragma unroll
     for (int u2 = 0; u2 < NSUB; ++u2) {
       const int tau0 = st * KT + 32 * u2;
@@ -233,6 +244,10 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
             vf[u][i] = *reinterpret_cast<const u32x2*>(
                 &lds[buf][1][lds_off(rv, hh >> 1) + 8 * (hh & 1)]);
           }
+          // rows past the workgroup's last position are stand-ins or unused tail slots
+          // (possibly NaN): their weight is 0 and their V must be 0 too (select)
+          if (tau0 + 31 > p_hi_wg && tau0 + 16 * u + 4 * gq + i > p_hi_wg)
+            vf[u][i] = typename VF::T{};
         }
       }
       // V^T operand of M-tile mt, k element e <-> token 16*(e/4) + 4*gq + (e%4)
@@ -319,11 +334,6 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
         for (int c = 0; c < NCT; ++c)
           oacc[c][mt] = M::mma(__builtin_bit_cast(vec8, vw[mt]), pop[c], oacc[c][mt]);
     }
-    if (st + 1 < nstages) {
-      store_stage(st + 1, buf ^ 1);  // that buffer was last read before the previous barrier
-      if (st + 2 < nstages) issue_loads(st + 2);
-    }
-    __syncthreads();
   }
 
   // Normalise and store. oacc[c][mt][i] is O[column hh][dim MT*(4*gq + i) + mt]: for fixed i
@@ -375,7 +385,7 @@ static hipError_t launch_pf(const PrefillArgs& a, hipStream_t stream) {
   void* args[] = {&args_copy};
   return hipLaunchKernel(
       (const void*)prefill_mfma_kernel<dt, D, BS, kPrefillWaves, kPrefillColTiles,
-                                       kPrefillSubsteps>,
+                                       kPrefillSubsteps, kPrefillStages>,
       dim3((unsigned)total), dim3(kPrefillWaves * 64), args, 0, stream);
 }
 

@@ -61,6 +61,17 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(declared_functions()) | set(declared_functions(BM_HEADER)) <= exported
 
 
+def test_library_leaves_no_kernel_undefined():
+    """Every kernel the launchers reference is defined in libpa (a construct the host pass
+    rejects can drop a kernel's host stub without any diagnostic)."""
+    if not os.path.exists(pa.lib_path()):
+        pa_build.build()
+    out = subprocess.run(["nm", "-C", "--undefined-only", pa.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    missing = [l.strip() for l in out.splitlines() if "pa::" in l]
+    assert not missing, missing
+
+
 def test_header_compiles_as_c(tmp_path):
     src = tmp_path / "t.c"
     src.write_text('#include "pa.h"\n#include "pa_block_manager.h"\n'
