@@ -53,29 +53,37 @@ WORKLOADS = {
              "d=128, fp16) device -> pinned host and back"),
 }
 
-DECODE_SOURCES = ["paged_kv_cache_82_amd/csrc/pa_decode.hip",
-                  "paged_kv_cache_82_amd/csrc/pa_device.h",
-                  "paged_kv_cache_82_amd/csrc/pa_internal.h",
-                  "paged_kv_cache_82_amd/csrc/pa_api.hip"]
+# The sources each kernel family is built from: a committed counter summary is used only while
+# these files are unchanged since the counters were taken.
+KERNEL_SOURCES = {
+    "decode": ["paged_kv_cache_82_amd/csrc/pa_decode.hip",
+               "paged_kv_cache_82_amd/csrc/pa_device.h",
+               "paged_kv_cache_82_amd/csrc/pa_mfma.h",
+               "paged_kv_cache_82_amd/csrc/pa_internal.h"],
+    "prefill": ["paged_kv_cache_82_amd/csrc/pa_prefill.hip",
+                "paged_kv_cache_82_amd/csrc/pa_device.h",
+                "paged_kv_cache_82_amd/csrc/pa_mfma.h",
+                "paged_kv_cache_82_amd/csrc/pa_internal.h"],
+}
 
 
-def decode_source_hash() -> str:
+def source_hash(kind: str) -> str:
     h = hashlib.sha256()
-    for p in DECODE_SOURCES:
+    for p in KERNEL_SOURCES[kind]:
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes (read + written) per decode launch from the committed rocprofv3 counter
-    summary, if it was taken on the current decode sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"pa_decode_{workload}_pmc.txt")
+def measured_traffic(kind: str, workload: str):
+    """HBM bytes (read + written) per launch of the `kind` kernel from the committed rocprofv3
+    counter summary, if it was taken on the current sources of that kernel; else None."""
+    path = os.path.join(ROOT, "profiles", f"pa_{kind}_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    src = re.search(r"decode_source_sha256_16:\s*(\w+)", text)
+    src = re.search(r"source_sha256_16:\s*(\w+)", text)
     val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not src or not val or src.group(1) != decode_source_hash():
+    if not src or not val or src.group(1) != source_hash(kind):
         return None
     return float(val.group(1))
 
@@ -150,6 +158,18 @@ def prefill_flops(step) -> float:
         T = int(step.context_lens[s])
         total += n * (T - n) + n * (n + 1) // 2  # sum over i of (T - n + i + 1)
     return float(total) * step.num_q_heads * 4.0 * step.head_dim
+
+
+def prefill_bytes(step) -> float:
+    """HBM bytes one pa_prefill launch must move: each sequence's K and V once per KV head, the
+    q rows read and the out rows written, the block tables and lengths."""
+    e = step.elem_bytes
+    T = step.context_lens.astype(float)
+    B = step.block_size
+    kv = float(T.sum()) * 2 * step.num_kv_heads * step.head_dim * e
+    qo = 2.0 * step.num_q_tokens * step.num_q_heads * step.head_dim * e
+    idx = 4.0 * (float(sum(math.ceil(t / B) for t in T)) + 2 * step.num_seqs + 1)
+    return kv + qo + idx
 
 
 def prefill_cpu_baseline(step, budget_s: float = 12.0) -> dict:
@@ -279,8 +299,9 @@ def run_prefill(args):
             "peak": PEAK_MFMA_TFLOPS_16,
             "unit": "TFLOP/s",
             "frac": round(fl / att_s / 1e12 / PEAK_MFMA_TFLOPS_16, 4),
-            "traffic": None,
+            "traffic": measured_traffic("prefill", args.workload[len("prefill-"):]),
             "algorithmic_flops_per_launch": fl,
+            "algorithmic_bytes_per_launch": prefill_bytes(step),
             "avg_launch_us": round(att_s * 1e6, 3),
         },
         "input_generation_s": round(t_gen, 2),
@@ -486,7 +507,7 @@ def main():
     step_bytes = nb["decode"] + nb["write"]
     value = step_bytes / (wall / args.steps) / 1e9
     achieved = nb["decode"] / dec_s / 1e9
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic("decode", args.workload)
     res = {
         "metric": "paged decode attention: achieved HBM GB/s (% of peak) + seq-tokens/s",
         "value": round(value, 2),

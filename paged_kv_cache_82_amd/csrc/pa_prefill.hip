@@ -17,17 +17,17 @@
 //     query heads of its group; a workgroup of NW waves covers NW * NCT * 16 consecutive rows
 //     as 16-row column tiles dealt round-robin to the waves (so every wave reaches about the
 //     same causal depth);
-//   - the workgroup walks its context in stages of KT = 32 * NSUB tokens: every thread loads
-//     a few 16-byte chunks of the stage's K and V rows (through the block table) and writes
-//     them to an LDS tile, double-buffered, with the loads of the stage after next in flight
-//     while a stage is consumed; one barrier per stage;
+//   - the workgroup walks its context in 32-token stages: each wave loads 8 rows of the
+//     stage's K and V (rows of one block, found through the block table) straight from HBM
+//     into LDS, with two stages in flight while one is consumed; one barrier per stage;
 //   - LDS rows are XOR-swizzled in 16-byte chunks so that the MFMA operand reads (16 rows at
-//     one column for K, one row for V) and the stage writes hit distinct banks;
-//   - each wave reads a 32-token substep's K and V fragments once from LDS and uses them for
-//     all its column tiles (their MFMA chains interleave); a tile is masked only where the
-//     substep reaches past its first position;
-//   - each wave-wide load reads rows of one block, so its physical block id is wave-uniform
-//     and comes through the scalar cache;
+//     one column for K, one row for V) hit distinct banks;
+//   - each wave reads a stage's K and V fragments once from LDS and uses them for all its
+//     column tiles (their MFMA chains interleave); only stages that reach past the first
+//     position of one of the wave's tiles (the causal diagonal, and the workgroup's tail) take
+//     the masked path, every other stage runs without any per-score test;
+//   - a wave's physical block ids come 64 stages at a time into one register (lane k = stage
+//     k) and are broadcast with readlane;
 //   - workgroups are ordered so that the row tiles of one (sequence, KV head) run on one XCD
 //     (workgroups are dealt round-robin over the 8 XCDs) and share that XCD's L2, heaviest
 //     (latest) tiles first.
@@ -42,7 +42,6 @@ namespace {
 
 constexpr int kPrefillWaves = 4;     // waves per workgroup
 constexpr int kPrefillColTiles = 2;  // 16-row column tiles per wave
-constexpr int kPrefillSubsteps = 1;  // 32-token substeps per LDS stage
 constexpr int kPrefillStages = 3;    // LDS stage buffers (stages in flight + the one consumed)
 constexpr int kXcds = 8;             // MI355X: workgroups are dealt round-robin over 8 XCDs
 // A score may exceed the reference maximum by this much (base 2) before the running state is
@@ -53,9 +52,30 @@ __device__ __forceinline__ int clampi(int x, int lo, int hi) {
   return x < lo ? lo : (x > hi ? hi : x);
 }
 
+// Word holding 16-bit element e of x in its low half and of y in its high half (one
+// v_perm_b32: selector bytes 0-3 pick bytes of the second operand, 4-7 of the first).
+template <int D>
+__device__ __forceinline__ uint32_t vpair(const typename VFrag<D>::T& x,
+                                          const typename VFrag<D>::T& y, int e) {
+  return __builtin_amdgcn_perm(y[e >> 1], x[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to nearest-even 16-bit values, packed low/high (one v_cvt_pk_*_f32).
+template <DT dt>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (dt == DT::BF16) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+  }
+}
+
 }  // namespace
 
-template <DT dt, int D, int BS, int NW, int NCT, int NSUB, int NBUF>
+template <DT dt, int D, int BS, int NW, int NCT, int NBUF>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillArgs a) {
   static_assert(dt != DT::F32, "MFMA path takes 16-bit inputs");
   using M = MfmaT<dt>;
@@ -66,15 +86,15 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
   constexpr int MT = D / 16;        // p.V M-tiles; row r of tile mt is head dimension MT*r + mt
   constexpr int RB = D * E;         // bytes per token row
   constexpr int CPR = RB / 16;      // 16-byte chunks per row
-  constexpr int KT = 32 * NSUB;     // tokens per stage
-  constexpr int BPS = KT / BS;      // blocks per stage
+  constexpr int KT = 32;            // tokens per stage
   constexpr int RPL = 1024 / RB;    // rows one wave-wide 16-byte-per-lane load covers
   constexpr int WLW = KT * RB / 1024 / NW;  // wave-wide loads per wave per tensor per stage
+  constexpr int RPW = KT / NW;      // rows of a stage one wave loads: [RPW*w, RPW*(w+1))
   constexpr int ROWS_W = 16 * NCT;
   constexpr int ROWS = NW * ROWS_W;
   constexpr int TILE = KT * RB;     // LDS bytes per tensor per stage
-  static_assert(KT * RB % (1024 * NW) == 0, "a stage splits evenly over the waves");
-  static_assert(BS % RPL == 0 && 64 % BPS == 0, "a wave-wide load stays in one block");
+  static_assert(KT * RB % (1024 * NW) == 0 && WLW * RPL == RPW, "a stage splits over the waves");
+  static_assert(BS % RPW == 0, "the rows one wave loads lie in one block");
   __shared__ __attribute__((aligned(1024))) char lds[NBUF][2][TILE];  // [stage][K, V]
 
   // Workgroup -> (row tile, KV head, sequence). Linear id L runs on XCD L % 8; renumber so
@@ -113,10 +133,19 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
   const int w = wave_id();
   const int hh = lane & 15, gq = lane >> 4;
 
+  // The scores are scaled by cs > 0, so that the largest raw score gives the largest scaled
+  // one: a negative scale is applied as |scale| to the negated query, and a zero scale as 1
+  // to a zero query (every score 0, as with scale 0); both are exact.
+  const float cs = a.scale_log2 == 0.0f ? 1.0f : __builtin_fabsf(a.scale_log2);
+  const uint32_t qflip = a.scale_log2 < 0.0f ? 0x80008000u : 0u;
+  const uint32_t qkeep = a.scale_log2 == 0.0f ? 0u : 0xffffffffu;
+
   // Column tiles of this wave: tile c is workgroup column tile w + NW*c.
   int pos[NCT];                // position of this lane's query row; -1 past the chunk
-  int t_lo[NCT], t_hi[NCT];    // first / last position of the tile's rows (uniform); -1 if empty
+  int t_lo[NCT];               // first position of the tile's rows (uniform); -1 if empty
   vec8 qop[NCT][KC];
+  int p_hi_w = -1;             // last position any tile of this wave needs
+  int t_lo_w = 0x7fffffff;     // first position any tile of this wave starts at
 #pragma unroll
   for (int c = 0; c < NCT; ++c) {
     const int Rt = W0 + 16 * (w + NW * c);  // first row of the tile
@@ -126,19 +155,19 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
     const int head = kvh * g + (valid ? R % g : 0);
     pos[c] = valid ? base_pos + i : -1;
     t_lo[c] = Rt < nrows ? base_pos + Rt / g : -1;
-    t_hi[c] = Rt < nrows ? base_pos + ((Rt + 16 < nrows ? Rt + 16 : nrows) - 1) / g : -1;
+    const int t_hi = Rt < nrows ? base_pos + ((Rt + 16 < nrows ? Rt + 16 : nrows) - 1) / g : -1;
+    p_hi_w = t_hi > p_hi_w ? t_hi : p_hi_w;
+    t_lo_w = t_lo[c] < t_lo_w ? t_lo[c] : t_lo_w;
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) {
       u32x4 raw = {0u, 0u, 0u, 0u};
       if (valid)
         raw = load16((const char*)a.q +
                      (((int64_t)(q0 + i) * Hq + head) * D + 32 * kk + 8 * gq) * E);
+      raw = (raw ^ qflip) & qkeep;
       qop[c][kk] = __builtin_bit_cast(vec8, raw);
     }
   }
-  int p_hi_w = -1;  // last position any tile of this wave needs
-#pragma unroll
-  for (int c = 0; c < NCT; ++c) p_hi_w = t_hi[c] > p_hi_w ? t_hi[c] : p_hi_w;
 
   f32x4 oacc[NCT][MT];
   float m[NCT], lsum[NCT];
@@ -150,13 +179,17 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
     for (int mt = 0; mt < MT; ++mt) oacc[c][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Block ids: every wave-wide load reads rows of one block, so its id is wave-uniform and is
-  // read with a scalar load (scalar cache; counted apart from the K/V loads in flight).
-  // (The table is read-only during the kernel, so it is read through the constant address
-  // space, which lets uniform reads become scalar loads.)
-  typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
-  const const_i32_ptr bt =
-      (const_i32_ptr)(a.block_tables + (int64_t)s * a.max_blocks_per_seq);
+  // Block ids: the rows a wave loads in stage st lie in block (KT*st + RPW*w) / BS. Lane k of
+  // ids_cur holds that id for stage 64*id_chunk + k (clamped to the workgroup's last block:
+  // stages past it load stand-in rows that are masked later); the next 64 are loaded ahead.
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  auto load_ids = [&](int chunk) {
+    const int j = (KT * (64 * chunk + lane) + RPW * w) / BS;
+    return bt[j < jlast ? j : jlast];  // jlast < max_blocks_per_seq since T <= cap
+  };
+  int id_chunk = 0;
+  int ids_cur = load_ids(0);
+  int ids_nxt = load_ids(1);
 
   // LDS rows are swizzled in 16-byte chunks: chunk cc of row r sits at physical chunk
   // cc ^ swz(r), with swz running over the rows that share one 256-byte line of banks.
@@ -166,24 +199,26 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
   // Stage loads go straight from global memory into LDS (global_load_lds_dwordx4): lane L
   // of a wave-wide load writes LDS bytes [base + 16L, base + 16L + 16), so one load fills
   // 1 KB = RPL whole rows. Lane L carries physical chunk L % CPR of row L / CPR and fetches
-  // the logical chunk the swizzle maps there. No registers hold data in flight, so NBUF
-  // stages can be in flight.
+  // the logical chunk the swizzle maps there. No registers hold data in flight, so NBUF - 1
+  // stages can be in flight while one is consumed.
   const char* kbase = (const char*)a.k_cache;
   const char* vbase = (const char*)a.v_cache;
   const int64_t tile_bytes = (int64_t)BS * RB;
   const int row_in_load = lane / CPR;
   const int pchunk = lane % CPR;
-  auto issue_stage = [&](int st) {
-    const int buf = st % NBUF;
+  auto issue_stage = [&](int st, int buf) {
+    if ((st >> 6) != id_chunk) {  // uniform; stages are issued in order
+      ids_cur = ids_nxt;
+      ++id_chunk;
+      ids_nxt = load_ids(id_chunk + 1);
+    }
+    const int32_t id = __builtin_amdgcn_readlane(ids_cur, st & 63);
+    const int64_t t = (clamp_block(id, a.num_blocks) * Hkv + kvh) * tile_bytes;
 #pragma unroll
     for (int k = 0; k < WLW; ++k) {
-      const int mload = w * WLW + k;           // wave-wide load index within the tensor
+      const int mload = w * WLW + k;            // wave-wide load index within the tensor
       const int r = mload * RPL + row_in_load;  // row within the stage
       const int cc = pchunk ^ swz(r);           // logical chunk landing at physical pchunk
-      int j = st * BPS + (mload * RPL) / BS;    // the load's rows share one block (uniform)
-      j = j < jlast ? j : jlast;  // past the last needed block: stand-in rows, masked later
-      const int32_t id = bt[j];   // jlast < max_blocks_per_seq since T <= cap
-      const int64_t t = (clamp_block(id, a.num_blocks) * Hkv + kvh) * tile_bytes;
       const uint32_t off = (uint32_t)((r % BS) * RB + cc * 16);
       // (explicit void pointers: with char pointers clang's host pass drops the kernel stub)
       __builtin_amdgcn_global_load_lds((const void*)(kbase + t + off),
@@ -208,131 +243,145 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
     }
   };
 
-  const int prolog = nstages < NBUF - 1 ? nstages : NBUF - 1;
-  for (int st = 0; st < prolog; ++st) issue_stage(st);
-
-  for (int st = 0; st < nstages; ++st) {
-    const int later = (nstages - 1 - st) < (NBUF - 2) ? (nstages - 1 - st) : (NBUF - 2);
-    wait_stage(later);
-    // Every wave's loads of stage st have landed and stage st-1 is consumed. A bare barrier:
-    // a fence here would also wait for the later stages' loads still in flight. The empty asm
-    // keeps the compiler from moving LDS accesses across it.
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (st + NBUF - 1 < nstages) issue_stage(st + NBUF - 1);  // into stage st-1's buffer
-    const int buf = st % NBUF;
+  // One 32-token stage in LDS buffer `buf` for every column tile of this wave. `mask`
+  // (uniform): some token of the stage lies past some row's position, or past the
+  // workgroup's last position (stand-in or unused tail rows, possibly NaN); then hidden scores
+  // are set to -inf and V rows past the workgroup's last position to 0, both by select.
+  // Otherwise every token is visible to every row and no score is tested.
+  auto consume = [&](int tau0, int buf, bool mask) {
+    u32x4 kf[2][KC];
+    typename VF::T vf[2][4];
 #pragma unroll
-    for (int u2 = 0; u2 < NSUB; ++u2) {
-      const int tau0 = st * KT + 32 * u2;
-      if (tau0 > p_hi_w) break;  // uniform: every tile of this wave is done
-      const int rbase = 32 * u2;
-      u32x4 kf[2][KC];
-      typename VF::T vf[2][4];
+    for (int u = 0; u < 2; ++u) {
+      const int r = 16 * u + hh;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int r = rbase + 16 * u + hh;
+      for (int kk = 0; kk < KC; ++kk)
+        kf[u][kk] = *reinterpret_cast<const u32x4*>(&lds[buf][0][lds_off(r, 4 * kk + gq)]);
 #pragma unroll
-        for (int kk = 0; kk < KC; ++kk)
-          kf[u][kk] = *reinterpret_cast<const u32x4*>(&lds[buf][0][lds_off(r, 4 * kk + gq)]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rv = rbase + 16 * u + 4 * gq + i;
-          if constexpr (D == 128) {
-            vf[u][i] = *reinterpret_cast<const u32x4*>(&lds[buf][1][lds_off(rv, hh)]);
-          } else {
-            vf[u][i] = *reinterpret_cast<const u32x2*>(
-                &lds[buf][1][lds_off(rv, hh >> 1) + 8 * (hh & 1)]);
-          }
-          // rows past the workgroup's last position are stand-ins or unused tail slots
-          // (possibly NaN): their weight is 0 and their V must be 0 too (select)
-          if (tau0 + 31 > p_hi_wg && tau0 + 16 * u + 4 * gq + i > p_hi_wg)
-            vf[u][i] = typename VF::T{};
+      for (int i = 0; i < 4; ++i) {
+        const int rv = 16 * u + 4 * gq + i;
+        if constexpr (D == 128) {
+          vf[u][i] = *reinterpret_cast<const u32x4*>(&lds[buf][1][lds_off(rv, hh)]);
+        } else {
+          vf[u][i] = *reinterpret_cast<const u32x2*>(
+              &lds[buf][1][lds_off(rv, hh >> 1) + 8 * (hh & 1)]);
         }
       }
-      // V^T operand of M-tile mt, k element e <-> token 16*(e/4) + 4*gq + (e%4)
-      u32x4 vw[MT];
+    }
+    if (tau0 + KT - 1 > p_hi_wg) {  // uniform
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          const int e0 = 2 * q2, e1 = 2 * q2 + 1;
-          const uint32_t lo = vfrag_elem<D>(vf[e0 / 4][e0 % 4], mt);
-          const uint32_t hi = vfrag_elem<D>(vf[e1 / 4][e1 % 4], mt);
-          vw[mt][q2] = lo | (hi << 16);
-        }
-      // S^T = K Q^T for every column tile: 2*NCT independent accumulation chains. A tile whose
-      // rows all precede the substep is computed too and masked out entirely (straight-line
-      // code; this happens only in the last substeps of the diagonal).
-      f32x4 sacc[NCT][2];
+        for (int i = 0; i < 4; ++i)
+          if (tau0 + 16 * u + 4 * gq + i > p_hi_wg) vf[u][i] = typename VF::T{};
+    }
+    // S^T = K Q^T for every column tile: 2*NCT independent accumulation chains.
+    f32x4 sacc[NCT][2];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) sacc[c][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk)
 #pragma unroll
       for (int c = 0; c < NCT; ++c)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) sacc[c][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < 2; ++u)
+          sacc[c][u] = M::mma(__builtin_bit_cast(vec8, kf[u][kk]), qop[c][kk], sacc[c][u]);
+    // V^T operand of M-tile mt, k element e <-> token 16*(e/4) + 4*gq + (e%4)
+    u32x4 vw[MT];
 #pragma unroll
-      for (int kk = 0; kk < KC; ++kk)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int c = 0; c < NCT; ++c)
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-            sacc[c][u] = M::mma(__builtin_bit_cast(vec8, kf[u][kk]), qop[c][kk], sacc[c][u]);
-      // Scaled scores (base 2), masked by select. The weights are taken against a reference
-      // maximum m[c] that is raised only when some score exceeds it by more than kSlack:
-      // weights stay below 2^kSlack, and the running sum and output use the same reference,
-      // so the normalised result is the same as with the exact running maximum.
-      float sc[NCT][8];
-      float lm[NCT];
-      bool raise = false;
+      for (int q2 = 0; q2 < 4; ++q2) {
+        const int e0 = 2 * q2, e1 = 2 * q2 + 1;
+        vw[mt][q2] = vpair<D>(vf[e0 / 4][e0 % 4], vf[e1 / 4][e1 % 4], mt);
+      }
+    if (mask) {  // uniform; token 16u + 4gq + i is hidden from the lane's row past its position
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
-        const bool masked = tau0 + 31 > t_lo[c];  // uniform
-        lm[c] = kNegInf;
+        const int lim = pos[c] - tau0 - 4 * gq;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float x = sacc[c][u][i] * a.scale_log2;
-            if (masked && tau0 + 16 * u + 4 * gq + i > pos[c]) x = kNegInf;  // select
-            sc[c][4 * u + i] = x;
-            lm[c] = fmaxf(lm[c], x);
-          }
-        raise = raise || (lm[c] > m[c] + kSlack);
+          for (int i = 0; i < 4; ++i)
+            if (16 * u + i > lim) sacc[c][u][i] = kNegInf;  // select
       }
-      if (__builtin_amdgcn_ballot_w64(raise)) {  // uniform; rare once the maxima settle
+    }
+    // Weights are taken against a reference maximum m[c] (scaled, base 2) that is raised only
+    // when some score exceeds it by more than kSlack: weights stay below 2^kSlack, and the
+    // running sum and output use the same reference, so the normalised result is the same as
+    // with the exact running maximum. The scaled, shifted score cs * s - m is one FMA.
+    float lm[NCT];  // largest scaled score of the lane's 8
+    bool raise = false;
 #pragma unroll
-        for (int c = 0; c < NCT; ++c) {
-          float bm = fmaxf(lm[c], __shfl_xor(lm[c], 16));
-          bm = fmaxf(bm, __shfl_xor(bm, 32));
-          const float mn = fmaxf(m[c], bm);
-          const float corr = (m[c] == kNegInf) ? (mn == kNegInf ? 1.0f : 0.0f)
-                                               : fast_exp2(m[c] - mn);
-          lsum[c] *= corr;
+    for (int c = 0; c < NCT; ++c) {
+      float r = sacc[c][0][0];
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) oacc[c][mt] *= corr;
-          m[c] = mn;
-        }
-      }
-      vec8 pop[NCT];
+      for (int e = 1; e < 8; ++e) r = fmaxf(r, sacc[c][e / 4][e % 4]);
+      lm[c] = r * cs;
+      raise = raise || (lm[c] > m[c] + kSlack);
+    }
+    if (__builtin_amdgcn_ballot_w64(raise)) {  // uniform; rare once the maxima settle
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
-        // m[c] is -inf only while no row of the column has a visible token (then every x is
-        // -inf too): use 0 as the reference so that the weights are exp2(-inf) = 0
-        const float mref = (m[c] == kNegInf) ? 0.0f : m[c];
-        float ps = 0.0f;
+        float bm = fmaxf(lm[c], __shfl_xor(lm[c], 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float mn = fmaxf(m[c], bm);
+        const float corr = (m[c] == kNegInf) ? (mn == kNegInf ? 1.0f : 0.0f)
+                                             : fast_exp2(m[c] - mn);
+        lsum[c] *= corr;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pe = fast_exp2(sc[c][e] - mref);
-          ps += pe;
-          pop[c][e] = (typename M::scalar)pe;
-        }
-        lsum[c] += ps;
+        for (int mt = 0; mt < MT; ++mt) oacc[c][mt] *= corr;
+        m[c] = mn;
       }
-      // O^T += V^T P^T: MT * NCT independent MFMAs
+    }
+    vec8 pop[NCT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+    for (int c = 0; c < NCT; ++c) {
+      // m[c] is -inf only while every row of the column has all its tokens hidden (all its
+      // scores -inf): shift by 0 then, so the weights are exp2(-inf) = 0
+      const float nm = (m[c] == kNegInf) ? 0.0f : -m[c];
+      float pe[8];
 #pragma unroll
-        for (int c = 0; c < NCT; ++c)
-          oacc[c][mt] = M::mma(__builtin_bit_cast(vec8, vw[mt]), pop[c], oacc[c][mt]);
+      for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(__builtin_fmaf(sacc[c][e / 4][e % 4], cs, nm));
+      float ps = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ps += pe[e];
+      lsum[c] += ps;
+      const u32x4 pw = {pack2<dt>(pe[0], pe[1]), pack2<dt>(pe[2], pe[3]),
+                        pack2<dt>(pe[4], pe[5]), pack2<dt>(pe[6], pe[7])};
+      pop[c] = __builtin_bit_cast(vec8, pw);
+    }
+    // O^T += V^T P^T: MT * NCT independent MFMAs
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+        oacc[c][mt] = M::mma(__builtin_bit_cast(vec8, vw[mt]), pop[c], oacc[c][mt]);
+  };
+
+  const int prolog = nstages < NBUF - 1 ? nstages : NBUF - 1;
+  for (int st = 0; st < prolog; ++st) issue_stage(st, st);
+
+  // Stages are unrolled NBUF at a time so that every LDS buffer offset is a constant.
+  for (int st0 = 0; st0 < nstages; st0 += NBUF) {
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+      const int st = st0 + b;  // st % NBUF == b
+      if (st >= nstages) break;  // uniform
+      const int later = (nstages - 1 - st) < (NBUF - 2) ? (nstages - 1 - st) : (NBUF - 2);
+      wait_stage(later);
+      // Every wave's loads of stage st have landed and stage st-1 is consumed. A bare barrier:
+      // a fence here would also wait for the later stages' loads still in flight. The empty
+      // asm keeps the compiler from moving LDS accesses across it.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (st + NBUF - 1 < nstages) issue_stage(st + NBUF - 1, (b + NBUF - 1) % NBUF);
+      const int tau0 = st * KT;
+      if (tau0 > p_hi_w) continue;  // uniform: every tile of this wave is done
+      consume(tau0, b, tau0 + KT - 1 > t_lo_w);  // t_lo_w is -1 when a tile is empty
     }
   }
 
@@ -385,7 +434,7 @@ static hipError_t launch_pf(const PrefillArgs& a, hipStream_t stream) {
   void* args[] = {&args_copy};
   return hipLaunchKernel(
       (const void*)prefill_mfma_kernel<dt, D, BS, kPrefillWaves, kPrefillColTiles,
-                                       kPrefillSubsteps, kPrefillStages>,
+                                       kPrefillStages>,
       dim3((unsigned)total), dim3(kPrefillWaves * 64), args, 0, stream);
 }
 

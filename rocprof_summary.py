@@ -1,15 +1,15 @@
 """Summarise rocprofv3 CSV output into the short text files kept under profiles/.
 
   python rocprof_summary.py trace  <kernel_stats.csv> <out.txt> --command "<command>"
-  python rocprof_summary.py pmc    <workload> <out.txt> --fetch <csv> --write <csv>
+  python rocprof_summary.py pmc    decode|prefill <workload> <out.txt> --fetch <csv> --write <csv>
                                    --copy-fetch <csv> --copy-write <csv> --command "<command>"
 
 `trace` keeps the kernel table (calls, average/min/max duration) of a --kernel-trace --stats
-run. `pmc` turns FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the decode kernel into HBM
+run. `pmc` turns FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the decode or prefill kernel into HBM
 bytes per launch, each scaled by what the same counter reads for the plain copy kernel
 (pa_copy_blocks moving 4096 blocks of 256 KiB: 2 GiB read and 2 GiB written per launch), and
-records the hash of the decode sources so bench.py only reports the figure while those sources
-are unchanged.
+records the hash of that kernel's sources so bench.py only reports the figure while those
+sources are unchanged.
 """
 from __future__ import annotations
 
@@ -59,12 +59,20 @@ def do_pmc(args) -> str:
     cw = pick(kernel_avgs(args.copy_write), "copy_blocks_kernel")[1]
     f_factor = COPY_BYTES / (cf * 1024)
     w_factor = COPY_BYTES / (cw * 1024)
-    name, fk = pick(fetch, "decode_")
-    _, wk = pick(write, "decode_")
+    kind = args.kind
+    needle = {"decode": "decode_", "prefill": "prefill_mfma_kernel"}[kind]
+    name, fk = pick(fetch, needle)
+    _, wk = pick(write, needle)
     rd = fk * 1024 * f_factor
     wr = wk * 1024 * w_factor
-    step = bench.make_workload(args.workload, poison=False)
-    alg = bench.algorithmic_bytes(step)["decode"]
+    if kind == "decode":
+        step = bench.make_workload(args.workload, poison=False)
+        alg = bench.algorithmic_bytes(step)["decode"]
+    else:
+        import workloads
+
+        step = getattr(workloads, bench.WORKLOADS["prefill-" + args.workload][0])(poison=False)
+        alg = bench.prefill_bytes(step)
     lines = [
         f"command: {args.command}",
         f"kernel: {name}",
@@ -77,7 +85,7 @@ def do_pmc(args) -> str:
         f"hbm_bytes_per_launch: {rd + wr:.6g}",
         f"algorithmic_bytes_per_launch: {alg:.6g}",
         f"traffic_over_algorithmic: {(rd + wr) / alg:.4f}",
-        f"decode_source_sha256_16: {bench.decode_source_hash()}",
+        f"source_sha256_16: {bench.source_hash(kind)}",
     ]
     return "\n".join(lines) + "\n"
 
@@ -90,6 +98,7 @@ def main():
     t.add_argument("out")
     t.add_argument("--command", required=True)
     p = sub.add_parser("pmc")
+    p.add_argument("kind", choices=["decode", "prefill"])
     p.add_argument("workload")
     p.add_argument("out")
     for k in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--command"):

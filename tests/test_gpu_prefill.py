@@ -101,6 +101,15 @@ def test_prefill_large_scores_stay_finite():
     _check(step, "large scores")
 
 
+@pytest.mark.parametrize("scale", [0.0, -1.0 / 128 ** 0.5, 3.0])
+def test_prefill_scale_zero_negative_large(scale):
+    # scale 0 weighs every visible token equally (the mean of V over the causal prefix); a
+    # negative scale reverses the score order; both are taken exactly by the kernel
+    step = make_prefill_step("pscale", 465, [90, 300, 17], [90, 64, 17], 8, 2, 128, 16, "bf16",
+                             scale=scale)
+    _check(step, f"scale {scale}")
+
+
 def test_prefill_rows_outside_sequences_untouched():
     # query_start need not start at 0 nor end at num_q_tokens: rows no sequence owns keep
     # their contents
