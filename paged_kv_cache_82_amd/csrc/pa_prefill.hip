@@ -32,6 +32,8 @@
 //     (workgroups are dealt round-robin over the 8 XCDs) and share that XCD's L2, heaviest
 //     (latest) tiles first.
 // Scores are kept in the base-2 exponent domain: s' = s * log2(e), exp(s - m) = 2^(s' - m').
+#include <utility>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 #include "pa_mfma.h"
@@ -52,12 +54,65 @@ __device__ __forceinline__ int clampi(int x, int lo, int hi) {
   return x < lo ? lo : (x > hi ? hi : x);
 }
 
-// Word holding 16-bit element e of x in its low half and of y in its high half (one
-// v_perm_b32: selector bytes 0-3 pick bytes of the second operand, 4-7 of the first).
-template <int D>
-__device__ __forceinline__ uint32_t vpair(const typename VFrag<D>::T& x,
-                                          const typename VFrag<D>::T& y, int e) {
-  return __builtin_amdgcn_perm(y[e >> 1], x[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+// The V^T operand of the p.V product comes from ds_read_b64_tr_b16: inside each aligned group
+// of 16 lanes, lane 4q + p receives element p of the 8-byte chunks addressed by lanes q,
+// q + 4, q + 8 and q + 12 (in that order). The reads are issued from one asm block that also
+// waits for them: the compiler treats the intrinsic as possibly reading the LDS that the
+// stage loads (LDS DMA) are still writing and would drain every load in flight before it.
+// va[mt] is the lane's LDS byte address for M-tile mt and token tile u = 0 of stage buffer 0;
+// OFF0 / OFF1 are the byte offsets of the stage buffer's token tiles 0 and 1.
+template <int OFF0, int OFF1>
+__device__ __forceinline__ void lds_read_vt(u32x2 (&t)[8][2], const uint32_t (&va)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %2, %17 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %4, %18 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %5, %18 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %6, %19 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %8, %20 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %9, %20 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %10, %21 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %11, %21 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %12, %22 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %13, %22 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %14, %23 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(t[0][0]), "=&v"(t[0][1]), "=&v"(t[1][0]), "=&v"(t[1][1]), "=&v"(t[2][0]),
+        "=&v"(t[2][1]), "=&v"(t[3][0]), "=&v"(t[3][1]), "=&v"(t[4][0]), "=&v"(t[4][1]),
+        "=&v"(t[5][0]), "=&v"(t[5][1]), "=&v"(t[6][0]), "=&v"(t[6][1]), "=&v"(t[7][0]),
+        "=&v"(t[7][1])
+      : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]),
+        "v"(va[7]), "i"(OFF0), "i"(OFF1));
+}
+template <int OFF0, int OFF1>
+__device__ __forceinline__ void lds_read_vt(u32x2 (&t)[4][2], const uint32_t (&va)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %6, %11 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(t[0][0]), "=&v"(t[0][1]), "=&v"(t[1][0]), "=&v"(t[1][1]), "=&v"(t[2][0]),
+        "=&v"(t[2][1]), "=&v"(t[3][0]), "=&v"(t[3][1])
+      : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "i"(OFF0), "i"(OFF1));
+}
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>)
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -80,7 +135,6 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
   static_assert(dt != DT::F32, "MFMA path takes 16-bit inputs");
   using M = MfmaT<dt>;
   using vec8 = typename M::vec8;
-  using VF = VFrag<D>;
   constexpr int E = 2;
   constexpr int KC = D / 32;        // q.K MFMAs per 16-token tile
   constexpr int MT = D / 16;        // p.V M-tiles; row r of tile mt is head dimension MT*r + mt
@@ -180,21 +234,37 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
   }
 
   // Block ids: the rows a wave loads in stage st lie in block (KT*st + RPW*w) / BS. Lane k of
-  // ids_cur holds that id for stage 64*id_chunk + k (clamped to the workgroup's last block:
-  // stages past it load stand-in rows that are masked later); the next 64 are loaded ahead.
+  // `ids` holds that id for stage 64*(st/64) + k (clamped to the workgroup's last block:
+  // stages past it load stand-in rows that are masked later). The next 64 are loaded when the
+  // first of them is issued and used at once: one wait for the loads in flight per 64 stages,
+  // and no load of `ids` is ever outstanding across stages.
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   auto load_ids = [&](int chunk) {
     const int j = (KT * (64 * chunk + lane) + RPW * w) / BS;
     return bt[j < jlast ? j : jlast];  // jlast < max_blocks_per_seq since T <= cap
   };
-  int id_chunk = 0;
-  int ids_cur = load_ids(0);
-  int ids_nxt = load_ids(1);
+  int ids = load_ids(0);
 
   // LDS rows are swizzled in 16-byte chunks: chunk cc of row r sits at physical chunk
-  // cc ^ swz(r), with swz running over the rows that share one 256-byte line of banks.
-  auto swz = [](int r) { return (r / (16 / CPR)) % CPR; };
-  auto lds_off = [&](int r, int cc) { return r * RB + ((cc ^ swz(r)) * 16); };
+  // cc ^ swz(r). K (read as 16 rows at one chunk): swz runs over the rows that share one
+  // 256-byte line of banks. V (read transposed: 16 rows, two adjacent chunks each, per 32
+  // lanes): rows of a line take even offsets, so the two chunks of eight consecutive rows
+  // land on sixteen distinct chunk positions.
+  constexpr int RPBL = 256 / RB;  // rows per 256-byte line of banks
+  auto swz_k = [](int r) { return (r / RPBL) % CPR; };
+  auto swz_v = [](int r) { return (2 * ((r / RPBL) % (CPR / 2)) + (r / RPBL / (CPR / 2)) % 2); };
+  auto koff = [&](int r, int cc) { return r * RB + ((cc ^ swz_k(r)) * 16); };
+  auto voff = [&](int r, int cc) { return r * RB + ((cc ^ swz_v(r)) * 16); };
+  // Transposed V reads: lane (gq, s) addresses row 16u + 4gq + s/4, head dims
+  // 16mt + 4(s%4) .. +3 (swz_v repeats every 16 rows, so token tile u adds 16 rows).
+  typedef __attribute__((address_space(3))) char lds_char;
+  const uint32_t lds_v0 = (uint32_t)(uintptr_t)(lds_char*)&lds[0][1][0];
+  uint32_t va[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int cb = 32 * mt + 8 * (hh & 3);  // byte offset of the 4 dims in the row
+    va[mt] = lds_v0 + voff(4 * gq + (hh >> 2), cb >> 4) + (cb & 15);
+  }
 
   // Stage loads go straight from global memory into LDS (global_load_lds_dwordx4): lane L
   // of a wave-wide load writes LDS bytes [base + 16L, base + 16L + 16), so one load fills
@@ -207,23 +277,23 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
   const int row_in_load = lane / CPR;
   const int pchunk = lane % CPR;
   auto issue_stage = [&](int st, int buf) {
-    if ((st >> 6) != id_chunk) {  // uniform; stages are issued in order
-      ids_cur = ids_nxt;
-      ++id_chunk;
-      ids_nxt = load_ids(id_chunk + 1);
+    if (st > 0 && (st & 63) == 0) {  // uniform
+      ids = load_ids(st >> 6);
+      __builtin_amdgcn_s_waitcnt(0x0F70 & ~0x0F);  // vmcnt(0): ids is never pending past here
     }
-    const int32_t id = __builtin_amdgcn_readlane(ids_cur, st & 63);
+    const int32_t id = __builtin_amdgcn_readlane(ids, st & 63);
     const int64_t t = (clamp_block(id, a.num_blocks) * Hkv + kvh) * tile_bytes;
 #pragma unroll
     for (int k = 0; k < WLW; ++k) {
       const int mload = w * WLW + k;            // wave-wide load index within the tensor
       const int r = mload * RPL + row_in_load;  // row within the stage
-      const int cc = pchunk ^ swz(r);           // logical chunk landing at physical pchunk
-      const uint32_t off = (uint32_t)((r % BS) * RB + cc * 16);
+      // logical chunks landing at physical chunk pchunk of row r
+      const uint32_t ko = (uint32_t)((r % BS) * RB + (pchunk ^ swz_k(r)) * 16);
+      const uint32_t vo = (uint32_t)((r % BS) * RB + (pchunk ^ swz_v(r)) * 16);
       // (explicit void pointers: with char pointers clang's host pass drops the kernel stub)
-      __builtin_amdgcn_global_load_lds((const void*)(kbase + t + off),
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + t + ko),
                                        (void*)&lds[buf][0][mload * 1024], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vbase + t + off),
+      __builtin_amdgcn_global_load_lds((const void*)(vbase + t + vo),
                                        (void*)&lds[buf][1][mload * 1024], 16, 0, 0);
     }
   };
@@ -248,32 +318,34 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
   // workgroup's last position (stand-in or unused tail rows, possibly NaN); then hidden scores
   // are set to -inf and V rows past the workgroup's last position to 0, both by select.
   // Otherwise every token is visible to every row and no score is tested.
-  auto consume = [&](int tau0, int buf, bool mask) {
+  auto consume = [&](int tau0, auto bufc, bool mask) {
+    constexpr int buf = decltype(bufc)::value;
     u32x4 kf[2][KC];
-    typename VF::T vf[2][4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int r = 16 * u + hh;
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int kk = 0; kk < KC; ++kk)
-        kf[u][kk] = *reinterpret_cast<const u32x4*>(&lds[buf][0][lds_off(r, 4 * kk + gq)]);
+        kf[u][kk] = *reinterpret_cast<const u32x4*>(&lds[buf][0][koff(16 * u + hh, 4 * kk + gq)]);
+    // V^T operand of M-tile mt (head dims 16mt .. 16mt+15), k element e <-> token
+    // 16*(e/4) + 4*gq + (e%4): the transposed read hands lane (gq, 4q + p) dim 16mt + 4q + p
+    // of tokens 16u + 4gq + 0..3.
+    u32x2 tv[MT][2];
+    lds_read_vt<buf * 2 * TILE, buf * 2 * TILE + 16 * RB>(tv, va);
+    u32x4 vw[MT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rv = 16 * u + 4 * gq + i;
-        if constexpr (D == 128) {
-          vf[u][i] = *reinterpret_cast<const u32x4*>(&lds[buf][1][lds_off(rv, hh)]);
-        } else {
-          vf[u][i] = *reinterpret_cast<const u32x2*>(
-              &lds[buf][1][lds_off(rv, hh >> 1) + 8 * (hh & 1)]);
+    for (int mt = 0; mt < MT; ++mt) vw[mt] = u32x4{tv[mt][0][0], tv[mt][0][1], tv[mt][1][0], tv[mt][1][1]};
+    if (tau0 + KT - 1 > p_hi_wg) {  // uniform: V of tokens past the last position is 0
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int t0 = tau0 + 16 * u + 4 * gq;  // token of element 4u
+        const uint32_t keep0 = (t0 > p_hi_wg ? 0u : 0xffffu) | (t0 + 1 > p_hi_wg ? 0u : 0xffff0000u);
+        const uint32_t keep1 = (t0 + 2 > p_hi_wg ? 0u : 0xffffu) | (t0 + 3 > p_hi_wg ? 0u : 0xffff0000u);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          vw[mt][2 * u] &= keep0;
+          vw[mt][2 * u + 1] &= keep1;
         }
       }
-    }
-    if (tau0 + KT - 1 > p_hi_wg) {  // uniform
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (tau0 + 16 * u + 4 * gq + i > p_hi_wg) vf[u][i] = typename VF::T{};
     }
     // S^T = K Q^T for every column tile: 2*NCT independent accumulation chains.
     f32x4 sacc[NCT][2];
@@ -288,15 +360,6 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
 #pragma unroll
         for (int u = 0; u < 2; ++u)
           sacc[c][u] = M::mma(__builtin_bit_cast(vec8, kf[u][kk]), qop[c][kk], sacc[c][u]);
-    // V^T operand of M-tile mt, k element e <-> token 16*(e/4) + 4*gq + (e%4)
-    u32x4 vw[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) {
-        const int e0 = 2 * q2, e1 = 2 * q2 + 1;
-        vw[mt][q2] = vpair<D>(vf[e0 / 4][e0 % 4], vf[e1 / 4][e1 % 4], mt);
-      }
     if (mask) {  // uniform; token 16u + 4gq + i is hidden from the lane's row past its position
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
@@ -366,10 +429,10 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
 
   // Stages are unrolled NBUF at a time so that every LDS buffer offset is a constant.
   for (int st0 = 0; st0 < nstages; st0 += NBUF) {
-#pragma unroll
-    for (int b = 0; b < NBUF; ++b) {
+    static_for<NBUF>([&](auto bc) {
+      constexpr int b = decltype(bc)::value;
       const int st = st0 + b;  // st % NBUF == b
-      if (st >= nstages) break;  // uniform
+      if (st >= nstages) return;  // uniform
       const int later = (nstages - 1 - st) < (NBUF - 2) ? (nstages - 1 - st) : (NBUF - 2);
       wait_stage(later);
       // Every wave's loads of stage st have landed and stage st-1 is consumed. A bare barrier:
@@ -380,13 +443,13 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
       asm volatile("" ::: "memory");
       if (st + NBUF - 1 < nstages) issue_stage(st + NBUF - 1, (b + NBUF - 1) % NBUF);
       const int tau0 = st * KT;
-      if (tau0 > p_hi_w) continue;  // uniform: every tile of this wave is done
-      consume(tau0, b, tau0 + KT - 1 > t_lo_w);  // t_lo_w is -1 when a tile is empty
-    }
+      if (tau0 > p_hi_w) return;  // uniform: every tile of this wave is done
+      consume(tau0, bc, tau0 + KT - 1 > t_lo_w);  // t_lo_w is -1 when a tile is empty
+    });
   }
 
-  // Normalise and store. oacc[c][mt][i] is O[column hh][dim MT*(4*gq + i) + mt]: for fixed i
-  // the MT values are consecutive dimensions, one 16-byte (D = 128) or 8-byte (D = 64) store.
+  // Normalise and store. oacc[c][mt][i] is O[column hh][dim 16mt + 4gq + i]: four
+  // consecutive dimensions, one 8-byte store per M-tile.
 #pragma unroll
   for (int c = 0; c < NCT; ++c) {
     float l = lsum[c];
@@ -397,21 +460,12 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
     const int i = R / g;
     const int head = kvh * g + R % g;
     char* orow = (char*)a.out + ((int64_t)(q0 + i) * Hq + head) * D * E;
+    const float rl = 1.0f / l;
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      uint32_t packed[MT / 2];
-#pragma unroll
-      for (int h2 = 0; h2 < MT / 2; ++h2) {
-        const uint32_t lo = narrow_bits<dt>(oacc[c][2 * h2][i4] / l);
-        const uint32_t hi = narrow_bits<dt>(oacc[c][2 * h2 + 1][i4] / l);
-        packed[h2] = lo | (hi << 16);
-      }
-      char* dst = orow + MT * (4 * gq + i4) * E;
-      if constexpr (MT == 8) {
-        *reinterpret_cast<u32x4*>(dst) = u32x4{packed[0], packed[1], packed[2], packed[3]};
-      } else {
-        *reinterpret_cast<u32x2*>(dst) = u32x2{packed[0], packed[1]};
-      }
+    for (int mt = 0; mt < MT; ++mt) {
+      const u32x2 packed = {pack2<dt>(oacc[c][mt][0] * rl, oacc[c][mt][1] * rl),
+                            pack2<dt>(oacc[c][mt][2] * rl, oacc[c][mt][3] * rl)};
+      *reinterpret_cast<u32x2*>(orow + (16 * mt + 4 * gq) * E) = packed;
     }
   }
 }
