@@ -326,9 +326,28 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
 #pragma unroll
       for (int kk = 0; kk < KC; ++kk)
         kf[u][kk] = *reinterpret_cast<const u32x4*>(&lds[buf][0][koff(16 * u + hh, 4 * kk + gq)]);
+    // S^T = K Q^T for every column tile: 2*NCT independent accumulation chains.
+    f32x4 sacc[NCT][2];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) sacc[c][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // The MFMA blocks run at raised wave priority, so that a wave holding matrix work issues
+    // it ahead of the other wave's vector work on the same SIMD.
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk)
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          sacc[c][u] = M::mma(__builtin_bit_cast(vec8, kf[u][kk]), qop[c][kk], sacc[c][u]);
+    __builtin_amdgcn_s_setprio(0);
     // V^T operand of M-tile mt (head dims 16mt .. 16mt+15), k element e <-> token
     // 16*(e/4) + 4*gq + (e%4): the transposed read hands lane (gq, 4q + p) dim 16mt + 4q + p
     // of tokens 16u + 4gq + 0..3.
+    // (issued once the scores' MFMAs are: their latency overlaps the matrix cores)
+    __builtin_amdgcn_sched_barrier(0);
     u32x2 tv[MT][2];
     lds_read_vt<buf * 2 * TILE, buf * 2 * TILE + 16 * RB>(tv, va);
     u32x4 vw[MT];
@@ -347,19 +366,6 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
         }
       }
     }
-    // S^T = K Q^T for every column tile: 2*NCT independent accumulation chains.
-    f32x4 sacc[NCT][2];
-#pragma unroll
-    for (int c = 0; c < NCT; ++c)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) sacc[c][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < KC; ++kk)
-#pragma unroll
-      for (int c = 0; c < NCT; ++c)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          sacc[c][u] = M::mma(__builtin_bit_cast(vec8, kf[u][kk]), qop[c][kk], sacc[c][u]);
     if (mask) {  // uniform; token 16u + 4gq + i is hidden from the lane's row past its position
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
@@ -408,20 +414,19 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
       float pe[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(__builtin_fmaf(sacc[c][e / 4][e % 4], cs, nm));
-      float ps = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ps += pe[e];
-      lsum[c] += ps;
+      lsum[c] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
       const u32x4 pw = {pack2<dt>(pe[0], pe[1]), pack2<dt>(pe[2], pe[3]),
                         pack2<dt>(pe[4], pe[5]), pack2<dt>(pe[6], pe[7])};
       pop[c] = __builtin_bit_cast(vec8, pw);
     }
     // O^T += V^T P^T: MT * NCT independent MFMAs
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int c = 0; c < NCT; ++c)
         oacc[c][mt] = M::mma(__builtin_bit_cast(vec8, vw[mt]), pop[c], oacc[c][mt]);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   const int prolog = nstages < NBUF - 1 ? nstages : NBUF - 1;
