@@ -15,7 +15,7 @@ import oracle
 import paged_kv_cache_82_amd as pa
 from gpu_harness import assert_attention_close, to_dev, to_host
 from paged_kv_cache_82_amd.block_manager import BlockManager
-from workloads import full, nan_value, to_storage
+from workloads import full, nan_value, to_float64, to_storage
 
 pytestmark = pytest.mark.gpu
 
@@ -89,3 +89,67 @@ def test_sampling_and_swap_driven_by_the_native_manager():
     assert bm.tables([2])[0].tolist() != tables[2, :bm.num_seq_blocks(2)].tolist()
     again = decode(bm.tables([2]), np.array([bm.length(2)], np.int32), to_dev(q[2:3], dt))
     assert np.array_equal(again.view(np.uint16), got[2:3].view(np.uint16))
+
+
+def test_chunked_prefill_fork_and_decode_driven_by_the_native_manager():
+    # Two prompts prefilled in chunks of different lengths, batched into the same calls
+    # ([PA-summary] "vLLM": new requests join each iteration), blocks allocated on demand by
+    # the native manager; then prompt 0 forks into two samples (copy-on-write of its partly
+    # filled last block) and every sequence takes one decode step, through pa_prefill (n = 1)
+    # and pa_decode alike. Each call is checked against the oracle on the same pool.
+    rng = np.random.default_rng(910)
+    N, B, Hq, Hkv, d, dt = 96, 16, 16, 2, 128, "bf16"
+    scale = np.float32(1 / np.sqrt(d))
+    bm = BlockManager(N, B, rng.permutation(N))
+    kc = full((N, Hkv, B, d), nan_value(dt), dt)
+    vc = kc.copy()
+    dk, dv = to_dev(kc, dt), to_dev(vc, dt)
+
+    def step(seqs, counts):
+        """Append counts[i] tokens to seqs[i], write them, attend with their queries."""
+        slots, kn, vn = [], [], []
+        for s, n in zip(seqs, counts):
+            sl, pairs = bm.append(s, n)
+            if len(pairs):
+                oracle.copy_blocks(kc, vc, pairs, dt)
+                pa.pa_copy_blocks(dk, dv, to_dev(pairs))
+            k1, v1 = _kv(rng, n, Hkv, d, dt)
+            slots.append(sl)
+            kn.append(k1)
+            vn.append(v1)
+        slots, kn, vn = np.concatenate(slots), np.concatenate(kn), np.concatenate(vn)
+        oracle.write_kv(kc, vc, kn, vn, slots, dt)
+        pa.pa_write_kv(dk, dv, to_dev(kn, dt), to_dev(vn, dt), to_dev(slots))
+        q = to_storage(rng.standard_normal((int(sum(counts)), Hq, d)).astype(np.float32), dt)
+        qs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        tables = bm.tables(seqs)
+        lens = np.array([bm.length(s) for s in seqs], np.int32)
+        out = torch.empty_like(to_dev(q, dt))
+        pa.pa_prefill(out, to_dev(q, dt), dk, dv, to_dev(tables), to_dev(lens), to_dev(qs),
+                      float(scale), int(max(counts)), int(lens.max()))
+        torch.cuda.synchronize()
+        got = to_host(out, dt)
+        ref = oracle.prefill(q, kc, vc, tables, lens, qs, scale, dt)
+        assert_attention_close(got, ref, dt, f"chunks {counts}")
+        return q, tables, lens, got
+
+    bm.add(0)
+    bm.add(1)
+    for counts in ([128, 50], [100, 200], [77, 1]):  # prompt 0: 305 tokens, prompt 1: 251
+        step([0, 1], counts)
+    assert np.array_equal(to_host(dk, dt).view(np.uint16), kc.view(np.uint16))
+    for c in (2, 3):
+        bm.fork(0, c)
+    seqs = [0, 1, 2, 3]
+    q, tables, lens, got = step(seqs, [1, 1, 1, 1])
+    assert bm.stats()["shared_blocks"] == 305 // B  # the full prompt blocks stay shared
+    out = torch.empty_like(to_dev(q, dt))
+    ws = torch.empty(max(1, pa.pa_decode_workspace_size(4, Hq, Hkv, d, B, int(lens.max()), 0,
+                                                        torch.bfloat16)),
+                     dtype=torch.uint8, device="cuda")
+    pa.pa_decode(out, to_dev(q, dt), dk, dv, to_dev(tables), to_dev(lens), float(scale),
+                 int(lens.max()), ws)
+    torch.cuda.synchronize()
+    assert_attention_close(to_host(out, dt), oracle.decode(q, kc, vc, tables, lens, scale, dt),
+                           dt, "decode after fork")
+    assert_attention_close(got, to_float64(to_host(out, dt), dt), dt, "prefill n=1 vs decode")
