@@ -32,15 +32,15 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, vendor figure
 PEAK_MFMA_TFLOPS_16 = 2500.0  # MI355X dense fp16/bf16 matrix peak, vendor figure
 
 WORKLOADS = {
-    "mha13b": ("config2", "13B-shape fp16 MHA decode: 64 seqs, 40 heads, d=128, B=16, "
+    "mha13b": ("mha13b_f16", "13B-shape fp16 MHA decode: 64 seqs, 40 heads, d=128, B=16, "
                "lognormal lengths (median 512) clipped to [16,2048]"),
-    "gqa": ("config3", "GQA bf16 decode: 256 seqs, 64 query / 8 KV heads, d=128, B=16, "
+    "gqa": ("gqa_bf16", "GQA bf16 decode: 256 seqs, 64 query / 8 KV heads, d=128, B=16, "
             "lengths uniform in [128,4096]"),
-    "long": ("config4", "long-context bf16 split-K decode: 8 seqs, 32 heads, d=128, B=16, "
+    "long": ("long_bf16", "long-context bf16 split-K decode: 8 seqs, 32 heads, d=128, B=16, "
              "lengths uniform in [32768,131072]"),
-    "shared": ("config5", "shared-prefix fp16 decode: 16 prompts x 4 samples, 32 heads, "
+    "shared": ("shared_prefix_f16", "shared-prefix fp16 decode: 16 prompts x 4 samples, 32 heads, "
                "d=128, B=32, 1297 tokens each"),
-    "tiny": ("config1", "tiny fp32 decode: 4 seqs (7,16,33,50), 8 heads, d=64, B=16"),
+    "tiny": ("tiny_f32", "tiny fp32 decode: 4 seqs (7,16,33,50), 8 heads, d=64, B=16"),
     "prefill-mha13b": ("prefill_mha13b", "chunked prefill, 13B shape fp16 MHA: 16 seqs, 40 heads, "
                        "d=128, B=16, 512-token chunks after lognormal (median 512) prefixes "
                        "clipped to [0,1536]"),
@@ -107,7 +107,7 @@ def make_workload(name: str, poison: bool, placement: str = "random"):
 
     cfg = WORKLOADS[name][0]
     kw = {"poison": poison}
-    if placement == "contiguous" and cfg != "config5":
+    if placement == "contiguous" and cfg != "shared_prefix_f16":
         kw["alloc_rng"] = workloads.InOrder()
     return getattr(workloads, cfg)(**kw)
 
@@ -406,7 +406,7 @@ def main():
     if args.workload == "sharing":
         return run_sharing(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
               "(sequences and KV heads would shard with no exchange; see the design notes).",
               file=sys.stderr)
         sys.exit(2)

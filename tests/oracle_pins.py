@@ -37,7 +37,7 @@ import numpy as np
 import torch
 
 import oracle
-from workloads import (BlockAllocator, Sequence, append_tokens, block_tables_array, config5,
+from workloads import (BlockAllocator, Sequence, append_tokens, block_tables_array, shared_prefix_f16,
                        make_prefill_step, make_step, to_float64, to_storage)
 from oracle import blockwise
 
@@ -324,8 +324,8 @@ def pin_poison_invariance(lib):
 def pin_shared_prefix_matches_private(lib):
     kw = dict(prompts=2, samples=3, prompt_len=21, tail_len=9, heads=2, head_dim=8,
               block_size=4, dtype="f16", keep_logical=True)
-    shared = config5(**kw)
-    private = config5(private=True, **kw)
+    shared = shared_prefix_f16(**kw)
+    private = shared_prefix_f16(private=True, **kw)
     assert len(shared.copies) == 2 * 2 and len(private.copies) == 0
     a = _run(shared, lib)
     b = _run(private, lib)

@@ -15,7 +15,7 @@ torch = pytest.importorskip("torch")
 
 import oracle
 from gpu_harness import DevStep, assert_attention_close, to_dev, to_host
-from workloads import config2, config3, config4
+from workloads import mha13b_f16, gqa_bf16, long_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -29,21 +29,21 @@ def _full(step):
     return assert_attention_close(got, ref, step.dtype, step.name)
 
 
-def test_config2_mha13b_f16_full():
-    print("\n[gpu-test] config2 full", flush=True)
-    err = _full(config2())
-    print(f"config2 max abs err {err:.3g}", flush=True)
+def test_mha13b_f16_full():
+    print("\n[gpu-test] mha13b_f16 full", flush=True)
+    err = _full(mha13b_f16())
+    print(f"mha13b_f16 max abs err {err:.3g}", flush=True)
 
 
-def test_config3_gqa_bf16_full():
-    print("\n[gpu-test] config3 full", flush=True)
-    err = _full(config3())
-    print(f"config3 max abs err {err:.3g}", flush=True)
+def test_gqa_bf16_full():
+    print("\n[gpu-test] gqa_bf16 full", flush=True)
+    err = _full(gqa_bf16())
+    print(f"gqa_bf16 max abs err {err:.3g}", flush=True)
 
 
-def test_config4_long_bf16_sampled():
-    print("\n[gpu-test] config4 sampled", flush=True)
-    step = config4()
+def test_long_bf16_sampled():
+    print("\n[gpu-test] long_bf16 sampled", flush=True)
+    step = long_bf16()
     dev = DevStep(step)
     k_before = dev.k_cache.clone()
     got = dev.run()
@@ -60,6 +60,6 @@ def test_config4_long_bf16_sampled():
     del k_before
     sample = [int(np.argmin(step.context_lens)), int(np.argmax(step.context_lens))]
     ref, _, _ = oracle.run_step(step, seq_list=sample, in_place=True)
-    err = assert_attention_close(got[sample], ref, step.dtype, "config4 sample")
-    print(f"config4 sample {sample} lens {step.context_lens[sample].tolist()} max abs err {err:.3g}",
+    err = assert_attention_close(got[sample], ref, step.dtype, "long_bf16 sample")
+    print(f"long_bf16 sample {sample} lens {step.context_lens[sample].tolist()} max abs err {err:.3g}",
           flush=True)

@@ -10,7 +10,7 @@ torch = pytest.importorskip("torch")
 
 import oracle
 from gpu_harness import DevStep, assert_attention_close, to_host
-from workloads import config1, config5, make_step, to_float64, to_storage
+from workloads import tiny_f32, shared_prefix_f16, make_step, to_float64, to_storage
 
 pytestmark = pytest.mark.gpu
 
@@ -36,8 +36,8 @@ def _announce(request):
     yield
 
 
-def test_config1_tiny_f32():
-    got, ref = _run_and_check(config1(), what="config1")
+def test_tiny_f32():
+    got, ref = _run_and_check(tiny_f32(), what="tiny_f32")
     assert np.abs(got.astype(np.float64) - ref).max() <= 1e-5
 
 
@@ -78,9 +78,9 @@ def test_forced_split_k_gqa(P):
     _run_and_check(step, partition_tokens=P, what=f"gqa P={P}")
 
 
-def test_config1_split_k_every_partition_size():
+def test_tiny_split_k_every_partition_size():
     for P in (32, 64, 96, 128, 512):
-        _run_and_check(config1(), partition_tokens=P, what=f"config1 P={P}")
+        _run_and_check(tiny_f32(), partition_tokens=P, what=f"tiny_f32 P={P}")
 
 
 def test_empty_and_single_token_sequences():
@@ -159,20 +159,20 @@ def test_nondefault_stream():
     assert_attention_close(to_host(dev.out, "bf16"), ref, "bf16", "stream")
 
 
-def test_config5_small_shared_vs_private():
+def test_shared_prefix_small_shared_vs_private():
     kw = dict(prompts=3, samples=4, prompt_len=70, tail_len=20, heads=4, head_dim=128,
               block_size=32, dtype="f16")
-    shared = config5(**kw)
-    private = config5(private=True, **kw)
+    shared = shared_prefix_f16(**kw)
+    private = shared_prefix_f16(private=True, **kw)
     a, _ = _run_and_check(shared, what="shared")
     b, _ = _run_and_check(private, what="private")
     assert np.array_equal(a, b)
 
 
-def test_config5_full():
-    shared = config5()
-    a, _ = _run_and_check(shared, what="config5 shared")
-    b = DevStep(config5(private=True)).run()
+def test_shared_prefix_full():
+    shared = shared_prefix_f16()
+    a, _ = _run_and_check(shared, what="shared_prefix_f16 shared")
+    b = DevStep(shared_prefix_f16(private=True)).run()
     assert np.array_equal(a, b)
 
 

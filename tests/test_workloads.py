@@ -4,22 +4,22 @@ import math
 import numpy as np
 import pytest
 
-from workloads import (BlockAllocator, PoolExhausted, Sequence, append_tokens, config1,
-                       config5, fork, make_step, release, wasted_slots)
-from workloads.configs import (config2, config2_lengths, config3, config3_lengths,
-                               config4_lengths)
+from workloads import (BlockAllocator, PoolExhausted, Sequence, append_tokens, tiny_f32,
+                       shared_prefix_f16, fork, make_step, release, wasted_slots)
+from workloads.configs import (mha13b_f16, mha13b_lengths, gqa_bf16, gqa_lengths,
+                               long_lengths)
 
 
 def test_generators_are_deterministic():
-    a = config1()
-    b = config1()
+    a = tiny_f32()
+    b = tiny_f32()
     for x, y in ((a.k_cache, b.k_cache), (a.v_cache, b.v_cache), (a.q, b.q),
                  (a.block_tables, b.block_tables), (a.writes[0].slot_mapping, b.writes[0].slot_mapping)):
         assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
 
 
-def test_config1_shape():
-    st = config1()
+def test_tiny_shape():
+    st = tiny_f32()
     assert st.k_cache.shape == (64, 8, 16, 64) and st.dtype == "f32"
     assert list(st.context_lens) == [7, 16, 33, 50]
     assert st.block_tables.shape == (4, 4)
@@ -36,12 +36,12 @@ def test_config1_shape():
 
 
 def test_length_distributions():
-    t2 = config2_lengths()
+    t2 = mha13b_lengths()
     assert t2.min() >= 16 and t2.max() <= 2048 and len(t2) == 64
     assert 300 < np.median(t2) < 900
-    t3 = config3_lengths()
+    t3 = gqa_lengths()
     assert t3.min() >= 128 and t3.max() <= 4096 and len(t3) == 256
-    t4 = config4_lengths()
+    t4 = long_lengths()
     assert t4.min() >= 32768 and t4.max() <= 131072 and len(t4) == 8
 
 
@@ -83,8 +83,8 @@ def test_fork_and_copy_on_write():
     assert root.table[0] == kids[0].table[0] == kids[1].table[0] and al.ref[root.table[0]] == 3
 
 
-def test_config5_structure():
-    st = config5(poison=False)
+def test_shared_prefix_structure():
+    st = shared_prefix_f16(poison=False)
     assert st.num_seqs == 64 and st.block_size == 32 and st.dtype == "f16"
     assert len(st.copies) == 48
     assert (st.context_lens == 1297).all()
@@ -100,9 +100,9 @@ def test_config5_structure():
     assert len(set(dst.tolist())) == 48 and not set(dst.tolist()) & set(src.tolist())
 
 
-def test_config2_config3_metadata_small():
+def test_mha13b_gqa_metadata_small():
     # structure only (pools are big): block counts agree with the lengths
-    for fn, H in ((config2, 40), (config3, 8)):
+    for fn, H in ((mha13b_f16, 40), (gqa_bf16, 8)):
         st = fn(poison=False)
         assert st.k_cache.shape[1] == H
         nblk = (st.block_tables >= 0).sum(axis=1)

@@ -336,47 +336,47 @@ def prefill_gqa(**kw) -> PrefillStep:
     return make_prefill_step("prefill-gqa-bf16", 7, prefix + n, n, 64, 8, 128, 16, "bf16", **kw)
 
 
-# ---- the five workloads ---------------------------------------------------------------------
+# ---- the decode workloads ---------------------------------------------------------------------
 
 
-def config1(**kw) -> DecodeStep:
+def tiny_f32(**kw) -> DecodeStep:
     """Tiny fp32: 4 sequences of lengths 7, 16, 33, 50; 8 heads, d=64, B=16, 64-block pool."""
     return make_step("tiny-f32", 1, [7, 16, 33, 50], 8, 8, 64, 16, "f32", num_blocks=64, **kw)
 
 
-def config2_lengths(seed: int = 2, S: int = 64) -> np.ndarray:
+def mha13b_lengths(seed: int = 2, S: int = 64) -> np.ndarray:
     rng = np.random.default_rng(seed)
     t = np.rint(rng.lognormal(mean=math.log(512.0), sigma=1.0, size=S))
     return np.clip(t, 16, 2048).astype(np.int64)
 
 
-def config2(**kw) -> DecodeStep:
+def mha13b_f16(**kw) -> DecodeStep:
     """13B-shape fp16 MHA: 64 sequences, 40 heads, d=128, B=16, lengths lognormal (median
     512, sigma 1) clipped to [16, 2048], pool 1.2x the blocks needed."""
-    return make_step("mha13b-f16", 2, config2_lengths(), 40, 40, 128, 16, "f16", **kw)
+    return make_step("mha13b-f16", 2, mha13b_lengths(), 40, 40, 128, 16, "f16", **kw)
 
 
-def config3_lengths(seed: int = 3, S: int = 256) -> np.ndarray:
+def gqa_lengths(seed: int = 3, S: int = 256) -> np.ndarray:
     return np.random.default_rng(seed).integers(128, 4096 + 1, size=S)
 
 
-def config3(**kw) -> DecodeStep:
+def gqa_bf16(**kw) -> DecodeStep:
     """GQA bf16: 256 sequences, 64 query heads over 8 KV heads, d=128, B=16, lengths uniform
     in [128, 4096]."""
-    return make_step("gqa-bf16", 3, config3_lengths(), 64, 8, 128, 16, "bf16", **kw)
+    return make_step("gqa-bf16", 3, gqa_lengths(), 64, 8, 128, 16, "bf16", **kw)
 
 
-def config4_lengths(seed: int = 4, S: int = 8) -> np.ndarray:
+def long_lengths(seed: int = 4, S: int = 8) -> np.ndarray:
     return np.random.default_rng(seed).integers(32768, 131072 + 1, size=S)
 
 
-def config4(**kw) -> DecodeStep:
+def long_bf16(**kw) -> DecodeStep:
     """Long-context bf16: 8 sequences, 32 heads, d=128, B=16, lengths uniform in
     [32768, 131072]; the split-K partition-and-merge path."""
-    return make_step("long-bf16", 4, config4_lengths(), 32, 32, 128, 16, "bf16", **kw)
+    return make_step("long-bf16", 4, long_lengths(), 32, 32, 128, 16, "bf16", **kw)
 
 
-def config5(private: bool = False, prompts: int = 16, samples: int = 4, prompt_len: int = 1040,
+def shared_prefix_f16(private: bool = False, prompts: int = 16, samples: int = 4, prompt_len: int = 1040,
             tail_len: int = 256, heads: int = 32, head_dim: int = 128, block_size: int = 32,
             dtype: str = "f16", seed: int = 5, poison: bool = True,
             keep_logical: bool = False) -> DecodeStep:
@@ -463,9 +463,3 @@ def config5(private: bool = False, prompts: int = 16, samples: int = 4, prompt_l
                       logical_blocks=S * per_sample, refcounts=alloc.ref.copy())
     return step
 
-
-CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
-
-
-def make_config(i: int, **kw) -> DecodeStep:
-    return CONFIGS[i](**kw)
