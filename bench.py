@@ -1,7 +1,9 @@
 """Benchmark of the paged decode hot path on one MI355X.
 
-One step = pa_write_kv of every sequence's new token, then pa_decode of the whole batch (all
-partitions and the fused merge), on seeded synthetic inputs already resident in HBM. The
+One step = pa_write_kv of every sequence's new token, then pa_decode of the whole batch (the
+decode kernel, and the merge kernel when a sequence is split), on seeded synthetic inputs
+already resident in HBM. The timed steps replay a captured HIP graph of consecutive steps, as a
+serving loop would (--no-graph times eager launches; the eager rate is reported too). The
 default workload is the 13B-shape fp16 MHA decode batch: 64 sequences, 40 heads, head dim
 128, block size 16, context lengths lognormal (median 512, sigma 1) clipped to [16, 2048],
 blocks scattered over a pool 1.2x the need. Other workloads (--workload) are for profiling.
@@ -399,6 +401,8 @@ def main():
                     help="untimed seconds of steps before the warmup steps (GPU clock ramp)")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches instead of replays of a captured step graph")
     ap.add_argument("--placement", default="random", choices=["random", "contiguous"],
                     help="block placement; 'contiguous' is a diagnostic of what scattering costs")
     args = ap.parse_args()
@@ -480,7 +484,7 @@ def main():
     for i in range(args.warmup):
         one_step(i)
     torch.cuda.synchronize()
-    # Timed region, part 1: K steps (KV write + decode), events around each decode launch.
+    # Diagnostic (untimed for `value`): K eager steps with events around each decode launch.
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -488,8 +492,28 @@ def main():
     for i in range(args.steps):
         one_step(args.warmup + i, events[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    eager_wall = time.perf_counter() - t0
     step_event_us = float(np.mean([a.elapsed_time(b) for a, b in events])) * 1e3
+    # Timed region: exactly K steps. By default a serving loop's step is captured once as a
+    # HIP graph of `ncopy` consecutive steps (one per pool copy) and replayed, which removes
+    # the host launch gaps between the kernels; steps that do not fill a whole graph run eagerly.
+    if args.no_graph:
+        wall = eager_wall
+    else:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(ncopy):
+                one_step(i)
+        graph.replay()  # untimed first replay
+        torch.cuda.synchronize()
+        reps, rest = divmod(args.steps, ncopy)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        for i in range(rest):
+            one_step(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     # Part 2: K decode launches back to back (rotating pool copies) between two events on the
     # launch stream; the average is the decode kernel's launch duration for the roofline (an
     # event right before each launch would also time the dispatch gap after the KV write).
@@ -532,6 +556,8 @@ def main():
             "placement": args.placement,
             "parallelism": "single GPU",
         },
+        "execution": "eager" if args.no_graph else f"HIP graph of {ncopy} steps, replayed",
+        "eager_ms_per_step": round(eager_wall / args.steps * 1e3, 5),
         "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
         "seq_tokens_per_s": round(nb["tokens"] / (wall / args.steps), 1),
         "decode_seq_tokens_per_s": round(nb["tokens"] / dec_s, 1),

@@ -1,0 +1,84 @@
+"""The library's calls under HIP graph capture (torch.cuda.graph on the caller's stream): a
+serving loop can capture one step (copy-on-write, KV write, decode or prefill) and replay it.
+Every replay, with eager work and synchronizations between replays, must give the eager
+result bit for bit, and leave the pool as the eager step does. No call records a memset."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import paged_kv_cache_82_amd as pa
+from gpu_harness import DevPrefill, DevStep, to_host
+from workloads import make_prefill_step, make_step, shared_prefix_f16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu-test] {request.node.name}", flush=True)
+    yield
+
+
+def _bits(t, dt):
+    return to_host(t, dt).view(np.uint8).copy()
+
+
+def _replays_match(run_step, outputs, dt, n=3):
+    """Eager step, then n replays of its captured graph with eager work in between."""
+    run_step()
+    torch.cuda.synchronize()
+    want = [_bits(t, dt) for t in outputs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_step()
+    torch.cuda.synchronize()
+    scratch = torch.randn(1 << 20, device="cuda")
+    for r in range(n):
+        for t in outputs[:1]:
+            t.zero_()
+        scratch.mul_(1.0001).add_(r)  # eager work on the same stream between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [_bits(t, dt) for t in outputs]
+        for a, b in zip(got, want):
+            assert np.array_equal(a, b), f"replay {r} differs from the eager step"
+
+
+@pytest.mark.parametrize("dt,Hq,Hkv,P", [("f16", 8, 8, 0), ("bf16", 16, 2, 0), ("f16", 8, 8, 64)])
+def test_decode_step_graph_replay(dt, Hq, Hkv, P):
+    # MHA (vector kernel), GQA (matrix kernel), and a forced split into 64-token partitions
+    # so that the merge kernel is in the graph too
+    step = make_step("graph", 500, [300, 17, 1200, 1], Hq, Hkv, 128, 16, dt)
+    dev = DevStep(step, partition_tokens=P)
+
+    def run_step():
+        dev.apply_updates()
+        dev.decode()
+
+    _replays_match(run_step, [dev.out, dev.k_cache, dev.v_cache], dt)
+
+
+def test_shared_prefix_step_graph_replay():
+    # copy-on-write pairs, the tail and new-token writes and the decode in one graph
+    step = shared_prefix_f16(prompts=2, samples=3, prompt_len=72, tail_len=20, heads=4)
+    dev = DevStep(step)
+
+    def run_step():
+        dev.apply_updates()
+        dev.decode()
+
+    _replays_match(run_step, [dev.out, dev.k_cache, dev.v_cache], step.dtype)
+
+
+def test_prefill_step_graph_replay():
+    step = make_prefill_step("gprefill", 510, [300, 41, 129], [200, 41, 3], 16, 2, 128, 16,
+                             "bf16")
+    dev = DevPrefill(step)
+
+    def run_step():
+        dev.apply_updates()
+        dev.attend()
+
+    _replays_match(run_step, [dev.out, dev.k_cache, dev.v_cache], step.dtype)

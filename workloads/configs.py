@@ -376,10 +376,11 @@ def long_bf16(**kw) -> DecodeStep:
     return make_step("long-bf16", 4, long_lengths(), 32, 32, 128, 16, "bf16", **kw)
 
 
-def shared_prefix_f16(private: bool = False, prompts: int = 16, samples: int = 4, prompt_len: int = 1040,
-            tail_len: int = 256, heads: int = 32, head_dim: int = 128, block_size: int = 32,
-            dtype: str = "f16", seed: int = 5, poison: bool = True,
-            keep_logical: bool = False) -> DecodeStep:
+def shared_prefix_f16(private: bool = False, prompts: int = 16, samples: int = 4,
+                      prompt_len: int = 1040, tail_len: int = 256, heads: int = 32,
+                      head_dim: int = 128, block_size: int = 32, dtype: str = "f16",
+                      seed: int = 5, poison: bool = True,
+                      keep_logical: bool = False) -> DecodeStep:
     """Shared-prefix sampling: each prompt's blocks are shared by reference count across its
     samples (fork); the first write into the shared, partially filled last prompt block copies
     it (copy-on-write) for every sample but the last holder; then each sample's private tail
