@@ -266,7 +266,24 @@ def run_prefill(args):
     for i in range(args.steps):
         one_step(args.warmup + i)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    eager_wall = time.perf_counter() - t0
+    if args.no_graph:
+        wall = eager_wall
+    else:  # as for decode: a captured graph of ncopy steps, replayed; the rest eagerly
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(ncopy):
+                one_step(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        reps, rest = divmod(args.steps, ncopy)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        for i in range(rest):
+            one_step(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(args.steps):
@@ -294,6 +311,8 @@ def run_prefill(args):
             "max_context_len": maxT, "pool_copies": ncopy, "parallelism": "single GPU",
         },
         "query_tokens_per_s": round(n_new / (wall / args.steps), 1),
+        "execution": "eager" if args.no_graph else f"HIP graph of {ncopy} steps, replayed",
+        "eager_ms_per_step": round(eager_wall / args.steps * 1e3, 5),
         "roofline": {
             "kernel": "pa_prefill: prefill_mfma_kernel",
             "bound": "mfma",

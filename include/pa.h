@@ -1,5 +1,7 @@
 /*
- * pa.h — C ABI of libpa: paged KV-cache decode attention for AMD MI355X (gfx950).
+ * pa.h — C ABI of libpa: paged KV-cache attention for AMD MI355X (gfx950): slot-mapped KV
+ * writes, decode and causal multi-query (prefill) attention through block tables, and
+ * whole-block copies (copy-on-write) and moves between pools (swap).
  *
  * Sources cited in this header (the method is defined there; nothing else is):
  *   [PA-summary]  azimuth.plus, "Efficient Memory Management for Large Language Model Serving
@@ -46,7 +48,8 @@
  * PA_ERR_WORKSPACE for a workspace smaller than pa_decode_workspace_size; PA_ERR_HIP when the
  * HIP runtime reports an error at launch.
  *
- * Supported shapes: dtype f32, f16, bf16; head_dim 64 or 128; block_size 8, 16 or 32.
+ * Supported shapes: dtype f32, f16, bf16 (pa_prefill: f16, bf16); head_dim 64 or 128;
+ * block_size 8, 16 or 32.
  */
 #ifndef PA_H
 #define PA_H
