@@ -115,6 +115,7 @@ def test_decode_argument_checks(lib, monkeypatch):
         return f(*a)
 
     assert call(S=0) == PA_OK
+    assert call(S=65536) == PA_ERR_INVALID_ARG  # beyond the grid's sequence dimension
     assert call(q=None) == PA_ERR_INVALID_ARG
     assert call(Hq=8, Hkv=3) == PA_ERR_INVALID_ARG
     assert call(d=96) == PA_ERR_UNSUPPORTED

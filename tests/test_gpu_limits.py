@@ -1,0 +1,118 @@
+"""Decode and prefill at the size limits of their launches, through the C ABI, against the CPU
+oracle: the largest sequence count a decode grid takes (65,535), the merge of 256 partitions
+per (sequence, head) on both decode kernels, and a prefill launch of more than 100,000
+workgroups. Inputs are drawn directly (seeded N(0,1)); every pool slot that holds no token is
+NaN, so a read outside a sequence's tokens would show."""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import paged_kv_cache_82_amd as pa
+from gpu_harness import TORCH_DT, assert_attention_close, to_dev, to_host
+from workloads import nan_value, to_storage
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu-test] {request.node.name}", flush=True)
+    yield
+
+
+def _paged(rng, lens, Hkv, d, B, dt, spare=5):
+    """Pools holding each sequence's tokens in randomly placed blocks (NaN elsewhere) and the
+    padded block tables."""
+    lens = np.asarray(lens, np.int64)
+    need = (lens + B - 1) // B
+    N = int(need.sum()) + spare
+    kc = to_storage(rng.standard_normal((N, Hkv, B, d), dtype=np.float32), dt)
+    vc = to_storage(rng.standard_normal((N, Hkv, B, d), dtype=np.float32), dt)
+    perm = rng.permutation(N).astype(np.int32)
+    M = max(int(need.max()), 1)
+    tables = np.full((len(lens), M), -1, np.int32)
+    used = np.zeros(N, bool)
+    pos = 0
+    for s, nb in enumerate(need):
+        tables[s, :nb] = perm[pos:pos + nb]
+        used[perm[pos:pos + nb]] = True
+        tail = int(lens[s]) - (int(nb) - 1) * B  # tokens in the last block
+        if nb and tail < B:
+            kc[perm[pos + nb - 1], :, tail:] = nan_value(dt)
+            vc[perm[pos + nb - 1], :, tail:] = nan_value(dt)
+        pos += nb
+    kc[~used] = nan_value(dt)
+    vc[~used] = nan_value(dt)
+    return kc, vc, tables
+
+
+def _decode(q, kc, vc, tables, lens, dt, P=0):
+    S, Hq, d = q.shape
+    N, Hkv, B, _ = kc.shape
+    maxT = int(lens.max())
+    ws_bytes = pa.pa_decode_workspace_size(S, Hq, Hkv, d, B, maxT, P, TORCH_DT[dt])
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    dq = to_dev(q, dt)
+    out = torch.empty_like(dq)
+    pa.pa_decode(out, dq, to_dev(kc, dt), to_dev(vc, dt), to_dev(tables), to_dev(lens),
+                 1 / math.sqrt(d), maxT, ws, P)
+    torch.cuda.synchronize()
+    return to_host(out, dt)
+
+
+def test_decode_largest_sequence_count():
+    rng = np.random.default_rng(1000)
+    S, H, d, B, dt = 65535, 1, 64, 8, "f16"
+    lens = rng.integers(0, 25, size=S).astype(np.int32)
+    kc, vc, tables = _paged(rng, lens, H, d, B, dt)
+    q = to_storage(rng.standard_normal((S, H, d), dtype=np.float32), dt)
+    got = _decode(q, kc, vc, tables, lens, dt)
+    ref = oracle.decode(q, kc, vc, tables, lens, np.float32(1 / math.sqrt(d)), dt)
+    assert_attention_close(got, ref, dt, "65535 sequences")
+    assert not got[lens == 0].view(np.uint16).any()  # empty sequences give exact zeros
+
+
+@pytest.mark.parametrize("Hq,Hkv,dt", [(8, 8, "f16"), (16, 2, "bf16")])
+def test_decode_merges_256_partitions(Hq, Hkv, dt):
+    # 32-token partitions over contexts up to 8192 tokens: 256 partial states per (sequence,
+    # head), merged by the second kernel (vector kernel for single-head groups, matrix kernel
+    # for grouped heads)
+    rng = np.random.default_rng(1001 + Hkv)
+    d, B = 128, 16
+    lens = np.array([8192, 5001, 33, 1], np.int32)
+    kc, vc, tables = _paged(rng, lens, Hkv, d, B, dt)
+    q = to_storage(rng.standard_normal((len(lens), Hq, d), dtype=np.float32), dt)
+    got = _decode(q, kc, vc, tables, lens, dt, P=32)
+    ref = oracle.decode(q, kc, vc, tables, lens, np.float32(1 / math.sqrt(d)), dt)
+    assert_attention_close(got, ref, dt, "256 partitions")
+
+
+def test_prefill_launch_of_100k_workgroups():
+    # 1,000 sequences x 8 KV heads x 13 row tiles (the longest chunk, 1,600 new tokens, sizes
+    # the grid) = 104,000 workgroups; most sequences bring 10 tokens, so most workgroups find
+    # no rows and leave at once. The oracle checks the long chunk and a sample of the others.
+    rng = np.random.default_rng(1002)
+    S, H, d, B, dt = 1000, 8, 64, 16, "bf16"
+    n = np.full(S, 10, np.int64)
+    n[0] = 1600
+    lens = (n + rng.integers(0, 200, size=S)).astype(np.int32)
+    kc, vc, tables = _paged(rng, lens, H, d, B, dt)
+    qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    q = to_storage(rng.standard_normal((int(qs[-1]), H, d), dtype=np.float32), dt)
+    dq = to_dev(q, dt)
+    out = torch.empty_like(dq)
+    pa.pa_prefill(out, dq, to_dev(kc, dt), to_dev(vc, dt), to_dev(tables), to_dev(lens),
+                  to_dev(qs), 1 / math.sqrt(d), int(n.max()), int(lens.max()))
+    torch.cuda.synchronize()
+    got = to_host(out, dt)
+    seqs = np.unique(np.concatenate([[0, S - 1], rng.integers(1, S, size=30)]))
+    rows = np.concatenate([np.arange(qs[s], qs[s + 1]) for s in seqs])
+    sub_qs = np.concatenate([[0], np.cumsum(n[seqs])]).astype(np.int32)
+    ref = oracle.prefill(np.ascontiguousarray(q[rows]), kc, vc,
+                         np.ascontiguousarray(tables[seqs]), np.ascontiguousarray(lens[seqs]),
+                         sub_qs, np.float32(1 / math.sqrt(d)), dt)
+    assert_attention_close(got[rows], ref, dt, "100k workgroups")
