@@ -14,9 +14,9 @@
 // (pa_mfma.h): S^T = K Q^T with tokens on rows and query rows on columns, then
 // O^T += V^T P^T. Work decomposition (chosen for MI355X, not on the pages):
 //   - query rows are (query token, grouped head) pairs, head fastest, so one KV tile feeds all
-//     query heads of its group; a workgroup of NW waves covers NW * NCT * 16 consecutive rows
-//     as 16-row column tiles dealt round-robin to the waves (so every wave reaches about the
-//     same causal depth);
+//     query heads of its group; a workgroup of NW waves covers NW * NCT * 16 consecutive rows,
+//     each wave NCT adjacent 16-row column tiles, so that a wave's rows span few positions and
+//     few of its stages need the causal mask;
 //   - the workgroup walks its context in 32-token stages: each wave loads 8 rows of the
 //     stage's K and V (rows of one block, found through the block table) straight from HBM
 //     into LDS, with two stages in flight while one is consumed; one barrier per stage;
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
   const uint32_t qflip = a.scale_log2 < 0.0f ? 0x80008000u : 0u;
   const uint32_t qkeep = a.scale_log2 == 0.0f ? 0u : 0xffffffffu;
 
-  // Column tiles of this wave: tile c is workgroup column tile w + NW*c.
+  // Column tiles of this wave: tile c is workgroup column tile NCT*w + c.
   int pos[NCT];                // position of this lane's query row; -1 past the chunk
   int t_lo[NCT];               // first position of the tile's rows (uniform); -1 if empty
   vec8 qop[NCT][KC];
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
   int t_lo_w = 0x7fffffff;     // first position any tile of this wave starts at
 #pragma unroll
   for (int c = 0; c < NCT; ++c) {
-    const int Rt = W0 + 16 * (w + NW * c);  // first row of the tile
+    const int Rt = W0 + 16 * (NCT * w + c);  // first row of the tile
     const int R = Rt + hh;
     const bool valid = R < nrows;
     const int i = valid ? R / g : 0;
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     if (pos[c] < 0) continue;
-    const int R = W0 + 16 * (w + NW * c) + hh;
+    const int R = W0 + 16 * (NCT * w + c) + hh;
     const int i = R / g;
     const int head = kvh * g + R % g;
     char* orow = (char*)a.out + ((int64_t)(q0 + i) * Hq + head) * D * E;
