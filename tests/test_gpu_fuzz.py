@@ -1,0 +1,84 @@
+"""Seeded random sweep of decode and prefill shapes against the CPU oracle, through the C ABI:
+dtype, head size, block size, KV heads and group size, batch, context and chunk lengths
+(empty sequences and chunks included), forced split-K partitions and random scales (negative
+ones included). Each case prints its parameters before it runs. Tolerances as everywhere:
+max-abs 1e-5 for fp32, |gpu - ref| <= 2e-2 + 1e-2 |ref| for fp16/bf16; the KV write
+bit-exact."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+from gpu_harness import DevPrefill, DevStep, assert_attention_close, to_host
+from workloads import make_prefill_step, make_step
+
+pytestmark = pytest.mark.gpu
+
+DECODE_CASES = 24
+PREFILL_CASES = 16
+
+
+def _bits(a):
+    return a.view(np.uint8)
+
+
+def _decode_case(i):
+    rng = np.random.default_rng(7000 + i)
+    dt = ["f32", "f16", "bf16"][rng.integers(3)]
+    d = int(rng.choice([64, 128]))
+    B = int(rng.choice([8, 16, 32]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 4, 8, 16]))
+    S = int(rng.integers(1, 13))
+    lens = [int(x) for x in rng.choice([0, 1, 2, 15, 16, 17, 100, 333, 1024, 2500], size=S)]
+    lens[0] = max(lens[0], 1)
+    cap = 64 * 4 * B if (dt == "f32" or g == 1) else 8192
+    P = int(rng.choice([0, 0, 32, 64, 96, 512]))
+    P = P if P <= cap else 0
+    scale = float(rng.choice([1 / np.sqrt(d), 1 / np.sqrt(d), 0.5, -0.07]))
+    return dict(dt=dt, d=d, B=B, Hkv=Hkv, Hq=Hkv * g, lens=lens, P=P, scale=scale)
+
+
+def _prefill_case(i):
+    rng = np.random.default_rng(8000 + i)
+    dt = ["f16", "bf16"][rng.integers(2)]
+    d = int(rng.choice([64, 128]))
+    B = int(rng.choice([8, 16, 32]))
+    Hkv = int(rng.choice([1, 2]))
+    g = int(rng.choice([1, 2, 4, 8, 16]))
+    S = int(rng.integers(1, 7))
+    n = [int(x) for x in rng.choice([0, 1, 7, 33, 128, 300], size=S)]
+    T = [ni + int(rng.choice([0, 0, 5, 64, 700])) for ni in n]
+    T[0] = max(T[0], 1)
+    n[0] = max(min(n[0], T[0]), 1)
+    scale = float(rng.choice([1 / np.sqrt(d), 1 / np.sqrt(d), 0.5, -0.07]))
+    return dict(dt=dt, d=d, B=B, Hkv=Hkv, Hq=Hkv * g, T=T, n=n, scale=scale)
+
+
+@pytest.mark.parametrize("i", range(DECODE_CASES))
+def test_decode_random_shapes(i):
+    c = _decode_case(i)
+    print(f"\n[gpu-test] decode fuzz {i}: {c}", flush=True)
+    step = make_step(f"fz{i}", 7000 + i, c["lens"], c["Hq"], c["Hkv"], c["d"], c["B"], c["dt"],
+                     scale=c["scale"])
+    ref, kc, vc = oracle.run_step(step)
+    dev = DevStep(step, c["P"])
+    got = dev.run()
+    assert np.array_equal(_bits(to_host(dev.k_cache, step.dtype)), _bits(kc))
+    assert np.array_equal(_bits(to_host(dev.v_cache, step.dtype)), _bits(vc))
+    assert_attention_close(got, ref, step.dtype, f"decode fuzz {i}")
+
+
+@pytest.mark.parametrize("i", range(PREFILL_CASES))
+def test_prefill_random_shapes(i):
+    c = _prefill_case(i)
+    print(f"\n[gpu-test] prefill fuzz {i}: {c}", flush=True)
+    step = make_prefill_step(f"pfz{i}", 8000 + i, c["T"], c["n"], c["Hq"], c["Hkv"], c["d"],
+                             c["B"], c["dt"], scale=c["scale"])
+    ref, kc, vc = oracle.run_prefill_step(step)
+    dev = DevPrefill(step)
+    got = dev.run()
+    assert np.array_equal(_bits(to_host(dev.k_cache, step.dtype)), _bits(kc))
+    assert np.array_equal(_bits(to_host(dev.v_cache, step.dtype)), _bits(vc))
+    assert_attention_close(got, ref, step.dtype, f"prefill fuzz {i}")
