@@ -51,6 +51,9 @@ WORKLOADS = {
     "copy": (None, "plain copy calibration: pa_copy_blocks of 4096 blocks of 256 KiB"),
     "sharing": (None, "KV memory accounting on the host block manager (no GPU): prompt sharing "
                 "in parallel sampling and beam search, paged vs contiguous waste"),
+    "kvwrite": (None, "pa_write_kv of an 8192-token chunk (40 KV heads, d=128, fp16) into "
+                "scattered slots"),
+    "cow": (None, "pa_copy_blocks of 4096 random block pairs (40 heads, B=16, d=128, fp16)"),
     "swap": (None, "preemption swap: pa_swap_blocks of 2048 blocks of 160 KiB (40 heads, B=16, "
              "d=128, fp16) device -> pinned host and back"),
 }
@@ -355,6 +358,65 @@ def run_copy_calibration(args):
                       "bytes_written_per_launch": nbytes // 2, "GB_per_s": nbytes / dt / 1e9}))
 
 
+def run_kv_bandwidth(args):
+    """Secondary measurements of the indexing kernels at a serving shape (40 KV heads, d=128,
+    B=16, fp16; a pool of 16,384 blocks = 2.5 GiB per tensor):
+      kvwrite: pa_write_kv of one 8,192-token chunk (the 13B-shape prefill chunk) to slots
+               scattered over the pool by a seeded permutation of its blocks;
+      cow:     pa_copy_blocks of 4,096 (src, dst) pairs drawn from a seeded permutation.
+    Bytes are the algorithmic ones (read + written); time is the HIP-event average of K
+    back-to-back launches on the launch stream."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_82_amd as pa
+
+    dev = torch.device("cuda")
+    N, H, B, d = 16384, 40, 16, 128
+    k = torch.zeros((N, H, B, d), dtype=torch.float16, device=dev)
+    v = torch.zeros_like(k)
+    rng = np.random.default_rng(11)
+    if args.workload == "kvwrite":
+        n = 8192
+        blocks = rng.permutation(N)[: n // B]
+        slots = (blocks[:, None] * B + np.arange(B)[None, :]).reshape(-1).astype(np.int32)
+        kn = torch.randn((n, H, d), device=dev).half()
+        vn = torch.randn_like(kn)
+        sm = torch.from_numpy(slots).to(dev)
+        launch = lambda: pa.pa_write_kv(k, v, kn, vn, sm)  # noqa: E731
+        nbytes = 2 * (2 * n * H * d * 2) + 4 * n
+        what = "pa_write_kv: 8192 tokens x 40 KV heads x d=128 fp16 into scattered slots"
+    else:
+        n = 4096
+        perm = rng.permutation(N)
+        pairs = torch.from_numpy(np.stack([perm[:n], perm[n:2 * n]], 1).astype(np.int32)).to(dev)
+        launch = lambda: pa.pa_copy_blocks(k, v, pairs)  # noqa: E731
+        nbytes = 2 * (2 * n * H * B * d * 2) + 8 * n
+        what = "pa_copy_blocks: 4096 random (src, dst) pairs of 40x16x128 fp16 blocks, K and V"
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        launch()
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / args.steps
+    gbs = nbytes / sec / 1e9
+    print(json.dumps({
+        "metric": f"{args.workload} bandwidth: algorithmic bytes read + written per second",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": what, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_us": round(sec * 1e6, 3)},
+    }))
+
+
 def run_swap(args):
     """Swap-out (device -> pinned host) and swap-in (host -> device) rates of pa_swap_blocks.
     The bound is the host link, not HBM."""
@@ -448,6 +510,8 @@ def main():
         return run_copy_calibration(args)
     if args.workload == "swap":
         return run_swap(args)
+    if args.workload in ("kvwrite", "cow"):
+        return run_kv_bandwidth(args)
     if args.workload.startswith("prefill"):
         return run_prefill(args)
 
