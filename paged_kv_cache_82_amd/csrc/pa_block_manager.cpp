@@ -106,15 +106,15 @@ pa_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
   if (!bm || parent == child) return PA_ERR_INVALID_ARG;
   const pa_bm::Seq* p = bm->find(parent);
   if (!p || bm->find(child)) return PA_ERR_INVALID_ARG;
-  pa_bm::Seq c;
   try {
+    pa_bm::Seq c;
     c.table = p->table;
     c.len = p->len;
-    for (int32_t b : c.table) ++bm->ref[b];
-    bm->seqs.emplace(child, std::move(c));
+    bm->seqs.emplace(child, std::move(c));  // may throw: nothing is changed before it
   } catch (...) {
     return PA_ERR_INVALID_ARG;
   }
+  for (int32_t b : bm->find(child)->table) ++bm->ref[b];
   return PA_OK;
 }
 
@@ -181,21 +181,21 @@ pa_status pa_bm_move(pa_bm* from, pa_bm* to, int64_t seq, int32_t* pairs, int ma
   const int64_t n = (int64_t)s->table.size();
   if (n > max_pairs || (n > 0 && !pairs)) return PA_ERR_INVALID_ARG;
   if (n > (int64_t)to->free_list.size()) return PA_ERR_NO_BLOCKS;
-  pa_bm::Seq moved;
-  try {
-    moved.table.reserve((size_t)n);
-    to->seqs.reserve(to->seqs.size() + 1);
+  pa_bm::Seq* moved = nullptr;
+  try {  // the only steps that may throw come first, before anything is changed
+    pa_bm::Seq fresh;
+    fresh.table.reserve((size_t)n);
+    moved = &to->seqs.emplace(seq, std::move(fresh)).first->second;
   } catch (...) {
     return PA_ERR_INVALID_ARG;
   }
-  moved.len = s->len;
+  moved->len = s->len;
   for (int64_t j = 0; j < n; ++j) {
     const int32_t dst = to->take();
     pairs[2 * j] = s->table[(size_t)j];
     pairs[2 * j + 1] = dst;
-    moved.table.push_back(dst);
+    moved->table.push_back(dst);  // capacity reserved: no allocation
   }
-  to->seqs.emplace(seq, std::move(moved));
   *n_pairs = (int)n;
   return pa_bm_release(from, seq);
 }
