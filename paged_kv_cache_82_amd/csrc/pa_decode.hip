@@ -227,16 +227,21 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
   // Per-lane byte offset inside a (block, head) tile: loop-invariant and 32-bit, so loads take
   // the form (wave-uniform 64-bit tile base) + (per-lane 32-bit offset).
   const uint32_t lane_off = (uint32_t)(r * row_bytes + c * 16);
+  // Fetch k >= nb is a prefetch past the wave's last block, never consumed. It reads the pool's
+  // first tile, which such prefetches of every workgroup share, so it stays cached; the wave's
+  // own last block would not be, since the streaming loads evict it first.
   auto fetch = [&](int k, u32x4* kr, u32x4* vr) {
-    const int32_t id = __builtin_amdgcn_readlane(my_id, k);
+    const bool live = k < nb;
+    const int32_t id = __builtin_amdgcn_readlane(my_id, live ? k : 0);
     const int64_t tile =
-        (clamp_block(id, a.num_blocks) * a.num_kv_heads + kvh) * (int64_t)(BS * row_bytes);
+        live ? (clamp_block(id, a.num_blocks) * a.num_kv_heads + kvh) * (int64_t)(BS * row_bytes)
+             : 0;
     const char* kt = kbase + tile;
     const char* vt = vbase + tile;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      kr[i] = load16(kt + lane_off + i * TPI * row_bytes);
-      vr[i] = load16(vt + lane_off + i * TPI * row_bytes);
+      kr[i] = load16_stream(kt + lane_off + i * TPI * row_bytes);
+      vr[i] = load16_stream(vt + lane_off + i * TPI * row_bytes);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the consume that follows
   };
@@ -248,20 +253,18 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
       valu_block<dt, D, BS, NW, true>(qf, kr, vr, tok0, t1, r, m, l, o);
   };
   // A ring of NBUF register buffers: the loads of the next NBUF-1 blocks are in flight while
-  // one block is consumed. Prefetches are unconditional (past the end they re-read the final
-  // block, a cache hit) so that the compiler's wait before each consume only covers the
+  // one block is consumed. Prefetches are unconditional (past the end they read the shared
+  // first tile, a cache hit) so that the compiler's wait before each consume only covers the
   // oldest buffer.
   if (nb > 0) {
     u32x4 kbuf[NBUF][NL], vbuf[NBUF][NL];
 #pragma unroll
-    for (int u = 0; u + 1 < NBUF; ++u) fetch(u < nb ? u : nb - 1, kbuf[u], vbuf[u]);
+    for (int u = 0; u + 1 < NBUF; ++u) fetch(u, kbuf[u], vbuf[u]);
     for (int k = 0; k < nb; k += NBUF) {
 #pragma unroll
       for (int u = 0; u < NBUF; ++u) {
         if (k + u >= nb) break;
-        const int ahead = k + u + NBUF - 1;
-        fetch(ahead < nb ? ahead : nb - 1, kbuf[(u + NBUF - 1) % NBUF],
-              vbuf[(u + NBUF - 1) % NBUF]);
+        fetch(k + u + NBUF - 1, kbuf[(u + NBUF - 1) % NBUF], vbuf[(u + NBUF - 1) % NBUF]);
         consume(k + u, kbuf[u], vbuf[u]);
       }
     }
@@ -496,7 +499,11 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
     m = mn;
   };
 
-  if (ns > 0) {  // ring of NBUF register buffers, unconditional prefetch (see the VALU kernel)
+  // Ring of NBUF register buffers with unconditional prefetch, as in the VALU kernel; past the
+  // end it re-reads the wave's last step, a cache hit for these ordinary loads. (Streaming
+  // loads were measured slower here: a K load instruction covers only half of each 128-byte
+  // line, and the other half comes from a second instruction.)
+  if (ns > 0) {
     StepRegs<D, KC> rb[NBUF];
 #pragma unroll
     for (int u = 0; u + 1 < NBUF; ++u) fetch(u < ns ? u : ns - 1, rb[u]);

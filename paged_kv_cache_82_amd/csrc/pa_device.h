@@ -90,6 +90,12 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
 __device__ __forceinline__ u32x2 load8(const void* p) {
   return *reinterpret_cast<const u32x2*>(p);
 }
+// Non-temporal 16-byte load, for K/V tiles a launch reads once: the caches evict these lines
+// first, which lets a stream of whole 128-byte lines run closer to the HBM rate. Do not re-read
+// such a line later in the same launch and expect a cache hit.
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 // ---- cross-lane reductions ----------------------------------------------------------------
 
