@@ -396,17 +396,25 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
   const uint32_t koff = (uint32_t)((hh % BS) * RB + 8 * gq * E);
   const uint32_t voff = (uint32_t)(((4 * gq) % BS) * RB + MT * hh * E);
   const int64_t tile_bytes = (int64_t)BS * RB;
+  // Loads: K ordinary, V non-temporal. A V load instruction covers whole token rows (whole
+  // 128-byte lines); a K load instruction covers 64 bytes of each of 16 rows, and the other half
+  // of each line comes from the next instruction, so K is kept cacheable (measured on MI355X:
+  // streaming K as well was 8% slower, streaming V alone 6% faster). Fetch k >= ns is a
+  // prefetch past the wave's last step, never consumed: it reads the pool's first tile, shared
+  // by such prefetches of every workgroup and so cached, not the wave's own streamed last step.
   auto fetch = [&](int k, StepRegs<D, KC>& R) {
     const char* kt[NBS];
     const char* vt[NBS];
+    const bool live = k < ns;
+    const int kq = live ? k : 0;
     const int jfirst = (st0 + w + k * NW) * (32 / BS);
 #pragma unroll
     for (int b = 0; b < NBS; ++b) {
       // a block past this partition's last one holds no valid token: read the step's first
       // block instead (its tokens are masked), never an id beyond the sequence's blocks
-      const int32_t id = (jfirst + b <= jlast) ? __builtin_amdgcn_readlane(my_id[b], k)
-                                               : __builtin_amdgcn_readlane(my_id[0], k);
-      const int64_t tile = (clamp_block(id, a.num_blocks) * Hkv + kvh) * tile_bytes;
+      const int32_t id = (jfirst + b <= jlast) ? __builtin_amdgcn_readlane(my_id[b], kq)
+                                               : __builtin_amdgcn_readlane(my_id[0], kq);
+      const int64_t tile = live ? (clamp_block(id, a.num_blocks) * Hkv + kvh) * tile_bytes : 0;
       kt[b] = kbase + tile;
       vt[b] = vbase + tile;
     }
@@ -431,7 +439,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
         } else {  // token 16u + 4gq + i sits in block 2u + gq/2 at row 4*(gq&1) + i
           rp = vt[2 * u + (gq >> 1)] + voff + i * RB;
         }
-        R.v[u][i] = VF::load(rp);
+        R.v[u][i] = VF::load_stream(rp);
       }
     __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the consume that follows
   };
@@ -499,20 +507,15 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
     m = mn;
   };
 
-  // Ring of NBUF register buffers with unconditional prefetch, as in the VALU kernel; past the
-  // end it re-reads the wave's last step, a cache hit for these ordinary loads. (Streaming
-  // loads were measured slower here: a K load instruction covers only half of each 128-byte
-  // line, and the other half comes from a second instruction.)
-  if (ns > 0) {
+  if (ns > 0) {  // ring of NBUF register buffers, unconditional prefetch (see the VALU kernel)
     StepRegs<D, KC> rb[NBUF];
 #pragma unroll
-    for (int u = 0; u + 1 < NBUF; ++u) fetch(u < ns ? u : ns - 1, rb[u]);
+    for (int u = 0; u + 1 < NBUF; ++u) fetch(u, rb[u]);
     for (int k = 0; k < ns; k += NBUF) {
 #pragma unroll
       for (int u = 0; u < NBUF; ++u) {
         if (k + u >= ns) break;
-        const int ahead = k + u + NBUF - 1;
-        fetch(ahead < ns ? ahead : ns - 1, rb[(u + NBUF - 1) % NBUF]);
+        fetch(k + u + NBUF - 1, rb[(u + NBUF - 1) % NBUF]);
         consume(k + u, rb[u]);
       }
     }

@@ -96,6 +96,9 @@ __device__ __forceinline__ u32x2 load8(const void* p) {
 __device__ __forceinline__ u32x4 load16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
+__device__ __forceinline__ u32x2 load8_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
 
 // ---- cross-lane reductions ----------------------------------------------------------------
 

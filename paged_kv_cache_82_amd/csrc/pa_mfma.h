@@ -43,12 +43,14 @@ struct VFrag<128> {
   using T = u32x4;
   static constexpr int words = 4;
   static __device__ __forceinline__ T load(const char* p) { return load16(p); }
+  static __device__ __forceinline__ T load_stream(const char* p) { return load16_stream(p); }
 };
 template <>
 struct VFrag<64> {
   using T = u32x2;
   static constexpr int words = 2;
   static __device__ __forceinline__ T load(const char* p) { return load8(p); }
+  static __device__ __forceinline__ T load_stream(const char* p) { return load8_stream(p); }
 };
 
 // 16-bit element `e` of a V fragment, as raw bits in the low half.
