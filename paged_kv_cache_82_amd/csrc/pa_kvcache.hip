@@ -41,6 +41,10 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
 // grid = (chunk groups, n_pairs, 2 for K|V); each thread copies kUnroll chunks spaced a
 // workgroup apart, so a workgroup covers kUnroll * 256 * 16 bytes of one block. Source and
 // destination pools may be the same (copy-on-write) or different (swap to/from host memory).
+// Loads and stores are non-temporal: each byte is moved once, and whole 128-byte lines are
+// read and written per instruction. Measured on MI355X: a contiguous 2 GiB copy 5.73 -> 6.27
+// TB/s, random block pairs 4.98 -> 5.08 TB/s. (The KV write, whose rows land in scattered
+// slots, was 5% slower with the same hints and keeps ordinary accesses.)
 constexpr int kCopyUnroll = 4;
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(
@@ -59,12 +63,12 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(
 #pragma unroll
   for (int u = 0; u < kCopyUnroll; ++u) {
     const int64_t c = first + u * 256;
-    if (c < chunks_per_block) tmp[u] = from[c];
+    if (c < chunks_per_block) tmp[u] = __builtin_nontemporal_load(from + c);
   }
 #pragma unroll
   for (int u = 0; u < kCopyUnroll; ++u) {
     const int64_t c = first + u * 256;
-    if (c < chunks_per_block) to[c] = tmp[u];
+    if (c < chunks_per_block) __builtin_nontemporal_store(tmp[u], to + c);
   }
 }
 
