@@ -385,8 +385,6 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
 
   // This wave takes steps st0 + w + k*NW, k < ns; lane k holds the NBS physical ids of step k.
   const int ns = (st1 - st0 - w + NW - 1) / NW;
-  const char* kbase = (const char*)a.k_cache;
-  const char* vbase = (const char*)a.v_cache;
   const int64_t Hkv = a.num_kv_heads;
 
   // Loop-invariant per-lane byte offsets inside a (block, head) tile. Token tk of a step lives
@@ -396,51 +394,74 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
   const uint32_t koff = (uint32_t)((hh % BS) * RB + 8 * gq * E);
   const uint32_t voff = (uint32_t)(((4 * gq) % BS) * RB + MT * hh * E);
   const int64_t tile_bytes = (int64_t)BS * RB;
+  // Tile (block p, head kvh) starts at p * blk_stride + kvh * tile_bytes in each pool; the head
+  // offset is folded into the bases once.
+  const int64_t blk_stride = Hkv * tile_bytes;
+  const char* kbase = (const char*)a.k_cache + kvh * tile_bytes;
+  const char* vbase = (const char*)a.v_cache + kvh * tile_bytes;
+  const int id_max = last_block_id(a.num_blocks);
   // Loads: K ordinary, V non-temporal. A V load instruction covers whole token rows (whole
   // 128-byte lines); a K load instruction covers 64 bytes of each of 16 rows, and the other half
   // of each line comes from the next instruction, so K is kept cacheable (measured on MI355X:
   // streaming K as well was 8% slower, streaming V alone 6% faster). Fetch k >= ns is a
-  // prefetch past the wave's last step, never consumed: it reads the pool's first tile, shared
-  // by such prefetches of every workgroup and so cached, not the wave's own streamed last step.
+  // prefetch past the wave's last step, never consumed.
   auto fetch = [&](int k, StepRegs<D, KC>& R) {
-    const char* kt[NBS];
-    const char* vt[NBS];
     const bool live = k < ns;
     const int kq = live ? k : 0;
     const int jfirst = (st0 + w + k * NW) * (32 / BS);
+    if constexpr (BS >= 16) {
+      // Every load instruction reads within one block: it goes through buffer resources that
+      // span the block's K and V tiles. A block past this partition's last one (no valid token)
+      // and every block of a fetch past the wave's last step get resources spanning no bytes:
+      // those loads return 0 and read nothing.
+      __amdgpu_buffer_rsrc_t kr[NBS], vr[NBS];
 #pragma unroll
-    for (int b = 0; b < NBS; ++b) {
-      // a block past this partition's last one holds no valid token: read the step's first
-      // block instead (its tokens are masked), never an id beyond the sequence's blocks
-      const int32_t id = (jfirst + b <= jlast) ? __builtin_amdgcn_readlane(my_id[b], kq)
-                                               : __builtin_amdgcn_readlane(my_id[0], kq);
-      const int64_t tile = live ? (clamp_block(id, a.num_blocks) * Hkv + kvh) * tile_bytes : 0;
-      kt[b] = kbase + tile;
-      vt[b] = vbase + tile;
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const char* rp;
-      if constexpr (BS >= 16) {
-        rp = kt[(16 * u) / BS] + koff + ((16 * u) % BS) * RB;
-      } else {  // BS == 8: lanes hh < 8 and hh >= 8 read different blocks
-        rp = kt[2 * u + (hh >> 3)] + koff;
+      for (int b = 0; b < NBS; ++b) {
+        const int id = clamp_id(__builtin_amdgcn_readlane(my_id[b], kq), id_max);
+        const int64_t tile = (int64_t)id * blk_stride;
+        const int bytes = (live && jfirst + b <= jlast) ? (int)tile_bytes : 0;
+        kr[b] = tile_rsrc(kbase + tile, bytes);
+        vr[b] = tile_rsrc(vbase + tile, bytes);
       }
 #pragma unroll
-      for (int kk = 0; kk < KC; ++kk) R.k[u][kk] = load16(rp + 32 * kk * E);
-    }
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+        for (int kk = 0; kk < KC; ++kk)
+          R.k[u][kk] = load16_tile(kr[(16 * u) / BS], koff + ((16 * u) % BS) * RB + 32 * kk * E);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const char* rp;
-        if constexpr (BS >= 16) {
-          rp = vt[(16 * u) / BS] + voff + ((16 * u) % BS + i) * RB;
-        } else {  // token 16u + 4gq + i sits in block 2u + gq/2 at row 4*(gq&1) + i
-          rp = vt[2 * u + (gq >> 1)] + voff + i * RB;
-        }
-        R.v[u][i] = VF::load_stream(rp);
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          R.v[u][i] = VF::load_tile_stream(vr[(16 * u) / BS], voff + ((16 * u) % BS + i) * RB);
+    } else {
+      // BS == 8: lanes of one load instruction read two different blocks, which one buffer
+      // resource cannot span. Plain loads; a fetch past the wave's last step reads block 0 of
+      // its KV head (shared by every such fetch on that head, so cached), not its own streamed
+      // last step.
+      const char* kt[NBS];
+      const char* vt[NBS];
+#pragma unroll
+      for (int b = 0; b < NBS; ++b) {
+        // a block past this partition's last one holds no valid token: read the step's first
+        // block instead (its tokens are masked), never an id beyond the sequence's blocks
+        const int32_t id = (jfirst + b <= jlast) ? __builtin_amdgcn_readlane(my_id[b], kq)
+                                                 : __builtin_amdgcn_readlane(my_id[0], kq);
+        const int64_t tile = live ? (int64_t)clamp_id(id, id_max) * blk_stride : 0;
+        kt[b] = kbase + tile;
+        vt[b] = vbase + tile;
       }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const char* rp = kt[2 * u + (hh >> 3)] + koff;  // lanes hh < 8 and hh >= 8: two blocks
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) R.k[u][kk] = load16(rp + 32 * kk * E);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)  // token 16u + 4gq + i: block 2u + gq/2, row 4*(gq&1) + i
+          R.v[u][i] = VF::load_stream(vt[2 * u + (gq >> 1)] + voff + i * RB);
+    }
     __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the consume that follows
   };
 
@@ -597,8 +618,14 @@ int max_partition_tokens(DecodePath path, int block_size) {
 template <DT dt, int D, int BS>
 static hipError_t launch_t(DecodePath path, const DecodeArgs& a, hipStream_t stream) {
   const dim3 block(kWaves * 64);
-  const dim3 grid((unsigned)a.max_parts,
-                  (unsigned)decode_units_per_seq(path, a.num_q_heads, a.num_kv_heads),
+  // Grid (partition, unit, sequence), partition fastest. Workgroups are dealt round-robin over
+  // the 8 XCDs in order of their linear id p + gx * (unit + units * s), so an even gx would put
+  // each partition index on a fixed subset of XCDs: with gx = 2 every sequence's first partition
+  // ran on four of them, with gx = 4 on two (measured: 13B-shape batch split at 1024 / 512
+  // tokens, 192 / 246 us instead of 156 us). An odd gx steps every (unit, sequence) through all
+  // eight; the extra partition slot finds no work and returns at once.
+  const unsigned gx = (unsigned)a.max_parts | 1u;
+  const dim3 grid(gx, (unsigned)decode_units_per_seq(path, a.num_q_heads, a.num_kv_heads),
                   (unsigned)a.num_seqs);
   DecodeArgs args_copy = a;
   void* args[] = {&args_copy};

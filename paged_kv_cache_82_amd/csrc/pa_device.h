@@ -76,6 +76,15 @@ __device__ __forceinline__ void store_elem(void* base, int64_t idx, float x) {
 __device__ __forceinline__ int64_t clamp_block(int32_t phys, int64_t n) {
   return phys < 0 ? 0 : (phys >= n ? n - 1 : (int64_t)phys);
 }
+// The same clamp in 32-bit scalar arithmetic, against id_max = last_block_id(num_blocks),
+// computed once per wave.
+__device__ __forceinline__ int last_block_id(int64_t n) {
+  return n - 1 > 0x7fffffff ? 0x7fffffff : (int)(n - 1);
+}
+__device__ __forceinline__ int clamp_id(int32_t phys, int id_max) {
+  const int lo = phys > 0 ? phys : 0;
+  return lo < id_max ? lo : id_max;
+}
 
 // Wave index inside the workgroup as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() {
@@ -98,6 +107,29 @@ __device__ __forceinline__ u32x4 load16_stream(const void* p) {
 }
 __device__ __forceinline__ u32x2 load8_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+
+// ---- tile loads through buffer resources --------------------------------------------------
+// A buffer resource spanning `bytes` bytes from `base` (untyped, stride 0). A load at an offset
+// at or past `bytes` returns 0 and accesses no memory, so a resource with bytes = 0 makes inert
+// loads: they keep their place in the instruction stream and in the wait counters, which lets
+// a register ring prefetch unconditionally without reading anything past its last tile.
+// Word 3 sets DATA_FORMAT = 32 bit (a zero data format reads as 0 on gfx9).
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kCachePolicyNt = 2;  // the instruction's nt bit: lines are evicted first
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 load16_tile(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ u32x4 load16_tile_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCachePolicyNt));
+}
+__device__ __forceinline__ u32x2 load8_tile_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2,
+                            __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kCachePolicyNt));
 }
 
 // ---- cross-lane reductions ----------------------------------------------------------------

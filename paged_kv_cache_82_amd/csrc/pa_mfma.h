@@ -44,6 +44,9 @@ struct VFrag<128> {
   static constexpr int words = 4;
   static __device__ __forceinline__ T load(const char* p) { return load16(p); }
   static __device__ __forceinline__ T load_stream(const char* p) { return load16_stream(p); }
+  static __device__ __forceinline__ T load_tile_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return load16_tile_stream(r, off);
+  }
 };
 template <>
 struct VFrag<64> {
@@ -51,6 +54,9 @@ struct VFrag<64> {
   static constexpr int words = 2;
   static __device__ __forceinline__ T load(const char* p) { return load8(p); }
   static __device__ __forceinline__ T load_stream(const char* p) { return load8_stream(p); }
+  static __device__ __forceinline__ T load_tile_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return load8_tile_stream(r, off);
+  }
 };
 
 // 16-bit element `e` of a V fragment, as raw bits in the low half.
