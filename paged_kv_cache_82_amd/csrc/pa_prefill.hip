@@ -115,6 +115,19 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// Maxima of scores without the NaN-quieting copies the compiler puts in front of fmaxf (two of
+// its six instructions per eight scores): v_max3_f32 takes three at a time. A NaN score can
+// only come from a NaN key or query element and makes that row's output NaN either way.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max2f(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -224,10 +237,12 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
   }
 
   f32x4 oacc[NCT][MT];
-  float m[NCT], lsum[NCT];
+  float m[NCT], lsum[NCT], thr[NCT];
+  const float rcs = 1.0f / cs;
 #pragma unroll
   for (int c = 0; c < NCT; ++c) {
     m[c] = kNegInf;
+    thr[c] = kNegInf;
     lsum[c] = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) oacc[c][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -380,21 +395,24 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
     // Weights are taken against a reference maximum m[c] (scaled, base 2) that is raised only
     // when some score exceeds it by more than kSlack: weights stay below 2^kSlack, and the
     // running sum and output use the same reference, so the normalised result is the same as
-    // with the exact running maximum. The scaled, shifted score cs * s - m is one FMA.
-    float lm[NCT];  // largest scaled score of the lane's 8
+    // with the exact running maximum. The test runs on raw scores against thr[c] =
+    // (m[c] + kSlack) / cs, which changes only when m[c] does. The scaled, shifted score
+    // cs * s - m is one FMA.
+    float lr[NCT];  // largest raw score of the lane's 8
     bool raise = false;
 #pragma unroll
     for (int c = 0; c < NCT; ++c) {
-      float r = sacc[c][0][0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) r = fmaxf(r, sacc[c][e / 4][e % 4]);
-      lm[c] = r * cs;
-      raise = raise || (lm[c] > m[c] + kSlack);
+      const float r0 = max3f(sacc[c][0][0], sacc[c][0][1], sacc[c][0][2]);
+      const float r1 = max3f(r0, sacc[c][0][3], sacc[c][1][0]);
+      const float r2 = max3f(r1, sacc[c][1][1], sacc[c][1][2]);
+      lr[c] = max2f(r2, sacc[c][1][3]);
+      raise = raise || (lr[c] > thr[c]);
     }
     if (__builtin_amdgcn_ballot_w64(raise)) {  // uniform; rare once the maxima settle
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
-        float bm = fmaxf(lm[c], __shfl_xor(lm[c], 16));
+        const float lm = lr[c] * cs;
+        float bm = fmaxf(lm, __shfl_xor(lm, 16));
         bm = fmaxf(bm, __shfl_xor(bm, 32));
         const float mn = fmaxf(m[c], bm);
         const float corr = (m[c] == kNegInf) ? (mn == kNegInf ? 1.0f : 0.0f)
@@ -403,6 +421,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) oacc[c][mt] *= corr;
         m[c] = mn;
+        thr[c] = (mn + kSlack) * rcs;
       }
     }
     vec8 pop[NCT];
