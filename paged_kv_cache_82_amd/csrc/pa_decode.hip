@@ -587,6 +587,14 @@ constexpr int kWaves = 4;          // waves per workgroup
 // Prefetch depth and occupancy, measured on MI355X (13B-shape fp16 MHA and GQA bf16 batches):
 // more blocks in flight per wave beat more waves per SIMD up to these depths.
 constexpr int kValuBuffers = 4;    // VALU kernel: blocks in registers (NBUF-1 in flight)
+// fp32 blocks of 8 or more loads per tensor (d = 64 with B = 32, d = 128 with B >= 16) take 3:
+// four of them need more registers than a wave has and spill. The 16-bit B = 32 kernel keeps 4
+// although it then runs one wave per SIMD: with 3 (two waves per SIMD) the shared-prefix step's
+// decode took 174.9 against 169.9 us (measured on MI355X).
+template <DT dt, int D, int BS>
+constexpr int valu_buffers() {
+  return (dt == DT::F32 && ValuCfg<dt, D, BS, kWaves>::NL >= 8) ? 3 : kValuBuffers;
+}
 constexpr int kMfmaBuffers = 3;    // MFMA kernel: 32-token steps in registers
 constexpr int kMfmaMinBlocks = 1;  // MFMA kernel: workgroups per CU the registers must allow
 
@@ -637,7 +645,7 @@ static hipError_t launch_t(DecodePath path, const DecodeArgs& a, hipStream_t str
       return hipErrorInvalidValue;
     }
   } else {
-    fn = (const void*)decode_valu_kernel<dt, D, BS, kWaves, kValuBuffers>;
+    fn = (const void*)decode_valu_kernel<dt, D, BS, kWaves, valu_buffers<dt, D, BS>()>;
   }
   hipError_t e = hipLaunchKernel(fn, grid, block, args, 0, stream);
   if (e != hipSuccess || a.max_parts <= 1) return e;
