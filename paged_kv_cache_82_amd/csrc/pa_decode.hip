@@ -316,6 +316,44 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
 
 // ---- MFMA kernel (grouped query heads) -----------------------------------------------------
 
+// s_waitcnt vmcnt(N) (vmcnt in bits [3:0] and [15:14]), expcnt and lgkmcnt left at their maxima.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// K operand fragments of a 32-token step from the wave's LDS slot: t[u][kk] from ka[kk] +
+// OFF + u * UOFF. One asm block that also waits for the reads: the compiler treats LDS reads
+// as possibly aliasing the K DMA loads still in flight and would drain every load before them.
+template <int OFF, int UOFF>
+__device__ __forceinline__ void lds_read_k(u32x4 (&t)[2][4], const uint32_t (&ka)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:%12\n\t"
+      "ds_read_b128 %1, %9 offset:%12\n\t"
+      "ds_read_b128 %2, %10 offset:%12\n\t"
+      "ds_read_b128 %3, %11 offset:%12\n\t"
+      "ds_read_b128 %4, %8 offset:%13\n\t"
+      "ds_read_b128 %5, %9 offset:%13\n\t"
+      "ds_read_b128 %6, %10 offset:%13\n\t"
+      "ds_read_b128 %7, %11 offset:%13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(t[0][0]), "=&v"(t[0][1]), "=&v"(t[0][2]), "=&v"(t[0][3]), "=&v"(t[1][0]),
+        "=&v"(t[1][1]), "=&v"(t[1][2]), "=&v"(t[1][3])
+      : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "i"(OFF), "i"(OFF + UOFF));
+}
+template <int OFF, int UOFF>
+__device__ __forceinline__ void lds_read_k(u32x4 (&t)[2][2], const uint32_t (&ka)[2]) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%6\n\t"
+      "ds_read_b128 %1, %5 offset:%6\n\t"
+      "ds_read_b128 %2, %4 offset:%7\n\t"
+      "ds_read_b128 %3, %5 offset:%7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(t[0][0]), "=&v"(t[0][1]), "=&v"(t[1][0]), "=&v"(t[1][1])
+      : "v"(ka[0]), "v"(ka[1]), "i"(OFF), "i"(OFF + UOFF));
+}
+
 template <DT dt, int D, int BS, int NW, int NBUF, int MINB>
 __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const DecodeArgs a) {
   static_assert(dt != DT::F32, "MFMA path takes 16-bit inputs");
@@ -328,6 +366,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
   constexpr int MT = D / 16;  // p.V M-tiles; row r of tile mt is head dimension MT*r + mt
   constexpr int NBS = 32 / BS;
   constexpr int NT = NW * 64;
+  __shared__ __attribute__((aligned(1024))) char lds_k[NW][NBUF][32 * D * 2];  // K ring
   __shared__ float lds_o[NW][16][D];
   __shared__ float lds_m[NW][16], lds_l[NW][16];
   __shared__ float lds_fm[16], lds_fl[16];
@@ -387,11 +426,9 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
   const int ns = (st1 - st0 - w + NW - 1) / NW;
   const int64_t Hkv = a.num_kv_heads;
 
-  // Loop-invariant per-lane byte offsets inside a (block, head) tile. Token tk of a step lives
-  // in the step's block tk / BS at row tk % BS; for BS >= 16 the block of tile u is the same
-  // for every lane, so loads are (wave-uniform tile base) + (32-bit lane offset).
   constexpr int RB = D * E;  // bytes per token row
-  const uint32_t koff = (uint32_t)((hh % BS) * RB + 8 * gq * E);
+  // V: loop-invariant per-lane byte offset inside a (block, head) tile. Token tk of a step lives
+  // in the step's block tk / BS at row tk % BS.
   const uint32_t voff = (uint32_t)(((4 * gq) % BS) * RB + MT * hh * E);
   const int64_t tile_bytes = (int64_t)BS * RB;
   // Tile (block p, head kvh) starts at p * blk_stride + kvh * tile_bytes in each pool; the head
@@ -400,62 +437,79 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
   const char* kbase = (const char*)a.k_cache + kvh * tile_bytes;
   const char* vbase = (const char*)a.v_cache + kvh * tile_bytes;
   const int id_max = last_block_id(a.num_blocks);
-  // Loads: K ordinary, V non-temporal. A V load instruction covers whole token rows (whole
-  // 128-byte lines); a K load instruction covers 64 bytes of each of 16 rows, and the other half
-  // of each line comes from the next instruction, so K is kept cacheable (measured on MI355X:
-  // streaming K as well was 8% slower, streaming V alone 6% faster). Fetch k >= ns is a
-  // prefetch past the wave's last step, never consumed.
-  auto fetch = [&](int k, StepRegs<D, KC>& R) {
+
+  // K goes through a ring of NBUF LDS slots per wave (no other wave touches them), V through a
+  // ring of NBUF register sets. A step's K is KD DMA loads (buffer_load ... lds) of 1 KB, RPL
+  // whole rows each, so every K load instruction reads whole 128-byte lines and can be
+  // non-temporal. Loaded straight into registers in the MFMA operand layout, a K load
+  // instruction would cover 64 bytes of each of 16 rows, with the other half of each line in the
+  // next instruction; that only works with ordinary loads, which keep the line cached in between
+  // (measured on MI355X: the GQA batch took 366.8 us that way). The operand is read back with
+  // ds_read_b128; rows are XOR-swizzled in 16-byte chunks so that the 16 rows read at one chunk
+  // hit distinct banks. V loads cover whole token rows and are non-temporal loads into
+  // registers. A fetch past the wave's last step, and a block of the last step past the
+  // partition's last token, read nothing: their buffer resources span no bytes (B = 8 V loads
+  // excepted, see below).
+  constexpr int KSTEP = 32 * RB;  // K bytes per 32-token step
+  constexpr int KD = KSTEP / 1024;
+  constexpr int RPL = 1024 / RB;  // rows per K load
+  constexpr int CPR = RB / 16;    // 16-byte chunks per row
+  constexpr int RPBL = 256 / RB;  // rows per 256-byte line of banks
+  static_assert(BS % RPL == 0, "the rows of one K load lie in one block");
+  auto swz = [](int r) { return (r / RPBL) % CPR; };
+  // K load j: lane L fills LDS chunk L % CPR of step row j * RPL + L / CPR with the logical
+  // chunk the swizzle maps there.
+  uint32_t kdo[KD];
+#pragma unroll
+  for (int j = 0; j < KD; ++j) {
+    const int r = j * RPL + lane / CPR;
+    kdo[j] = (uint32_t)((r % BS) * RB + (((lane % CPR) ^ swz(r)) * 16));
+  }
+  // K operand of tile u, MFMA kk: lane (gq, hh) reads row 16u + hh, chunk 4kk + gq (head dims
+  // 32kk + 8gq ..); swz(16u + hh) = swz(hh), so tile u is a constant offset of 16 rows.
+  typedef __attribute__((address_space(3))) char lds_char;
+  uint32_t ka[KC];
+#pragma unroll
+  for (int kk = 0; kk < KC; ++kk)
+    ka[kk] = (uint32_t)(uintptr_t)(lds_char*)&lds_k[w][0][0] + hh * RB +
+             (((4 * kk + gq) ^ swz(hh)) * 16);
+
+  auto fetch = [&](int k, auto slotc, VRegs<D>& R) {
+    constexpr int slot = decltype(slotc)::value;
     const bool live = k < ns;
     const int kq = live ? k : 0;
     const int jfirst = (st0 + w + k * NW) * (32 / BS);
+    __amdgpu_buffer_rsrc_t kr[NBS];
+    int64_t tile[NBS];
+    bool has[NBS];
+#pragma unroll
+    for (int b = 0; b < NBS; ++b) {
+      const int id = clamp_id(__builtin_amdgcn_readlane(my_id[b], kq), id_max);
+      tile[b] = (int64_t)id * blk_stride;
+      has[b] = live && jfirst + b <= jlast;
+      kr[b] = tile_rsrc(kbase + tile[b], has[b] ? (int)tile_bytes : 0);
+    }
+    // K first, then V: 0.7% faster on the GQA batch than the other order (measured on MI355X).
+#pragma unroll
+    for (int j = 0; j < KD; ++j)
+      load16_tile_stream_lds(kr[(j * RPL) / BS], &lds_k[w][slot][j * 1024], kdo[j]);
     if constexpr (BS >= 16) {
-      // Every load instruction reads within one block: it goes through buffer resources that
-      // span the block's K and V tiles. A block past this partition's last one (no valid token)
-      // and every block of a fetch past the wave's last step get resources spanning no bytes:
-      // those loads return 0 and read nothing.
-      __amdgpu_buffer_rsrc_t kr[NBS], vr[NBS];
+      __amdgpu_buffer_rsrc_t vr[NBS];
 #pragma unroll
-      for (int b = 0; b < NBS; ++b) {
-        const int id = clamp_id(__builtin_amdgcn_readlane(my_id[b], kq), id_max);
-        const int64_t tile = (int64_t)id * blk_stride;
-        const int bytes = (live && jfirst + b <= jlast) ? (int)tile_bytes : 0;
-        kr[b] = tile_rsrc(kbase + tile, bytes);
-        vr[b] = tile_rsrc(vbase + tile, bytes);
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int kk = 0; kk < KC; ++kk)
-          R.k[u][kk] = load16_tile(kr[(16 * u) / BS], koff + ((16 * u) % BS) * RB + 32 * kk * E);
+      for (int b = 0; b < NBS; ++b) vr[b] = tile_rsrc(vbase + tile[b], has[b] ? (int)tile_bytes : 0);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           R.v[u][i] = VF::load_tile_stream(vr[(16 * u) / BS], voff + ((16 * u) % BS + i) * RB);
     } else {
-      // BS == 8: lanes of one load instruction read two different blocks, which one buffer
-      // resource cannot span. Plain loads; a fetch past the wave's last step reads block 0 of
-      // its KV head (shared by every such fetch on that head, so cached), not its own streamed
-      // last step.
-      const char* kt[NBS];
+      // BS == 8: lanes of one V load instruction read two different blocks, which one buffer
+      // resource cannot span. Plain loads of the clamped block ids (any block id in the pool
+      // is readable memory; tokens past the partition are masked); a fetch past the wave's last
+      // step reads block 0 of its KV head, shared by every such fetch and so cached.
       const char* vt[NBS];
 #pragma unroll
-      for (int b = 0; b < NBS; ++b) {
-        // a block past this partition's last one holds no valid token: read the step's first
-        // block instead (its tokens are masked), never an id beyond the sequence's blocks
-        const int32_t id = (jfirst + b <= jlast) ? __builtin_amdgcn_readlane(my_id[b], kq)
-                                                 : __builtin_amdgcn_readlane(my_id[0], kq);
-        const int64_t tile = live ? (int64_t)clamp_id(id, id_max) * blk_stride : 0;
-        kt[b] = kbase + tile;
-        vt[b] = vbase + tile;
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const char* rp = kt[2 * u + (hh >> 3)] + koff;  // lanes hh < 8 and hh >= 8: two blocks
-#pragma unroll
-        for (int kk = 0; kk < KC; ++kk) R.k[u][kk] = load16(rp + 32 * kk * E);
-      }
+      for (int b = 0; b < NBS; ++b) vt[b] = vbase + (live ? tile[b] : 0);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -465,8 +519,14 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
     __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the consume that follows
   };
 
-  auto consume = [&](int k, StepRegs<D, KC>& R) {
+  auto consume = [&](int k, auto slotc, VRegs<D>& R) {
+    constexpr int slot = decltype(slotc)::value;
     const int tau0 = (st0 + w + k * NW) * 32;
+    // This step's K loads (and all loads issued before them) are done once at most its own 8 V
+    // loads and those of the NBUF - 1 later fetches (8 V and KD K loads each) are outstanding.
+    wait_vmcnt<(NBUF - 1) * (8 + KD) + 8>();
+    u32x4 kf[2][KC];
+    lds_read_k<slot * KSTEP, 16 * RB>(kf, ka);
     // S^T = K Q^T: sacc[u][i] = score of token tau0 + 16u + 4*gq + i for head hh.
     f32x4 sacc[2];
 #pragma unroll
@@ -474,7 +534,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
       sacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KC; ++kk)
-        sacc[u] = M::mma(__builtin_bit_cast(vec8, R.k[u][kk]), qop[kk], sacc[u]);
+        sacc[u] = M::mma(__builtin_bit_cast(vec8, kf[u][kk]), qop[kk], sacc[u]);
     }
     const bool tail = tau0 + 32 > t1;
     float sc[8];
@@ -528,17 +588,18 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
     m = mn;
   };
 
-  if (ns > 0) {  // ring of NBUF register buffers, unconditional prefetch (see the VALU kernel)
-    StepRegs<D, KC> rb[NBUF];
-#pragma unroll
-    for (int u = 0; u + 1 < NBUF; ++u) fetch(u, rb[u]);
+  if (ns > 0) {  // rings of NBUF slots, unconditional prefetch (see the VALU kernel)
+    VRegs<D> rb[NBUF];
+    static_for<NBUF - 1>([&](auto uc) { fetch(decltype(uc)::value, uc, rb[decltype(uc)::value]); });
+    // Unrolled NBUF steps at a time so that every slot index is a constant.
     for (int k = 0; k < ns; k += NBUF) {
-#pragma unroll
-      for (int u = 0; u < NBUF; ++u) {
-        if (k + u >= ns) break;
-        fetch(k + u + NBUF - 1, rb[(u + NBUF - 1) % NBUF]);
-        consume(k + u, rb[u]);
-      }
+      static_for<NBUF>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        if (k + u >= ns) return;  // uniform
+        constexpr int ahead = (u + NBUF - 1) % NBUF;
+        fetch(k + u + NBUF - 1, std::integral_constant<int, ahead>{}, rb[ahead]);
+        consume(k + u, uc, rb[u]);
+      });
     }
   }
 

@@ -4,7 +4,20 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace pa {
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>): unrolls a loop whose index
+// must be a compile-time constant (register ring slots, LDS offsets in asm immediates).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -126,6 +139,15 @@ __device__ __forceinline__ u32x4 load16_tile(__amdgpu_buffer_rsrc_t r, uint32_t 
 __device__ __forceinline__ u32x4 load16_tile_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4,
                             __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCachePolicyNt));
+}
+// One 16-byte-per-lane DMA load through a buffer resource, non-temporal, straight into LDS:
+// lane L writes LDS bytes [lds + 16 L, lds + 16 L + 16) (lds wave-uniform). The LDS address is
+// taken as a generic pointer (with an LDS-typed one in a kernel template, clang's host pass
+// drops the kernel's stub).
+__device__ __forceinline__ void load16_tile_stream_lds(__amdgpu_buffer_rsrc_t r, void* lds,
+                                                       uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           off, 0, 0, kCachePolicyNt);
 }
 __device__ __forceinline__ u32x2 load8_tile_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x2,

@@ -66,11 +66,10 @@ __device__ __forceinline__ uint32_t vfrag_elem(const typename VFrag<D>::T& f, in
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-// One 32-token step of one wave: loads of tile u hold K rows of tokens 16u + hh (KC chunks)
-// and V rows of tokens 16u + 4*gq + i (i < 4).
-template <int D, int KC>
-struct StepRegs {
-  u32x4 k[2][KC];
+// The V registers of one 32-token step of one wave: loads of tile u hold V rows of tokens
+// 16u + 4*gq + i (i < 4).
+template <int D>
+struct VRegs {
   typename VFrag<D>::T v[2][4];
 };
 

@@ -105,16 +105,6 @@ __device__ __forceinline__ void lds_read_vt(u32x2 (&t)[4][2], const uint32_t (&v
       : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "i"(OFF0), "i"(OFF1));
 }
 
-// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>)
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
 // Maxima of scores without the NaN-quieting copies the compiler puts in front of fmaxf (two of
 // its six instructions per eight scores): v_max3_f32 takes three at a time. A NaN score can
 // only come from a NaN key or query element and makes that row's output NaN either way.
