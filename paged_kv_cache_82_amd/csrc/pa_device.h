@@ -109,9 +109,6 @@ __device__ __forceinline__ int wave_id() {
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
-__device__ __forceinline__ u32x2 load8(const void* p) {
-  return *reinterpret_cast<const u32x2*>(p);
-}
 // Non-temporal 16-byte load, for K/V tiles a launch reads once: the caches evict these lines
 // first, which lets a stream of whole 128-byte lines run closer to the HBM rate. Do not re-read
 // such a line later in the same launch and expect a cache hit.
@@ -132,9 +129,6 @@ constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kCachePolicyNt = 2;  // the instruction's nt bit: lines are evicted first
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
-}
-__device__ __forceinline__ u32x4 load16_tile(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 __device__ __forceinline__ u32x4 load16_tile_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4,

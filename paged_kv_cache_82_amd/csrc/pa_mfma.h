@@ -42,7 +42,6 @@ template <>
 struct VFrag<128> {
   using T = u32x4;
   static constexpr int words = 4;
-  static __device__ __forceinline__ T load(const char* p) { return load16(p); }
   static __device__ __forceinline__ T load_stream(const char* p) { return load16_stream(p); }
   static __device__ __forceinline__ T load_tile_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return load16_tile_stream(r, off);
@@ -52,7 +51,6 @@ template <>
 struct VFrag<64> {
   using T = u32x2;
   static constexpr int words = 2;
-  static __device__ __forceinline__ T load(const char* p) { return load8(p); }
   static __device__ __forceinline__ T load_stream(const char* p) { return load8_stream(p); }
   static __device__ __forceinline__ T load_tile_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return load8_tile_stream(r, off);
