@@ -116,3 +116,55 @@ def test_prefill_launch_of_100k_workgroups():
                          np.ascontiguousarray(tables[seqs]), np.ascontiguousarray(lens[seqs]),
                          sub_qs, np.float32(1 / math.sqrt(d)), dt)
     assert_attention_close(got[rows], ref, dt, "100k workgroups")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_pools_beyond_4gib(dt):
+    # A 5 GiB pool of each of K and V (NaN everywhere) holding a small problem's blocks at the
+    # top, past 4 GiB, so every tile offset needs more than 32 bits. Decode on the vector kernel
+    # (2 query heads over 2 KV heads) and the matrix kernel (16 over 2), whole and split, and
+    # prefill, against the oracle on the compact pools.
+    rng = np.random.default_rng(1003)
+    Hkv, d, B = 2, 128, 16
+    lens = np.array([700, 33, 1], np.int32)
+    kc, vc, tables = _paged(rng, lens, Hkv, d, B, dt)
+    block_bytes = Hkv * B * d * 2
+    N_big = (5 << 30) // block_bytes
+    hid = (N_big - 1 - 3 * np.arange(kc.shape[0])).astype(np.int64)
+    assert hid.min() * block_bytes > (4 << 30)
+    big_tables = np.where(tables >= 0, hid[np.maximum(tables, 0)], -1).astype(np.int32)
+    nan_bits = int(np.asarray(nan_value(dt)).view(np.uint16))
+    kbig = torch.full((N_big, Hkv, B, d), nan_bits, dtype=torch.int16, device="cuda")
+    vbig = torch.full((N_big, Hkv, B, d), nan_bits, dtype=torch.int16, device="cuda")
+    idx = torch.from_numpy(hid).cuda()
+    kbig[idx] = to_dev(kc, dt).view(torch.int16)
+    vbig[idx] = to_dev(vc, dt).view(torch.int16)
+    kbig, vbig = kbig.view(TORCH_DT[dt]), vbig.view(TORCH_DT[dt])
+    scale = np.float32(1 / math.sqrt(d))
+    for Hq in (2, 16):
+        q = to_storage(rng.standard_normal((len(lens), Hq, d), dtype=np.float32), dt)
+        ref = oracle.decode(q, kc, vc, tables, lens, scale, dt)
+        for P in (0, 64):
+            maxT = int(lens.max())
+            ws_bytes = pa.pa_decode_workspace_size(len(lens), Hq, Hkv, d, B, maxT, P,
+                                                   TORCH_DT[dt])
+            ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+            dq = to_dev(q, dt)
+            out = torch.empty_like(dq)
+            pa.pa_decode(out, dq, kbig, vbig, to_dev(big_tables), to_dev(lens), float(scale),
+                         maxT, ws, P)
+            torch.cuda.synchronize()
+            assert_attention_close(to_host(out, dt), ref, dt, f"decode >4 GiB Hq={Hq} P={P}")
+    n = np.array([300, 20, 1], np.int64)
+    qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    for Hq in (2, 16):
+        q = to_storage(rng.standard_normal((int(qs[-1]), Hq, d), dtype=np.float32), dt)
+        dq = to_dev(q, dt)
+        out = torch.empty_like(dq)
+        pa.pa_prefill(out, dq, kbig, vbig, to_dev(big_tables), to_dev(lens), to_dev(qs),
+                      float(scale), int(n.max()), int(lens.max()))
+        torch.cuda.synchronize()
+        ref = oracle.prefill(q, kc, vc, tables, lens, qs, scale, dt)
+        assert_attention_close(to_host(out, dt), ref, dt, f"prefill >4 GiB Hq={Hq}")
+    del kbig, vbig
+    torch.cuda.empty_cache()
