@@ -145,12 +145,44 @@ def cpu_baseline(step, budget_s: float = 12.0) -> dict:
     tok = float(step.context_lens[sample].sum()) * reps
     frac = float(step.context_lens[sample].sum()) / nb["tokens"]
     gbs = nb["decode"] * frac * reps / elapsed / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"decode of sequences 0..{n - 1} of {S} ({int(step.context_lens[sample].sum())} "
-                      f"of {int(nb['tokens'])} context tokens), fp64 oracle, {reps} passes in "
-                      f"{elapsed:.1f} s",
-            "seq_tokens_per_s": round(tok / elapsed, 1)}
+    res = {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+           "kind": "oracle",
+           "sample": f"decode of sequences 0..{n - 1} of {S} ({int(step.context_lens[sample].sum())} "
+                     f"of {int(nb['tokens'])} context tokens), fp64 oracle, {reps} passes in "
+                     f"{elapsed:.1f} s",
+           "seq_tokens_per_s": round(tok / elapsed, 1), "cpu_model": cpu_model()}
+    # The same oracle on one thread, on the first sequence(s) for about a quarter of the budget.
+    threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        one = np.asarray(seqs[:max(1, n // threads)], np.int32)
+        reps1, t0 = 0, time.perf_counter()
+        while reps1 == 0 or (time.perf_counter() - t0 < budget_s / 4 and reps1 < 1000):
+            oracle.decode(step.q, step.k_cache, step.v_cache, step.block_tables,
+                          step.context_lens, step.scale, step.dtype, seq_list=one)
+            reps1 += 1
+        el1 = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(threads)
+    t1 = float(step.context_lens[one].sum())
+    res["single_thread"] = {
+        "value": round(nb["decode"] * (t1 / nb["tokens"]) * reps1 / el1 / 1e9, 4), "unit": "GB/s",
+        "seq_tokens_per_s": round(t1 * reps1 / el1, 1),
+        "sample": f"decode of sequences 0..{len(one) - 1} ({int(t1)} context tokens), "
+                  f"{reps1} passes in {el1:.1f} s on 1 thread"}
+    return res
+
+
+def cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def prefill_flops(step) -> float:

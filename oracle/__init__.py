@@ -15,7 +15,9 @@ invariants, brute force on tiny inputs, and a mutation test showing that planted
 a pin). No function is "parity unpinned".
 """
 from .core import (build, copy_blocks, decode, lib_path, num_threads, prefill, round_to,
+                   set_num_threads,
                    run_prefill_step, run_step, swap_blocks, widen, write_kv)
 
 __all__ = ["build", "copy_blocks", "decode", "lib_path", "num_threads", "prefill", "round_to",
+           "set_num_threads",
            "run_prefill_step", "run_step", "swap_blocks", "widen", "write_kv"]

@@ -85,6 +85,14 @@ def num_threads(lib: str | None = None) -> int:
     return int(_load(lib).oracle_num_threads())
 
 
+def set_num_threads(n: int, lib: str | None = None) -> None:
+    """Threads the oracle's later calls use; timing only, results do not depend on it."""
+    f = _load(lib).oracle_set_num_threads
+    f.argtypes = [ctypes.c_int]
+    f.restype = None
+    f(int(n))
+
+
 def widen(a: np.ndarray, dtype: str, lib: str | None = None) -> np.ndarray:
     a = _need(np.ascontiguousarray(a), dtype, "a")
     out = np.empty(a.shape, np.float64)

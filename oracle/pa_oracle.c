@@ -379,3 +379,13 @@ int oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Sets the number of threads the calls that follow use (n > 0); for timing the oracle on one
+ * core beside all of them. The arithmetic does not depend on it. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
