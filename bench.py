@@ -59,7 +59,7 @@ WORKLOADS = {
 }
 
 # The sources each kernel family is built from: a committed counter summary is used only while
-# these files are unchanged since the counters were taken.
+# their code (comments and spacing aside) is unchanged since the counters were taken.
 KERNEL_SOURCES = {
     "decode": ["paged_kv_cache_82_amd/csrc/pa_decode.hip",
                "paged_kv_cache_82_amd/csrc/pa_device.h",
@@ -72,10 +72,36 @@ KERNEL_SOURCES = {
 }
 
 
+def code_only(text: str) -> str:
+    """C/C++ source without its comments, whitespace runs collapsed to one space (string and
+    character literals kept as they are)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
 def source_hash(kind: str) -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES[kind]:
-        h.update(open(os.path.join(ROOT, p), "rb").read())
+        h.update(code_only(open(os.path.join(ROOT, p)).read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

@@ -19,8 +19,9 @@
 //     the same launch would need device-scope release/acquire fences, which on gfx950 write
 //     back and invalidate the whole L2 of an XCD; the kernel boundary is far cheaper.
 //   - each wave's physical block ids are read once into one register (lane k = k-th block)
-//     and broadcast with readlane, and the next block's K/V loads are issued before the
-//     current block is consumed (two register buffers).
+//     and broadcast with readlane; the K/V loads of the next blocks (steps) are issued before
+//     the current one is consumed, through a ring of buffers; K/V bytes are read once per
+//     launch, with non-temporal loads.
 // Scores are kept in the base-2 exponent domain: s' = s * log2(e), exp(s - m) = 2^(s' - m').
 //
 // Two kernels:
@@ -30,8 +31,9 @@
 //   decode_mfma_kernel: one KV head and up to 16 query heads per workgroup (grouped-query
 //     attention); each K/V tile is read once for all heads of the group and both products run
 //     on 16x16x32 MFMA: S^T = K Q^T (tokens x heads) and O^T += V^T P^T (dims x heads).
-//     V is read with 16-byte row loads; the transposition the p.V product needs is absorbed by
-//     pairing M-tile row r with head dimension (D/16)*r + mt, so no LDS staging is needed.
+//     K reaches its operand layout through a per-wave LDS ring (whole-line DMA loads); V is
+//     read with 16-byte row loads straight into registers, the transposition the p.V product
+//     needs being absorbed by pairing M-tile row r with head dimension (D/16)*r + mt.
 #include "pa_device.h"
 #include "pa_internal.h"
 #include "pa_mfma.h"
