@@ -48,7 +48,7 @@
  * PA_ERR_WORKSPACE for a workspace smaller than pa_decode_workspace_size; PA_ERR_HIP when the
  * HIP runtime reports an error at launch.
  *
- * Supported shapes: dtype f32, f16, bf16 (pa_prefill: f16, bf16); head_dim 64 or 128;
+ * Supported shapes: dtype f32, f16, bf16; head_dim 64 or 128;
  * block_size 8, 16 or 32.
  */
 #ifndef PA_H
@@ -143,15 +143,17 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v
  * 0 .. T_s - n_s + i (the causal rule; a decode step is the case n_s = 1):
  *   out[r][h] = sum_{t <= p} exp(s_t - M) V_t / sum_{t <= p} exp(s_t - M),
  *   s_t = scale * q[r][h] . K_t,  K_t = k_cache[block_tables[s][t/B]][h/g][t%B],  p = T_s-n_s+i
- * computed in fp32 (MFMA) and rounded to nearest-even in `dt`.
+ * computed in fp32 (on MFMA for f16/bf16, on the vector ALU for f32) and rounded to
+ * nearest-even in `dt`.
  * q, out: [num_q_tokens][num_q_heads][head_dim], 16-byte aligned; rows that belong to no
  * sequence are left untouched.
  * query_start: int32 [num_seqs + 1], device, non-decreasing, within [0, num_q_tokens].
  * max_query_len: host-known bound on every n_s; max_context_len: on every T_s (they size the
  * grid; no device read on the host). n_s > T_s or n_s > max_query_len is a caller error: only
  * min(n_s, T_s, max_query_len) rows are computed.
- * Supported: dt f16 or bf16 (PA_ERR_UNSUPPORTED for f32), head_dim 64 or 128, block_size 8,
- * 16 or 32. No workspace. Device indices are clamped as for pa_decode.
+ * Supported: dt f32, f16 or bf16, head_dim 64 or 128, block_size 8, 16 or 32; for f32,
+ * num_q_tokens * num_q_heads <= 2^31 - 1 (PA_ERR_INVALID_ARG otherwise). No workspace. Device
+ * indices are clamped as for pa_decode.
  */
 pa_status pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
                      const int32_t *block_tables, const int32_t *context_lens,

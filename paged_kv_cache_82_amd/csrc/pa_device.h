@@ -99,6 +99,10 @@ __device__ __forceinline__ int clamp_id(int32_t phys, int id_max) {
   return lo < id_max ? lo : id_max;
 }
 
+__device__ __forceinline__ int clampi(int x, int lo, int hi) {
+  return x < lo ? lo : (x > hi ? hi : x);
+}
+
 // Wave index inside the workgroup as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));

@@ -50,10 +50,6 @@ constexpr int kXcds = 8;             // MI355X: workgroups are dealt round-robin
 // rescaled: weights stay below 2^8 = 256, well inside fp16/bf16 and fp32 sums.
 constexpr float kSlack = 8.0f;
 
-__device__ __forceinline__ int clampi(int x, int lo, int hi) {
-  return x < lo ? lo : (x > hi ? hi : x);
-}
-
 // The V^T operand of the p.V product comes from ds_read_b64_tr_b16: inside each aligned group
 // of 16 lanes, lane 4q + p receives element p of the 8-byte chunks addressed by lanes q,
 // q + 4, q + 8 and q + 12 (in that order). The reads are issued from one asm block that also
@@ -489,7 +485,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
 int prefill_rows_per_workgroup() { return kPrefillWaves * kPrefillColTiles * 16; }
 
 bool prefill_supported(int dt, int head_dim, int block_size) {
-  if (dt != 1 && dt != 2) return false;  // 16-bit inputs (MFMA)
+  if (dt < 0 || dt > 2) return false;  // 16-bit inputs on MFMA, fp32 on the vector ALU
   if (head_dim != 64 && head_dim != 128) return false;
   return block_size == 8 || block_size == 16 || block_size == 32;
 }
@@ -528,6 +524,7 @@ static hipError_t launch_pf_d(int d, int bs, const PrefillArgs& a, hipStream_t s
 hipError_t launch_prefill(int dt, int head_dim, int block_size, const PrefillArgs& a,
                           hipStream_t stream) {
   switch (dt) {
+    case 0: return launch_prefill_valu(head_dim, block_size, a, stream);
     case 1: return launch_pf_d<DT::F16>(head_dim, block_size, a, stream);
     case 2: return launch_pf_d<DT::BF16>(head_dim, block_size, a, stream);
     default: return hipErrorInvalidValue;

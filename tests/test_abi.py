@@ -153,7 +153,9 @@ def test_prefill_argument_checks(lib):
     assert call(qs=None) == PA_ERR_INVALID_ARG
     assert call(out=V(0x1008)) == PA_ERR_INVALID_ARG  # q/out rows need 16-byte alignment
     assert call(Hq=8, Hkv=3) == PA_ERR_INVALID_ARG
-    assert call(dt=F32) == PA_ERR_UNSUPPORTED  # MFMA path: 16-bit inputs only
+    # fp32 runs on the vector ALU: one workgroup per (query row, query head), at most 2^31 - 1
+    assert call(dt=F32, d=96) == PA_ERR_UNSUPPORTED
+    assert call(dt=F32, Nq=1 << 29, Hq=8, Hkv=8) == PA_ERR_INVALID_ARG
     assert call(d=96) == PA_ERR_UNSUPPORTED
     assert call(B=64) == PA_ERR_UNSUPPORTED
     assert call(M=0) == PA_ERR_INVALID_ARG

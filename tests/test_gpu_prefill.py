@@ -1,6 +1,7 @@
 """GPU parity of pa_prefill (causal multi-query attention over the paged pool) against the CPU
-oracle, through the C ABI: |gpu - ref| <= 2e-2 + 1e-2 |ref| elementwise (16-bit inputs, fp32
-accumulation), the chunk's KV write bit-exact. Shapes span several row tiles with ragged
+oracle, through the C ABI: |gpu - ref| <= 2e-2 + 1e-2 |ref| elementwise for 16-bit inputs (fp32
+accumulation, MFMA kernel) and max-abs 1e-5 for fp32 inputs (vector-ALU kernel), the chunk's KV
+write bit-exact. Shapes span several row tiles with ragged
 tails, contexts that need more than one register of block ids, every supported head size,
 block size and group size, empty chunks, whole prompts and single-token chunks."""
 import numpy as np
@@ -38,7 +39,7 @@ def _check(step, what=""):
     return got, ref
 
 
-@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("B", [8, 16, 32])
 def test_prefill_shapes_mha(dt, d, B):
@@ -50,7 +51,7 @@ def test_prefill_shapes_mha(dt, d, B):
     _check(step, f"mha {dt} d{d} B{B}")
 
 
-@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("g", [2, 4, 8, 16])
 @pytest.mark.parametrize("d,B", [(128, 16), (64, 8), (128, 32)])
 def test_prefill_shapes_gqa(dt, g, d, B):
@@ -60,13 +61,15 @@ def test_prefill_shapes_gqa(dt, g, d, B):
     _check(step, f"gqa {dt} g{g} d{d} B{B}")
 
 
-def test_prefill_long_context_rotates_block_ids():
-    # positions past 64 and 128 steps of 32 tokens: the kernel loads block ids 64 steps at a
-    # time; rows of one wave straddle a 32-token step boundary
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_prefill_long_context_rotates_block_ids(dt):
+    # positions past 64 and 128 steps of 32 tokens: the MFMA kernel loads block ids 64 steps at
+    # a time, and rows of one wave straddle a 32-token step boundary; the fp32 kernel loads them
+    # 64 blocks per wave at a time (4500 tokens: 282 blocks, 71 for some waves)
     T = [4500, 2100, 70]
     n = [100, 37, 70]
-    step = make_prefill_step("plong", 430, T, n, 8, 2, 128, 16, "bf16")
-    _check(step, "long")
+    step = make_prefill_step("plong", 430, T, n, 8, 2, 128, 16, dt)
+    _check(step, f"long {dt}")
 
 
 def test_prefill_single_token_matches_decode():
