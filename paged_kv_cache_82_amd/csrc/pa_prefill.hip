@@ -28,9 +28,9 @@
 //     the masked path, every other stage runs without any per-score test;
 //   - a wave's physical block ids come 64 stages at a time into one register (lane k = stage
 //     k) and are broadcast with readlane;
-//   - workgroups are ordered so that the row tiles of one (sequence, KV head) run on one XCD
-//     (workgroups are dealt round-robin over the 8 XCDs) and share that XCD's L2, heaviest
-//     (latest) tiles first.
+//   - workgroups are dealt round-robin over the 8 XCDs; (sequence, KV head) groups are spread
+//     over the XCDs so that each gets a share of every sequence, and the row tiles of one group
+//     run on one XCD, heaviest (latest) first, sharing its L2.
 // Scores are kept in the base-2 exponent domain: s' = s * log2(e), exp(s - m) = 2^(s' - m').
 #include <utility>
 
@@ -150,17 +150,31 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
   static_assert(BS % RPW == 0, "the rows one wave loads lie in one block");
   __shared__ __attribute__((aligned(1024))) char lds[NBUF][2][TILE];  // [stage][K, V]
 
-  // Workgroup -> (row tile, KV head, sequence). Linear id L runs on XCD L % 8; renumber so
-  // that each XCD takes a contiguous range of tiles (whole (sequence, KV head) groups).
+  // Workgroup -> (row tile, KV head, sequence). Linear id L runs on XCD L % 8. The (sequence,
+  // KV head) groups G = kvh + Hkv * s are dealt round-robin over the XCDs, so every XCD gets
+  // its share of every sequence (handing each XCD a contiguous range of groups gave it whole
+  // sequences, and its work followed their lengths); on its XCD a group's row tiles run one
+  // after the other, heaviest (latest) first, and share that XCD's L2. Groups past the last
+  // multiple of 8 follow in order.
   const int Hkv = a.num_kv_heads;
-  const int64_t total = (int64_t)a.row_tiles * Hkv * a.num_seqs;
-  int64_t L = blockIdx.x;
-  const int64_t per = total / kXcds;
-  if (L < per * kXcds) L = (L % kXcds) * per + L / kXcds;
-  const int tile = a.row_tiles - 1 - (int)(L % a.row_tiles);
-  const int64_t rest = L / a.row_tiles;
-  const int kvh = (int)(rest % Hkv);
-  const int s = (int)(rest / Hkv);
+  const int rt = a.row_tiles;
+  const int64_t groups = (int64_t)Hkv * a.num_seqs;
+  const int64_t dealt = groups / kXcds * kXcds;
+  const int64_t L = blockIdx.x;
+  int64_t G;
+  int t_idx;
+  if (L < dealt * rt) {
+    const int64_t k = L / kXcds;  // the k-th workgroup on XCD L % 8
+    G = L % kXcds + kXcds * (k / rt);
+    t_idx = (int)(k % rt);
+  } else {
+    const int64_t r = L - dealt * rt;
+    G = dealt + r / rt;
+    t_idx = (int)(r % rt);
+  }
+  const int tile = rt - 1 - t_idx;
+  const int kvh = (int)(G % Hkv);
+  const int s = (int)(G / Hkv);
 
   // Extent of the sequence, clamped into the buffers the sizes describe.
   const int Nq = a.num_q_tokens;
