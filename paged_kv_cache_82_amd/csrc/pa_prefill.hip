@@ -174,7 +174,39 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
   }
   const int tile = rt - 1 - t_idx;
   const int kvh = (int)(G % Hkv);
-  const int s = (int)(G / Hkv);
+  // G / Hkv is a rank. With few sequences and few row tiles per group, the ranks follow the
+  // sequences' work, heaviest first, so that each XCD also runs its share longest first: lane
+  // i weighs sequence i by its visible (row, token) pairs n (2T - n) and counts the sequences
+  // ahead of it (heavier, or as heavy with a smaller index), which makes the ranks a
+  // permutation. With many row tiles per group the tiles themselves balance each XCD, and the
+  // rank is the sequence index.
+  const int rank = (int)(G / Hkv);
+  int s = rank;
+  if (a.num_seqs <= 64 && rt <= 8) {  // uniform
+    const int ln = threadIdx.x & 63;
+    float wv = -1.0f;
+    if (ln < a.num_seqs) {
+      const int Nqr = a.num_q_tokens;
+      const int qa = clampi(a.query_start[ln], 0, Nqr);
+      const int qb = clampi(a.query_start[ln + 1], qa, Nqr);
+      const int64_t capr64 = (int64_t)a.max_blocks_per_seq * BS;
+      const int capr =
+          (int)(capr64 < (int64_t)a.max_context_len ? capr64 : (int64_t)a.max_context_len);
+      const int Tr = clampi(a.context_lens[ln], 0, capr);
+      int nr = qb - qa;
+      nr = nr < Tr ? nr : Tr;
+      nr = nr < a.max_query_len ? nr : a.max_query_len;
+      wv = (float)nr * (2.0f * (float)Tr - (float)nr);
+    }
+    int ahead = 0;
+    for (int j = 0; j < a.num_seqs; ++j) {
+      const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                     __builtin_bit_cast(int, wv), j));
+      ahead += (wj > wv || (wj == wv && j < ln)) ? 1 : 0;
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(ln < a.num_seqs && ahead == rank);
+    s = __builtin_ctzll(hit);
+  }
 
   // Extent of the sequence, clamped into the buffers the sizes describe.
   const int Nq = a.num_q_tokens;
