@@ -130,7 +130,18 @@ def algorithmic_bytes(step) -> dict:
     idx = 4.0 * (float(sum(math.ceil(t / B) for t in T)) + S)
     n_new = sum(len(w.slot_mapping) for w in step.writes)
     write = 2.0 * n_new * Hkv * d * e * 2 + 4.0 * n_new
-    return {"decode": kv + qo + idx, "write": write, "tokens": float(T.sum())}
+    # What must come from HBM: each distinct physical block once, at the most tokens any
+    # sequence uses of it. Equal to the logical count unless sequences share blocks (the
+    # shared-prefix step, whose samples re-read their prompt's blocks).
+    used = {}
+    for s in range(S):
+        t = int(step.context_lens[s])
+        for j in range(-(-t // B)):
+            p = int(step.block_tables[s, j])
+            used[p] = max(used.get(p, 0), min(B, t - j * B))
+    kv_unique = float(sum(used.values())) * 2 * Hkv * d * e
+    return {"decode": kv_unique + qo + idx, "decode_logical": kv + qo + idx, "write": write,
+            "tokens": float(T.sum())}
 
 
 def make_workload(name: str, poison: bool, placement: str = "random"):
@@ -719,6 +730,11 @@ def main():
         "bytes_per_step": step_bytes,
         "input_generation_s": round(t_gen, 2),
     }
+    if nb["decode_logical"] != nb["decode"]:
+        # shared blocks: `value` and `achieved` count each block once; the logical bytes (every
+        # sequence's tokens, shared prefixes once per sequence) beside them
+        res["roofline"]["logical_bytes_per_launch"] = nb["decode_logical"]
+        res["roofline"]["logical_GB_per_s"] = round(nb["decode_logical"] / dec_s / 1e9, 2)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(step)
     print(json.dumps(res))
