@@ -92,11 +92,38 @@ __global__ __launch_bounds__(D) void merge_partitions_kernel(const DecodeArgs a)
   const int nparts = (T + a.partition_tokens - 1) / a.partition_tokens;
   if (nparts <= 1) return;
   const int64_t base = ((int64_t)s * a.num_q_heads + h) * a.max_parts;
+  // Partitions are read 8 at a time, so that their loads are in flight together (one at a
+  // time, each waiting for the last, 64 partitions took 19 us).
+  constexpr int U = 8;
   float M = kNegInf;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, a.part_m[base + p]);
+  int p = 0;
+  for (; p + U <= nparts; p += U) {
+    float mv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) mv[u] = a.part_m[base + p + u];
+#pragma unroll
+    for (int u = 0; u < U; ++u) M = fmaxf(M, mv[u]);
+  }
+  for (; p < nparts; ++p) M = fmaxf(M, a.part_m[base + p]);
   float acc = 0.0f, L = 0.0f;
   const int dim = threadIdx.x;
-  for (int p = 0; p < nparts; ++p) {
+  p = 0;
+  for (; p + U <= nparts; p += U) {
+    float mv[U], lv[U], ov[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      mv[u] = a.part_m[base + p + u];
+      lv[u] = a.part_l[base + p + u];
+      ov[u] = a.part_o[(base + p + u) * D + dim];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float wgt = rescale(mv[u], M);
+      acc = fmaf(wgt, ov[u], acc);
+      L = fmaf(wgt, lv[u], L);
+    }
+  }
+  for (; p < nparts; ++p) {
     const float wgt = rescale(a.part_m[base + p], M);
     acc = fmaf(wgt, a.part_o[(base + p) * D + dim], acc);
     L = fmaf(wgt, a.part_l[base + p], L);
