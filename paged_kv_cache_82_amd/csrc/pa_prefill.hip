@@ -19,7 +19,8 @@
 //     few of its stages need the causal mask;
 //   - the workgroup walks its context in 32-token stages: each wave loads 8 rows of the
 //     stage's K and V (rows of one block, found through the block table) straight from HBM
-//     into LDS, with two stages in flight while one is consumed; one barrier per stage;
+//     into LDS (buffer loads into LDS), with two stages in flight while one is consumed; one
+//     barrier per stage;
 //   - LDS rows are XOR-swizzled in 16-byte chunks so that the MFMA operand reads (16 rows at
 //     one column for K, one row for V) hit distinct banks;
 //   - each wave reads a stage's K and V fragments once from LDS and uses them for all its
@@ -55,35 +56,9 @@ constexpr float kSlack = 8.0f;
 // q + 4, q + 8 and q + 12 (in that order). The reads are issued from one asm block that also
 // waits for them: the compiler treats the intrinsic as possibly reading the LDS that the
 // stage loads (LDS DMA) are still writing and would drain every load in flight before it.
-// va[mt] is the lane's LDS byte address for M-tile mt and token tile u = 0 of stage buffer 0;
-// OFF0 / OFF1 are the byte offsets of the stage buffer's token tiles 0 and 1.
-template <int OFF0, int OFF1>
-__device__ __forceinline__ void lds_read_vt(u32x2 (&t)[8][2], const uint32_t (&va)[8]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %1, %16 offset:%25\n\t"
-      "ds_read_b64_tr_b16 %2, %17 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %3, %17 offset:%25\n\t"
-      "ds_read_b64_tr_b16 %4, %18 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %5, %18 offset:%25\n\t"
-      "ds_read_b64_tr_b16 %6, %19 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %7, %19 offset:%25\n\t"
-      "ds_read_b64_tr_b16 %8, %20 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %9, %20 offset:%25\n\t"
-      "ds_read_b64_tr_b16 %10, %21 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %11, %21 offset:%25\n\t"
-      "ds_read_b64_tr_b16 %12, %22 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %13, %22 offset:%25\n\t"
-      "ds_read_b64_tr_b16 %14, %23 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(t[0][0]), "=&v"(t[0][1]), "=&v"(t[1][0]), "=&v"(t[1][1]), "=&v"(t[2][0]),
-        "=&v"(t[2][1]), "=&v"(t[3][0]), "=&v"(t[3][1]), "=&v"(t[4][0]), "=&v"(t[4][1]),
-        "=&v"(t[5][0]), "=&v"(t[5][1]), "=&v"(t[6][0]), "=&v"(t[6][1]), "=&v"(t[7][0]),
-        "=&v"(t[7][1])
-      : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]),
-        "v"(va[7]), "i"(OFF0), "i"(OFF1));
-}
+// va[mt] is the lane's LDS byte address for M-tile mt (of the half of the head dimension being
+// read) and token tile u = 0 of stage buffer 0; OFF0 / OFF1 are the byte offsets of the stage
+// buffer's token tiles 0 and 1.
 template <int OFF0, int OFF1>
 __device__ __forceinline__ void lds_read_vt(u32x2 (&t)[4][2], const uint32_t (&va)[4]) {
   asm volatile(
@@ -99,6 +74,34 @@ __device__ __forceinline__ void lds_read_vt(u32x2 (&t)[4][2], const uint32_t (&v
       : "=&v"(t[0][0]), "=&v"(t[0][1]), "=&v"(t[1][0]), "=&v"(t[1][1]), "=&v"(t[2][0]),
         "=&v"(t[2][1]), "=&v"(t[3][0]), "=&v"(t[3][1])
       : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "i"(OFF0), "i"(OFF1));
+}
+
+template <int OFF0, int OFF1>
+__device__ __forceinline__ void lds_read_vt(u32x2 (&t)[2][2], const uint32_t (&va)[2]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
+      "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(t[0][0]), "=&v"(t[0][1]), "=&v"(t[1][0]), "=&v"(t[1][1])
+      : "v"(va[0]), "v"(va[1]), "i"(OFF0), "i"(OFF1));
+}
+
+// One 16-byte-per-lane DMA load through a buffer resource straight into LDS (default cache
+// policy: other row tiles of the group read the same rows); lane L writes LDS bytes
+// [lds + 16 L, lds + 16 L + 16).
+__device__ __forceinline__ void load16_tile_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           off, 0, 0, 0);
+}
+
+// The lane id, recomputed where it is used (two instructions) rather than kept in a register
+// across the stage loop: used on paths that run once per 64 stages or on the last stage.
+__device__ __forceinline__ int fresh_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
 }
 
 // Maxima of scores without the NaN-quieting copies the compiler puts in front of fmaxf (two of
@@ -129,8 +132,12 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 
 }  // namespace
 
+// Three workgroups per CU (12 waves, 144 KB of LDS at d = 128): the kernel fits 168 VGPRs by
+// reading K and V from LDS half a head dimension at a time and recomputing the few
+// lane-derived values that rare paths need; three values spill, once per workgroup, outside
+// the stage loop.
 template <DT dt, int D, int BS, int NW, int NCT, int NBUF>
-__global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillArgs a) {
   static_assert(dt != DT::F32, "MFMA path takes 16-bit inputs");
   using M = MfmaT<dt>;
   using vec8 = typename M::vec8;
@@ -287,7 +294,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
   // and no load of `ids` is ever outstanding across stages.
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   auto load_ids = [&](int chunk) {
-    const int j = (KT * (64 * chunk + lane) + RPW * w) / BS;
+    const int j = (KT * (64 * chunk + fresh_lane()) + RPW * w) / BS;
     return bt[j < jlast ? j : jlast];  // jlast < max_blocks_per_seq since T <= cap
   };
   int ids = load_ids(0);
@@ -306,14 +313,12 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
   // 16mt + 4(s%4) .. +3 (swz_v repeats every 16 rows, so token tile u adds 16 rows).
   typedef __attribute__((address_space(3))) char lds_char;
   const uint32_t lds_v0 = (uint32_t)(uintptr_t)(lds_char*)&lds[0][1][0];
-  uint32_t va[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int cb = 32 * mt + 8 * (hh & 3);  // byte offset of the 4 dims in the row
-    va[mt] = lds_v0 + voff(4 * gq + (hh >> 2), cb >> 4) + (cb & 15);
-  }
+  // The address for M-tile mt is va0 ^ 32 mt: the swizzle moves a row's 16-byte chunks only
+  // within the bits that the M-tile's 32-byte offset occupies, and the row and buffer bits
+  // above them are unaffected. One XOR per read instead of a register per M-tile.
+  const uint32_t va0 = lds_v0 + voff(4 * gq + (hh >> 2), (8 * (hh & 3)) >> 4) + ((8 * (hh & 3)) & 15);
 
-  // Stage loads go straight from global memory into LDS (global_load_lds_dwordx4): lane L
+  // Stage loads go straight from global memory into LDS (buffer_load_dwordx4 ... lds): lane L
   // of a wave-wide load writes LDS bytes [base + 16L, base + 16L + 16), so one load fills
   // 1 KB = RPL whole rows. Lane L carries physical chunk L % CPR of row L / CPR and fetches
   // the logical chunk the swizzle maps there. No registers hold data in flight, so NBUF - 1
@@ -323,6 +328,13 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
   const int64_t tile_bytes = (int64_t)BS * RB;
   const int row_in_load = lane / CPR;
   const int pchunk = lane % CPR;
+  uint32_t ko[WLW], vo[WLW];  // byte offsets in the block's tile of the chunks this lane moves
+#pragma unroll
+  for (int k = 0; k < WLW; ++k) {
+    const int r = (w * WLW + k) * RPL + row_in_load;  // row within the stage
+    ko[k] = (uint32_t)((r % BS) * RB + (pchunk ^ swz_k(r)) * 16);
+    vo[k] = (uint32_t)((r % BS) * RB + (pchunk ^ swz_v(r)) * 16);
+  }
   auto issue_stage = [&](int st, int buf) {
     if (st > 0 && (st & 63) == 0) {  // uniform
       ids = load_ids(st >> 6);
@@ -330,18 +342,13 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
     }
     const int32_t id = __builtin_amdgcn_readlane(ids, st & 63);
     const int64_t t = (clamp_block(id, a.num_blocks) * Hkv + kvh) * tile_bytes;
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kbase + t, (int)tile_bytes);
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vbase + t, (int)tile_bytes);
 #pragma unroll
     for (int k = 0; k < WLW; ++k) {
-      const int mload = w * WLW + k;            // wave-wide load index within the tensor
-      const int r = mload * RPL + row_in_load;  // row within the stage
-      // logical chunks landing at physical chunk pchunk of row r
-      const uint32_t ko = (uint32_t)((r % BS) * RB + (pchunk ^ swz_k(r)) * 16);
-      const uint32_t vo = (uint32_t)((r % BS) * RB + (pchunk ^ swz_v(r)) * 16);
-      // (explicit void pointers: with char pointers clang's host pass drops the kernel stub)
-      __builtin_amdgcn_global_load_lds((const void*)(kbase + t + ko),
-                                       (void*)&lds[buf][0][mload * 1024], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vbase + t + vo),
-                                       (void*)&lds[buf][1][mload * 1024], 16, 0, 0);
+      const int mload = w * WLW + k;  // wave-wide load index within the tensor
+      load16_tile_lds(kr, &lds[buf][0][mload * 1024], ko[k]);
+      load16_tile_lds(vr, &lds[buf][1][mload * 1024], vo[k]);
     }
   };
   // This wave's loads of stage st are done once at most `later` stages' loads are outstanding.
@@ -367,52 +374,66 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
   // Otherwise every token is visible to every row and no score is tested.
   auto consume = [&](int tau0, auto bufc, bool mask) {
     constexpr int buf = decltype(bufc)::value;
-    u32x4 kf[2][KC];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int kk = 0; kk < KC; ++kk)
-        kf[u][kk] = *reinterpret_cast<const u32x4*>(&lds[buf][0][koff(16 * u + hh, 4 * kk + gq)]);
-    // S^T = K Q^T for every column tile: 2*NCT independent accumulation chains.
+    // S^T = K Q^T for every column tile: 2*NCT independent accumulation chains. K comes from
+    // LDS in two halves of the head dimension, so that only half of it is held at a time.
     f32x4 sacc[NCT][2];
 #pragma unroll
     for (int c = 0; c < NCT; ++c)
 #pragma unroll
       for (int u = 0; u < 2; ++u) sacc[c][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // The MFMA blocks run at raised wave priority, so that a wave holding matrix work issues
-    // it ahead of the other wave's vector work on the same SIMD.
-    __builtin_amdgcn_s_setprio(1);
+    constexpr int KH = KC / 2;
+    static_for<2>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      u32x4 kf[2][KH];
 #pragma unroll
-    for (int kk = 0; kk < KC; ++kk)
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int c = 0; c < NCT; ++c)
+        for (int j = 0; j < KH; ++j)
+          kf[u][j] = *reinterpret_cast<const u32x4*>(&lds[buf][0][koff(16 * u + hh, 4 * (h * KH + j) + gq)]);
+      // The MFMA blocks run at raised wave priority, so that a wave holding matrix work issues
+      // it ahead of the other wave's vector work on the same SIMD.
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          sacc[c][u] = M::mma(__builtin_bit_cast(vec8, kf[u][kk]), qop[c][kk], sacc[c][u]);
-    __builtin_amdgcn_s_setprio(0);
+      for (int j = 0; j < KH; ++j)
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            sacc[c][u] = M::mma(__builtin_bit_cast(vec8, kf[u][j]), qop[c][h * KH + j], sacc[c][u]);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
     // V^T operand of M-tile mt (head dims 16mt .. 16mt+15), k element e <-> token
     // 16*(e/4) + 4*gq + (e%4): the transposed read hands lane (gq, 4q + p) dim 16mt + 4q + p
     // of tokens 16u + 4gq + 0..3.
     // (issued once the scores' MFMAs are: their latency overlaps the matrix cores)
     __builtin_amdgcn_sched_barrier(0);
-    u32x2 tv[MT][2];
-    lds_read_vt<buf * 2 * TILE, buf * 2 * TILE + 16 * RB>(tv, va);
-    u32x4 vw[MT];
+    constexpr int MH = MT / 2;
+    u32x4 vw[MH];
+    auto read_v = [&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      u32x2 tv[MH][2];
+      uint32_t vah[MH];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) vw[mt] = u32x4{tv[mt][0][0], tv[mt][0][1], tv[mt][1][0], tv[mt][1][1]};
-    if (tau0 + KT - 1 > p_hi_wg) {  // uniform: V of tokens past the last position is 0
+      for (int mt = 0; mt < MH; ++mt) vah[mt] = va0 ^ (uint32_t)(32 * (h * MH + mt));
+      lds_read_vt<buf * 2 * TILE, buf * 2 * TILE + 16 * RB>(tv, vah);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int t0 = tau0 + 16 * u + 4 * gq;  // token of element 4u
-        const uint32_t keep0 = (t0 > p_hi_wg ? 0u : 0xffffu) | (t0 + 1 > p_hi_wg ? 0u : 0xffff0000u);
-        const uint32_t keep1 = (t0 + 2 > p_hi_wg ? 0u : 0xffffu) | (t0 + 3 > p_hi_wg ? 0u : 0xffff0000u);
+      for (int mt = 0; mt < MH; ++mt) vw[mt] = u32x4{tv[mt][0][0], tv[mt][0][1], tv[mt][1][0], tv[mt][1][1]};
+      if (tau0 + KT - 1 > p_hi_wg) {  // uniform: V of tokens past the last position is 0
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          vw[mt][2 * u] &= keep0;
-          vw[mt][2 * u + 1] &= keep1;
+        for (int u = 0; u < 2; ++u) {
+          const int t0 = tau0 + 16 * u + 4 * (fresh_lane() >> 4);  // token of element 4u
+          const uint32_t keep0 = (t0 > p_hi_wg ? 0u : 0xffffu) | (t0 + 1 > p_hi_wg ? 0u : 0xffff0000u);
+          const uint32_t keep1 = (t0 + 2 > p_hi_wg ? 0u : 0xffffu) | (t0 + 3 > p_hi_wg ? 0u : 0xffff0000u);
+#pragma unroll
+          for (int mt = 0; mt < MH; ++mt) {
+            vw[mt][2 * u] &= keep0;
+            vw[mt][2 * u + 1] &= keep1;
+          }
         }
       }
-    }
+    };
+    read_v(std::integral_constant<int, 0>{});
     if (mask) {  // uniform; token 16u + 4gq + i is hidden from the lane's row past its position
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
@@ -471,13 +492,17 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
       pop[c] = __builtin_bit_cast(vec8, pw);
     }
     // O^T += V^T P^T: MT * NCT independent MFMAs
-    __builtin_amdgcn_s_setprio(1);
+    static_for<2>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      if constexpr (h == 1) read_v(hc);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MH; ++mt)
 #pragma unroll
-      for (int c = 0; c < NCT; ++c)
-        oacc[c][mt] = M::mma(__builtin_bit_cast(vec8, vw[mt]), pop[c], oacc[c][mt]);
-    __builtin_amdgcn_s_setprio(0);
+        for (int c = 0; c < NCT; ++c)
+          oacc[c][h * MH + mt] = M::mma(__builtin_bit_cast(vec8, vw[mt]), pop[c], oacc[c][h * MH + mt]);
+      __builtin_amdgcn_s_setprio(0);
+    });
   };
 
   const int prolog = nstages < NBUF - 1 ? nstages : NBUF - 1;
@@ -506,13 +531,15 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
 
   // Normalise and store. oacc[c][mt][i] is O[column hh][dim 16mt + 4gq + i]: four
   // consecutive dimensions, one 8-byte store per M-tile.
+  const int lane_e = fresh_lane();
+  const int hh_e = lane_e & 15, gq_e = lane_e >> 4;
 #pragma unroll
   for (int c = 0; c < NCT; ++c) {
     float l = lsum[c];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     if (pos[c] < 0) continue;
-    const int R = W0 + 16 * (NCT * w + c) + hh;
+    const int R = W0 + 16 * (NCT * w + c) + hh_e;
     const int i = R / g;
     const int head = kvh * g + R % g;
     char* orow = (char*)a.out + ((int64_t)(q0 + i) * Hq + head) * D * E;
@@ -521,7 +548,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(const PrefillA
     for (int mt = 0; mt < MT; ++mt) {
       const u32x2 packed = {pack2<dt>(oacc[c][mt][0] * rl, oacc[c][mt][1] * rl),
                             pack2<dt>(oacc[c][mt][2] * rl, oacc[c][mt][3] * rl)};
-      *reinterpret_cast<u32x2*>(orow + (16 * mt + 4 * gq) * E) = packed;
+      *reinterpret_cast<u32x2*>(orow + (16 * mt + 4 * gq_e) * E) = packed;
     }
   }
 }
