@@ -130,6 +130,18 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   }
 }
 
+// acc + lo + hi of a packed pair of 16-bit values (v_dot2c_f32_{f16,bf16} against (1, 1)).
+template <DT dt>
+__device__ __forceinline__ float sum2(uint32_t pair, float acc) {
+  if constexpr (dt == DT::BF16) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+  } else {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
+  }
+}
+
 }  // namespace
 
 // Three workgroups per CU (12 waves, 144 KB of LDS at d = 128): the kernel fits 168 VGPRs by
@@ -276,11 +288,14 @@ __global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillA
   }
 
   f32x4 oacc[NCT][MT];
-  float m[NCT], lsum[NCT], thr[NCT];
+  // Running state per column tile: the reference maximum m (scaled, base 2) is kept as the
+  // shift nm = -m applied to every score (0 while m is -inf) and as the raw-score threshold
+  // thr = (m + kSlack) / cs (-inf while m is).
+  float nm[NCT], lsum[NCT], thr[NCT];
   const float rcs = 1.0f / cs;
 #pragma unroll
   for (int c = 0; c < NCT; ++c) {
-    m[c] = kNegInf;
+    nm[c] = 0.0f;
     thr[c] = kNegInf;
     lsum[c] = 0.0f;
 #pragma unroll
@@ -445,12 +460,12 @@ __global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillA
             if (16 * u + i > lim) sacc[c][u][i] = kNegInf;  // select
       }
     }
-    // Weights are taken against a reference maximum m[c] (scaled, base 2) that is raised only
+    // Weights are taken against a reference maximum m (scaled, base 2) that is raised only
     // when some score exceeds it by more than kSlack: weights stay below 2^kSlack, and the
     // running sum and output use the same reference, so the normalised result is the same as
     // with the exact running maximum. The test runs on raw scores against thr[c] =
-    // (m[c] + kSlack) / cs, which changes only when m[c] does. The scaled, shifted score
-    // cs * s - m is one FMA.
+    // (m + kSlack) / cs, which changes only when m does. The scaled, shifted score
+    // cs * s + nm[c] = cs * s - m is one FMA.
     float lr[NCT];  // largest raw score of the lane's 8
     bool raise = false;
 #pragma unroll
@@ -467,28 +482,32 @@ __global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillA
         const float lm = lr[c] * cs;
         float bm = fmaxf(lm, __shfl_xor(lm, 16));
         bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const float mn = fmaxf(m[c], bm);
-        const float corr = (m[c] == kNegInf) ? (mn == kNegInf ? 1.0f : 0.0f)
-                                             : fast_exp2(m[c] - mn);
+        // m is -inf exactly when thr is -inf and the shift is 0 (a finite m of 0 has a
+        // positive threshold; a threshold that overflowed to -inf has a large shift)
+        const float mo = (thr[c] == kNegInf && nm[c] == 0.0f) ? kNegInf : -nm[c];
+        const float mn = fmaxf(mo, bm);
+        const float corr = (mo == kNegInf) ? (mn == kNegInf ? 1.0f : 0.0f) : fast_exp2(mo - mn);
         lsum[c] *= corr;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) oacc[c][mt] *= corr;
-        m[c] = mn;
+        // m is -inf only while every row of the column has all its tokens hidden (all its
+        // scores -inf): the shift is 0 then, so the weights are exp2(-inf) = 0
+        nm[c] = mn == kNegInf ? 0.0f : -mn;
         thr[c] = (mn + kSlack) * rcs;
       }
     }
     vec8 pop[NCT];
 #pragma unroll
     for (int c = 0; c < NCT; ++c) {
-      // m[c] is -inf only while every row of the column has all its tokens hidden (all its
-      // scores -inf): shift by 0 then, so the weights are exp2(-inf) = 0
-      const float nm = (m[c] == kNegInf) ? 0.0f : -m[c];
       float pe[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(__builtin_fmaf(sacc[c][e / 4][e % 4], cs, nm));
-      lsum[c] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+      for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(__builtin_fmaf(sacc[c][e / 4][e % 4], cs, nm[c]));
       const u32x4 pw = {pack2<dt>(pe[0], pe[1]), pack2<dt>(pe[2], pe[3]),
                         pack2<dt>(pe[4], pe[5]), pack2<dt>(pe[6], pe[7])};
+      // The row sum takes the weights as the p.V product does, rounded to 16 bits: one dot2
+      // with (1, 1) per packed pair, accumulated in fp32.
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lsum[c] = sum2<dt>(pw[j], lsum[c]);
       pop[c] = __builtin_bit_cast(vec8, pw);
     }
     // O^T += V^T P^T: MT * NCT independent MFMAs

@@ -129,3 +129,41 @@ def prefill_rows_reference(step, kc, vc, rows):
     q_rows = np.ascontiguousarray(step.q[rows])
     tables = np.ascontiguousarray(step.block_tables[seq])
     return oracle.decode(q_rows, kc, vc, tables, visible, step.scale, step.dtype)
+
+
+def make_dominant_token(step, gap_log2: float = 15.0):
+    """Rewrite sequence 0 of a decode or prefill step so that token 0 outscores every other
+    token by gap_log2 in the base-2 exponent: every other token then weighs 2^-gap_log2 of it
+    (for 15, below fp16's smallest normal number, 2^-14, yet 3999 of them add 12% to the row
+    sum). Keys are big * e_0 for token 0 and 0 otherwise; queries are 4 e_0 (scale 1/sqrt(d));
+    V of KV head 0 is all ones (expected output exactly 1) and V of KV head 1 is ones except
+    token 0, which is 0 (expected N w / (1 + N w) with N = T - 1 small weights w). A kernel
+    that flushed the small weights in the weighted sum, or only in the row sum, misses either
+    head by more than the 16-bit tolerance."""
+    from workloads import to_storage
+
+    dt, B, d, Hkv = step.dtype, step.block_size, step.head_dim, step.num_kv_heads
+    assert Hkv >= 2 and step.num_seqs == 1
+    T = int(step.context_lens[0])
+    n_new = sum(w.k_new.shape[0] for w in step.writes)
+    prefix = T - n_new
+    scale = float(step.scale)
+    big = gap_log2 / (4.0 * scale * np.log2(np.e))
+    k = np.zeros((T, Hkv, d))
+    k[0, :, 0] = big
+    v = np.ones((T, Hkv, d))
+    v[0, 1, :] = 0.0
+    table = step.block_tables[0]
+    for t in range(prefix):
+        step.k_cache[table[t // B], :, t % B, :] = to_storage(k[t], dt)
+        step.v_cache[table[t // B], :, t % B, :] = to_storage(v[t], dt)
+    at = prefix
+    for w in step.writes:
+        m = w.k_new.shape[0]
+        w.k_new[...] = to_storage(k[at:at + m], dt)
+        w.v_new[...] = to_storage(v[at:at + m], dt)
+        at += m
+    q = np.zeros(step.q.shape)
+    q[..., 0] = 4.0
+    step.q[...] = to_storage(q, dt)
+    return step

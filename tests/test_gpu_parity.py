@@ -9,7 +9,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import oracle
-from gpu_harness import DevStep, assert_attention_close, to_host
+from gpu_harness import DevStep, assert_attention_close, make_dominant_token, to_host
 from workloads import tiny_f32, shared_prefix_f16, make_step, to_float64, to_storage
 
 pytestmark = pytest.mark.gpu
@@ -62,6 +62,17 @@ def test_both_decode_paths_on_gqa(path, monkeypatch):
     monkeypatch.setenv("PA_DECODE_PATH", path)
     step = make_step("paths", 50, [3, 64, 100, 511, 700], 16, 2, 128, 16, "bf16")
     _run_and_check(step, what=path)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("g,path", [(1, "valu"), (4, "valu"), (4, "mfma")])
+def test_small_weights_below_fp16_normal(dt, g, path, monkeypatch):
+    # one token outweighs 3999 others by 2^15: their weights are below fp16's smallest normal
+    # number and together add 12% to the row sum; both kernels, whole and split
+    monkeypatch.setenv("PA_DECODE_PATH", path)
+    for P in (0, 512):
+        step = make_dominant_token(make_step("ddom", 481, [4000], 2 * g, 2, 128, 16, dt))
+        _run_and_check(step, partition_tokens=P, what=f"dominant token {dt} g{g} {path} P{P}")
 
 
 @pytest.mark.parametrize("P", [32, 64, 96, 512])

@@ -10,8 +10,8 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import oracle
-from gpu_harness import (DevPrefill, DevStep, assert_attention_close, prefill_rows_reference,
-                         to_host)
+from gpu_harness import (DevPrefill, DevStep, assert_attention_close, make_dominant_token,
+                         prefill_rows_reference, to_host)
 from workloads import make_prefill_step, make_step, to_float64
 
 pytestmark = pytest.mark.gpu
@@ -102,6 +102,15 @@ def test_prefill_large_scores_stay_finite():
 
     step.q[...] = to_storage(to_float64(step.q, "bf16") * 30.0, "bf16")
     _check(step, "large scores")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("g", [1, 4])
+def test_prefill_small_weights_below_fp16_normal(dt, g):
+    # one token outweighs 3999 others by 2^15: their 16-bit weights are fp16 subnormals that
+    # together add 12% to the row sum; the weighted sum and the row sum must both keep them
+    step = make_dominant_token(make_prefill_step("pdom", 480, [4000], [4], 2 * g, 2, 128, 16, dt))
+    _check(step, f"dominant token {dt} g{g}")
 
 
 @pytest.mark.parametrize("scale", [0.0, -1.0 / 128 ** 0.5, 3.0])
