@@ -193,15 +193,14 @@ __global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillA
   }
   const int tile = rt - 1 - t_idx;
   const int kvh = (int)(G % Hkv);
-  // G / Hkv is a rank. With few sequences and few row tiles per group, the ranks follow the
+  // G / Hkv is a rank. With at most 64 sequences (one per lane) the ranks follow the
   // sequences' work, heaviest first, so that each XCD also runs its share longest first: lane
   // i weighs sequence i by its visible (row, token) pairs n (2T - n) and counts the sequences
   // ahead of it (heavier, or as heavy with a smaller index), which makes the ranks a
-  // permutation. With many row tiles per group the tiles themselves balance each XCD, and the
-  // rank is the sequence index.
+  // permutation. With more sequences the rank is the sequence index.
   const int rank = (int)(G / Hkv);
   int s = rank;
-  if (a.num_seqs <= 64 && rt <= 8) {  // uniform
+  if (a.num_seqs <= 64) {  // uniform
     const int ln = threadIdx.x & 63;
     float wv = -1.0f;
     if (ln < a.num_seqs) {
