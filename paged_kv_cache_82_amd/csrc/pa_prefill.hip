@@ -193,24 +193,28 @@ __global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillA
   }
   const int tile = rt - 1 - t_idx;
   const int kvh = (int)(G % Hkv);
+  // Extent of a sequence, clamped into the buffers the sizes describe.
+  const int Nq = a.num_q_tokens;
+  const int64_t cap64 = (int64_t)a.max_blocks_per_seq * BS;
+  const int cap = (int)(cap64 < (int64_t)a.max_context_len ? cap64 : (int64_t)a.max_context_len);
+  auto extent = [&](int i, int& qa, int& qb, int& t) {
+    qa = clampi(a.query_start[i], 0, Nq);
+    qb = clampi(a.query_start[i + 1], qa, Nq);
+    t = clampi(a.context_lens[i], 0, cap);
+  };
   // G / Hkv is a rank. With at most 64 sequences (one per lane) the ranks follow the
   // sequences' work, heaviest first, so that each XCD also runs its share longest first: lane
   // i weighs sequence i by its visible (row, token) pairs n (2T - n) and counts the sequences
   // ahead of it (heavier, or as heavy with a smaller index), which makes the ranks a
   // permutation. With more sequences the rank is the sequence index.
   const int rank = (int)(G / Hkv);
-  int s = rank;
+  int s = rank, q0, q1, T;
   if (a.num_seqs <= 64) {  // uniform
     const int ln = threadIdx.x & 63;
+    int qa = 0, qb = 0, Tr = 0;
     float wv = -1.0f;
     if (ln < a.num_seqs) {
-      const int Nqr = a.num_q_tokens;
-      const int qa = clampi(a.query_start[ln], 0, Nqr);
-      const int qb = clampi(a.query_start[ln + 1], qa, Nqr);
-      const int64_t capr64 = (int64_t)a.max_blocks_per_seq * BS;
-      const int capr =
-          (int)(capr64 < (int64_t)a.max_context_len ? capr64 : (int64_t)a.max_context_len);
-      const int Tr = clampi(a.context_lens[ln], 0, capr);
+      extent(ln, qa, qb, Tr);
       int nr = qb - qa;
       nr = nr < Tr ? nr : Tr;
       nr = nr < a.max_query_len ? nr : a.max_query_len;
@@ -224,15 +228,13 @@ __global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillA
     }
     const uint64_t hit = __builtin_amdgcn_ballot_w64(ln < a.num_seqs && ahead == rank);
     s = __builtin_ctzll(hit);
+    // the chosen sequence's extent as its lane loaded it: no second round trip to memory
+    q0 = __builtin_amdgcn_readlane(qa, s);
+    q1 = __builtin_amdgcn_readlane(qb, s);
+    T = __builtin_amdgcn_readlane(Tr, s);
+  } else {
+    extent(s, q0, q1, T);
   }
-
-  // Extent of the sequence, clamped into the buffers the sizes describe.
-  const int Nq = a.num_q_tokens;
-  const int q0 = clampi(a.query_start[s], 0, Nq);
-  const int q1 = clampi(a.query_start[s + 1], q0, Nq);
-  const int64_t cap64 = (int64_t)a.max_blocks_per_seq * BS;
-  const int cap = (int)(cap64 < (int64_t)a.max_context_len ? cap64 : (int64_t)a.max_context_len);
-  const int T = clampi(a.context_lens[s], 0, cap);
   int n = q1 - q0;
   n = n < T ? n : T;
   n = n < a.max_query_len ? n : a.max_query_len;
