@@ -104,17 +104,19 @@ __device__ __forceinline__ int fresh_lane() {
   return l;
 }
 
-// Maxima of scores without the NaN-quieting copies the compiler puts in front of fmaxf (two of
-// its six instructions per eight scores): v_max3_f32 takes three at a time. A NaN score can
-// only come from a NaN key or query element and makes that row's output NaN either way.
-__device__ __forceinline__ float max3f(float a, float b, float c) {
+// The largest of eight scores without the NaN-quieting copies the compiler puts in front of
+// fmaxf (two of its six instructions per eight scores): v_max3_f32 takes three at a time. One
+// asm block, so that the hazard padding the compiler adds around inline asm comes once, not
+// after each of the four instructions. A NaN score can only come from a NaN key or query
+// element and makes that row's output NaN either way.
+__device__ __forceinline__ float max8f(const f32x4& x, const f32x4& y) {
   float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-__device__ __forceinline__ float max2f(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  asm("v_max3_f32 %0, %1, %2, %3\n\t"
+      "v_max3_f32 %0, %0, %4, %5\n\t"
+      "v_max3_f32 %0, %0, %6, %7\n\t"
+      "v_max_f32 %0, %0, %8"
+      : "=&v"(r)
+      : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]));
   return r;
 }
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -146,7 +148,7 @@ __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
 
 // Three workgroups per CU (12 waves, 144 KB of LDS at d = 128): the kernel fits 168 VGPRs by
 // reading K and V from LDS half a head dimension at a time and recomputing the few
-// lane-derived values that rare paths need; three values spill, once per workgroup, outside
+// lane-derived values that rare paths need; two values spill, once per workgroup, outside
 // the stage loop.
 template <DT dt, int D, int BS, int NW, int NCT, int NBUF>
 __global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillArgs a) {
@@ -307,11 +309,13 @@ __global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillA
   // `ids` holds that id for stage 64*(st/64) + k (clamped to the workgroup's last block:
   // stages past it load stand-in rows that are masked later). The next 64 are loaded when the
   // first of them is issued and used at once: one wait for the loads in flight per 64 stages,
-  // and no load of `ids` is ever outstanding across stages.
+  // and no load of `ids` is ever outstanding across stages. Ids are clamped into the pool as
+  // they are loaded, 64 at a time, so a stage only scales its id.
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const int id_max = last_block_id(a.num_blocks);
   auto load_ids = [&](int chunk) {
     const int j = (KT * (64 * chunk + fresh_lane()) + RPW * w) / BS;
-    return bt[j < jlast ? j : jlast];  // jlast < max_blocks_per_seq since T <= cap
+    return clamp_id(bt[j < jlast ? j : jlast], id_max);  // jlast < max_blocks_per_seq: T <= cap
   };
   int ids = load_ids(0);
 
@@ -339,9 +343,10 @@ __global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillA
   // 1 KB = RPL whole rows. Lane L carries physical chunk L % CPR of row L / CPR and fetches
   // the logical chunk the swizzle maps there. No registers hold data in flight, so NBUF - 1
   // stages can be in flight while one is consumed.
-  const char* kbase = (const char*)a.k_cache;
-  const char* vbase = (const char*)a.v_cache;
   const int64_t tile_bytes = (int64_t)BS * RB;
+  const uint64_t blk_bytes = (uint64_t)Hkv * tile_bytes;  // one physical block, all KV heads
+  const char* kbase = (const char*)a.k_cache + kvh * tile_bytes;  // this KV head's tile of block 0
+  const char* vbase = (const char*)a.v_cache + kvh * tile_bytes;
   const int row_in_load = lane / CPR;
   const int pchunk = lane % CPR;
   uint32_t ko[WLW], vo[WLW];  // byte offsets in the block's tile of the chunks this lane moves
@@ -356,8 +361,7 @@ __global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillA
       ids = load_ids(st >> 6);
       __builtin_amdgcn_s_waitcnt(0x0F70 & ~0x0F);  // vmcnt(0): ids is never pending past here
     }
-    const int32_t id = __builtin_amdgcn_readlane(ids, st & 63);
-    const int64_t t = (clamp_block(id, a.num_blocks) * Hkv + kvh) * tile_bytes;
+    const uint64_t t = (uint64_t)(uint32_t)__builtin_amdgcn_readlane(ids, st & 63) * blk_bytes;
     const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kbase + t, (int)tile_bytes);
     const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vbase + t, (int)tile_bytes);
 #pragma unroll
@@ -407,7 +411,7 @@ __global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillA
         for (int j = 0; j < KH; ++j)
           kf[u][j] = *reinterpret_cast<const u32x4*>(&lds[buf][0][koff(16 * u + hh, 4 * (h * KH + j) + gq)]);
       // The MFMA blocks run at raised wave priority, so that a wave holding matrix work issues
-      // it ahead of the other wave's vector work on the same SIMD.
+      // it ahead of the other waves' vector work on the same SIMD.
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int j = 0; j < KH; ++j)
@@ -471,10 +475,7 @@ __global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillA
     bool raise = false;
 #pragma unroll
     for (int c = 0; c < NCT; ++c) {
-      const float r0 = max3f(sacc[c][0][0], sacc[c][0][1], sacc[c][0][2]);
-      const float r1 = max3f(r0, sacc[c][0][3], sacc[c][1][0]);
-      const float r2 = max3f(r1, sacc[c][1][1], sacc[c][1][2]);
-      lr[c] = max2f(r2, sacc[c][1][3]);
+      lr[c] = max8f(sacc[c][0], sacc[c][1]);
       raise = raise || (lr[c] > thr[c]);
     }
     if (__builtin_amdgcn_ballot_w64(raise)) {  // uniform; rare once the maxima settle
