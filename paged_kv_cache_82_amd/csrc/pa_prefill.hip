@@ -148,7 +148,7 @@ __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
 
 // Three workgroups per CU (12 waves, 144 KB of LDS at d = 128): the kernel fits 168 VGPRs by
 // reading K and V from LDS half a head dimension at a time and recomputing the few
-// lane-derived values that rare paths need; two values spill, once per workgroup, outside
+// lane-derived values that rare paths need; three values spill, once per workgroup, outside
 // the stage loop.
 template <DT dt, int D, int BS, int NW, int NCT, int NBUF>
 __global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillArgs a) {
