@@ -392,7 +392,7 @@ __global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillA
   // workgroup's last position (stand-in or unused tail rows, possibly NaN); then hidden scores
   // are set to -inf and V rows past the workgroup's last position to 0, both by select.
   // Otherwise every token is visible to every row and no score is tested.
-  auto consume = [&](int tau0, auto bufc, bool mask) {
+  auto consume = [&](int tau0, auto bufc, bool mask, bool tail) {
     constexpr int buf = decltype(bufc)::value;
     // S^T = K Q^T for every column tile: 2*NCT independent accumulation chains. K comes from
     // LDS in two halves of the head dimension, so that only half of it is held at a time.
@@ -439,7 +439,7 @@ __global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillA
       lds_read_vt<buf * 2 * TILE, buf * 2 * TILE + 16 * RB>(tv, vah);
 #pragma unroll
       for (int mt = 0; mt < MH; ++mt) vw[mt] = u32x4{tv[mt][0][0], tv[mt][0][1], tv[mt][1][0], tv[mt][1][1]};
-      if (tau0 + KT - 1 > p_hi_wg) {  // uniform: V of tokens past the last position is 0
+      if (tail && tau0 + KT - 1 > p_hi_wg) {  // uniform: V of tokens past the last position is 0
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int t0 = tau0 + 16 * u + 4 * (fresh_lane() >> 4);  // token of element 4u
@@ -529,24 +529,47 @@ __global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillA
   const int prolog = nstages < NBUF - 1 ? nstages : NBUF - 1;
   for (int st = 0; st < prolog; ++st) issue_stage(st, st);
 
-  // Stages are unrolled NBUF at a time so that every LDS buffer offset is a constant.
-  for (int st0 = 0; st0 < nstages; st0 += NBUF) {
+  // One stage: wait for its loads, then a bare barrier (every wave's loads of stage st have
+  // landed and stage st-1 is consumed; a fence here would also wait for the later stages'
+  // loads still in flight; the empty asm keeps the compiler from moving LDS accesses across
+  // it), then the loads of stage st + NBUF - 1 into the buffer stage st - 1 used.
+  auto enter_stage = [&](int st, int later, auto bc, bool issue) {
+    constexpr int b = decltype(bc)::value;
+    wait_stage(later);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (issue) issue_stage(st + NBUF - 1, (b + NBUF - 1) % NBUF);
+  };
+
+  // Leading stages in bulk: every row of the workgroup sees all their tokens (the first row
+  // sits at position t_lo_wg), and a later stage remains to be loaded. No test for the causal
+  // mask, the tail or the end of the loop is needed there; nbulk is a multiple of NBUF and the
+  // same for every wave.
+  const int t_lo_wg = base_pos + W0 / g;
+  int nbulk = (t_lo_wg + 1) / KT;  // stages ending at or before position t_lo_wg
+  nbulk = nbulk < nstages - (NBUF - 1) ? nbulk : nstages - (NBUF - 1);
+  nbulk = nbulk > 0 ? nbulk / NBUF * NBUF : 0;
+  int st0 = 0;
+  for (; st0 < nbulk; st0 += NBUF) {
+    static_for<NBUF>([&](auto bc) {
+      const int st = st0 + decltype(bc)::value;
+      enter_stage(st, NBUF - 2, bc, true);
+      consume(st * KT, bc, false, false);
+    });
+  }
+  // The remaining stages, with every test. Stages are unrolled NBUF at a time so that every
+  // LDS buffer offset is a constant.
+  for (; st0 < nstages; st0 += NBUF) {
     static_for<NBUF>([&](auto bc) {
       constexpr int b = decltype(bc)::value;
       const int st = st0 + b;  // st % NBUF == b
       if (st >= nstages) return;  // uniform
       const int later = (nstages - 1 - st) < (NBUF - 2) ? (nstages - 1 - st) : (NBUF - 2);
-      wait_stage(later);
-      // Every wave's loads of stage st have landed and stage st-1 is consumed. A bare barrier:
-      // a fence here would also wait for the later stages' loads still in flight. The empty
-      // asm keeps the compiler from moving LDS accesses across it.
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      if (st + NBUF - 1 < nstages) issue_stage(st + NBUF - 1, (b + NBUF - 1) % NBUF);
+      enter_stage(st, later, bc, st + NBUF - 1 < nstages);
       const int tau0 = st * KT;
       if (tau0 > p_hi_w) return;  // uniform: every tile of this wave is done
-      consume(tau0, bc, tau0 + KT - 1 > t_lo_w);  // t_lo_w is -1 when a tile is empty
+      consume(tau0, bc, tau0 + KT - 1 > t_lo_w, true);  // t_lo_w is -1 when a tile is empty
     });
   }
 
