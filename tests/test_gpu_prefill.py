@@ -72,6 +72,17 @@ def test_prefill_long_context_rotates_block_ids(dt):
     _check(step, f"long {dt}")
 
 
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_prefill_bulk_loop_boundaries(dt):
+    # prefixes of 0 .. 700 tokens in steps that move the end of the leading fully visible
+    # stages (whole 32-token stages before a workgroup's first row, rounded down to the stage
+    # unroll) through every stage and buffer phase, for chunks of one and of several row tiles
+    T = [p + n for p in range(0, 701, 37) for n in (48, 200)]
+    n = [n for p in range(0, 701, 37) for n in (48, 200)]
+    step = make_prefill_step("pbulk", 475, T, n, 4, 4, 128, 16, dt)
+    _check(step, f"bulk boundaries {dt}")
+
+
 def test_prefill_single_token_matches_decode():
     # n = 1 for every sequence is a decode step: both kernels against the oracle, and each other
     lengths = [1, 7, 100, 513, 1500]
