@@ -3,13 +3,15 @@
   python rocprof_summary.py trace  <kernel_stats.csv> <out.txt> --command "<command>"
   python rocprof_summary.py pmc    decode|prefill <workload> <out.txt> --fetch <csv> --write <csv>
                                    --copy-fetch <csv> --copy-write <csv> --command "<command>"
+  python rocprof_summary.py sq     <kernel-needle> <out.txt> --passes <csv> [<csv> ...] --command "<command>"
 
 `trace` keeps the kernel table (calls, average/min/max duration) of a --kernel-trace --stats
 run. `pmc` turns FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the decode or prefill kernel into HBM
 bytes per launch, each scaled by what the same counter reads for the plain copy kernel
 (pa_copy_blocks moving 4096 blocks of 256 KiB: 2 GiB read and 2 GiB written per launch), and
 records the hash of that kernel's sources so bench.py only reports the figure while those
-sources are unchanged.
+sources are unchanged. `sq` averages the SQ_* (and GRBM_*) counters of one kernel per dispatch
+over several --pmc passes and derives where its waves spend their cycles.
 """
 from __future__ import annotations
 
@@ -90,6 +92,43 @@ def do_pmc(args) -> str:
     return "\n".join(lines) + "\n"
 
 
+def do_sq(args) -> str:
+    vals = collections.defaultdict(list)
+    names = set()
+    for path in args.passes:
+        for r in csv.DictReader(open(path)):
+            if args.needle in r["Kernel_Name"]:
+                names.add(r["Kernel_Name"])
+                vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    if len(names) != 1:
+        raise SystemExit(f"expected one kernel matching {args.needle!r}, found {sorted(names)}")
+    v = {k: sum(x) / len(x) for k, x in vals.items()}
+    lines = [f"command: {args.command}", f"kernel: {names.pop()}",
+             "counter averages per dispatch (summed over the units that report them):"]
+    lines += [f"  {k}: {v[k]:.6g}" for k in sorted(v)]
+    wc = v.get("SQ_WAVE_CYCLES")
+    if wc:
+        lines.append("share of wave cycles:")
+        for k, label in (("SQ_ACTIVE_INST_ANY", "issuing any instruction"),
+                         ("SQ_ACTIVE_INST_VALU", "issuing vector ALU"),
+                         ("SQ_ACTIVE_INST_SCA", "issuing scalar"),
+                         ("SQ_ACTIVE_INST_LDS", "issuing LDS"),
+                         ("SQ_WAIT_INST_ANY", "waiting to issue (dependency or arbitration)"),
+                         ("SQ_WAIT_ANY", "waiting (s_waitcnt, barrier)")):
+            if k in v:
+                lines.append(f"  {label}: {v[k] / wc:.3f}")
+    if "SQ_INSTS_MFMA" in v and v["SQ_INSTS_MFMA"]:
+        m = v["SQ_INSTS_MFMA"]
+        lines.append("instructions per MFMA:")
+        for k in ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_SALU", "SQ_INSTS_LDS"):
+            if k in v:
+                lines.append(f"  {k}: {v[k] / m:.3f}")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in v and "SQ_VALU_MFMA_COEXEC_CYCLES" in v:
+        lines.append("vector ALU co-executing with MFMA, share of MFMA-busy cycles: "
+                     f"{v['SQ_VALU_MFMA_COEXEC_CYCLES'] / v['SQ_VALU_MFMA_BUSY_CYCLES']:.3f}")
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -103,8 +142,13 @@ def main():
     p.add_argument("out")
     for k in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--command"):
         p.add_argument(k, required=True)
+    q = sub.add_parser("sq")
+    q.add_argument("needle")
+    q.add_argument("out")
+    q.add_argument("--passes", nargs="+", required=True)
+    q.add_argument("--command", required=True)
     args = ap.parse_args()
-    text = do_trace(args) if args.mode == "trace" else do_pmc(args)
+    text = {"trace": do_trace, "pmc": do_pmc, "sq": do_sq}[args.mode](args)
     with open(args.out, "w") as f:
         f.write(text)
     print(text)
