@@ -148,8 +148,8 @@ __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
 
 // Three workgroups per CU (12 waves, 144 KB of LDS at d = 128): the kernel fits 168 VGPRs by
 // reading K and V from LDS half a head dimension at a time and recomputing the few
-// lane-derived values that rare paths need; three values spill, once per workgroup, outside
-// the stage loop.
+// lane-derived values that rare paths need; five values spill, each stored and reloaded once
+// per workgroup, outside both stage loops.
 template <DT dt, int D, int BS, int NW, int NCT, int NBUF>
 __global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillArgs a) {
   static_assert(dt != DT::F32, "MFMA path takes 16-bit inputs");
