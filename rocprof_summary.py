@@ -123,7 +123,7 @@ def do_sq(args) -> str:
         for k in ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_SALU", "SQ_INSTS_LDS"):
             if k in v:
                 lines.append(f"  {k}: {v[k] / m:.3f}")
-    if "SQ_VALU_MFMA_BUSY_CYCLES" in v and "SQ_VALU_MFMA_COEXEC_CYCLES" in v:
+    if v.get("SQ_VALU_MFMA_BUSY_CYCLES") and "SQ_VALU_MFMA_COEXEC_CYCLES" in v:
         lines.append("vector ALU co-executing with MFMA, share of MFMA-busy cycles: "
                      f"{v['SQ_VALU_MFMA_COEXEC_CYCLES'] / v['SQ_VALU_MFMA_BUSY_CYCLES']:.3f}")
     return "\n".join(lines) + "\n"

@@ -94,6 +94,13 @@ def test_sq_summary(tmp_path):
     assert "waiting to issue (dependency or arbitration): 0.450" in text
     assert "SQ_INSTS_VALU: 3.250" in text and "SQ_INSTS_SALU: 0.870" in text
     assert "share of MFMA-busy cycles: 0.250" in text
+    # a kernel without MFMA work gets no per-MFMA or co-execution lines
+    p3 = tmp_path / "p3.csv"
+    _write_counters(p3, k, {"SQ_WAVE_CYCLES": 1000, "SQ_INSTS_MFMA": 0,
+                            "SQ_VALU_MFMA_BUSY_CYCLES": 0, "SQ_VALU_MFMA_COEXEC_CYCLES": 0})
+    A.passes = [str(p3)]
+    text = rocprof_summary.do_sq(A)
+    assert "per MFMA" not in text and "co-executing" not in text
     A.needle = "no_such_kernel"
     with pytest.raises(SystemExit):
         rocprof_summary.do_sq(A)
