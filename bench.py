@@ -356,13 +356,14 @@ def run_prefill(args):
             one_step(i)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+    n_roof = max(args.steps, 100)  # as for decode: enough launches for a stable average
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(args.steps):
+    for i in range(n_roof):
         attend(i)
     e1.record()
     torch.cuda.synchronize()
-    att_s = e0.elapsed_time(e1) / 1e3 / args.steps
+    att_s = e0.elapsed_time(e1) / 1e3 / n_roof
     fl = prefill_flops(step)
     n_new = step.num_q_tokens
     res = {
@@ -551,6 +552,9 @@ def main():
                     help="untimed seconds of steps before the warmup steps (GPU clock ramp)")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time the default (13B-shape) workload only, not the other decode "
+                         "workloads after it")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of replays of a captured step graph")
     ap.add_argument("--placement", default="random", choices=["random", "contiguous"],
@@ -564,9 +568,6 @@ def main():
               "(sequences and KV heads would shard with no exchange; see the design notes).",
               file=sys.stderr)
         sys.exit(2)
-
-    import numpy as np
-    import torch
 
     import paged_kv_cache_82_amd as pa
 
@@ -584,8 +585,50 @@ def main():
     if args.workload.startswith("prefill"):
         return run_prefill(args)
 
+    res = measure_decode(args.workload, args, cpu=not args.no_cpu_baseline)
+    if args.workload == "mha13b" and not args.no_extra:
+        # The other decode workloads in the same process, each under its own key: the GQA batch
+        # is the second bandwidth target; long-context and shared-prefix run the split-K merge
+        # and shared blocks. Same step, graph replay and event timing; no CPU baseline.
+        res["workloads"] = {"mha13b": summary(res)}
+        for name in EXTRA_WORKLOADS:
+            t0 = time.perf_counter()
+            res["workloads"][name] = summary(measure_decode(name, args, cpu=False))
+            print(f"bench: {name} measured in {time.perf_counter() - t0:.1f} s", file=sys.stderr,
+                  flush=True)
+    print(json.dumps(res))
+
+
+EXTRA_WORKLOADS = ("gqa", "long", "shared")
+
+
+def summary(res: dict) -> dict:
+    """The per-workload figures of one decode measurement."""
+    r = res["roofline"]
+    out = {"workload": res["config"]["workload"], "dtype": res["dtype"],
+           "value": res["value"], "unit": res["unit"], "ms_per_step": res["ms_per_step"],
+           "seq_tokens_per_s": res["seq_tokens_per_s"],
+           "decode_seq_tokens_per_s": res["decode_seq_tokens_per_s"],
+           "roofline": {k: r[k] for k in ("kernel", "bound", "achieved", "peak", "unit", "frac",
+                                          "traffic", "algorithmic_bytes_per_launch",
+                                          "avg_launch_us")}}
+    for k in ("logical_bytes_per_launch", "logical_GB_per_s"):
+        if k in r:
+            out["roofline"][k] = r[k]
+    return out
+
+
+def measure_decode(workload: str, args, cpu: bool) -> dict:
+    """One decode workload: inputs generated and uploaded, W warmup steps, K timed steps (graph
+    replay unless --no-graph), then K back-to-back decode launches between HIP events on the
+    launch stream for the roofline. Frees its device memory before returning."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_82_amd as pa
+
     t_gen = time.perf_counter()
-    step = make_workload(args.workload, poison=False, placement=args.placement)
+    step = make_workload(workload, poison=False, placement=args.placement)
     t_gen = time.perf_counter() - t_gen
     dev = torch.device("cuda")
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[step.dtype]
@@ -669,21 +712,24 @@ def main():
     # Part 2: K decode launches back to back (rotating pool copies) between two events on the
     # launch stream; the average is the decode kernel's launch duration for the roofline (an
     # event right before each launch would also time the dispatch gap after the KV write).
+    # At least 100 launches: with the driver's 20 steps a short batch (7 ms for the GQA step)
+    # read a few percent slow.
+    n_roof = max(args.steps, 100)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(args.steps):
+    for i in range(n_roof):
         kc, vc = pools[i % ncopy]
         pa.pa_decode(out, q, kc, vc, bt, cl, scale, maxT, ws, P)
     e1.record()
     torch.cuda.synchronize()
-    dec_s = e0.elapsed_time(e1) / 1e3 / args.steps
+    dec_s = e0.elapsed_time(e1) / 1e3 / n_roof
 
     nb = algorithmic_bytes(step)
     ms_per_step = wall / args.steps * 1e3
     step_bytes = nb["decode"] + nb["write"]
     value = step_bytes / (wall / args.steps) / 1e9
     achieved = nb["decode"] / dec_s / 1e9
-    traffic = measured_traffic("decode", args.workload)
+    traffic = measured_traffic("decode", workload)
     res = {
         "metric": "paged decode attention: achieved HBM GB/s (% of peak) + seq-tokens/s",
         "value": round(value, 2),
@@ -699,7 +745,7 @@ def main():
         "accumulate": "f32",
         "data": "synthetic (seeded N(0,1) K/V/q; lengths and placement as described)",
         "config": {
-            "workload": WORKLOADS[args.workload][1],
+            "workload": WORKLOADS[workload][1],
             "num_seqs": step.num_seqs, "num_q_heads": step.num_q_heads,
             "num_kv_heads": step.num_kv_heads, "head_dim": step.head_dim,
             "block_size": step.block_size, "num_blocks": step.num_blocks,
@@ -735,9 +781,14 @@ def main():
         # sequence's tokens, shared prefixes once per sequence) beside them
         res["roofline"]["logical_bytes_per_launch"] = nb["decode_logical"]
         res["roofline"]["logical_GB_per_s"] = round(nb["decode_logical"] / dec_s / 1e9, 2)
-    if not args.no_cpu_baseline:
+    if cpu:
         res["cpu_baseline"] = cpu_baseline(step)
-    print(json.dumps(res))
+    del pools, kc0, vc0, q, bt, cl, copies, writes, out, ws
+    if not args.no_graph:
+        del graph
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":

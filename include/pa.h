@@ -30,9 +30,11 @@
  * Query head h reads KV head h / (num_q_heads / num_kv_heads) (contiguous groups).
  *
  * Ownership and execution: every pointer except the return of pa_status_string is a DEVICE
- * pointer owned by the caller. The library allocates no memory and keeps no state between
- * calls. Each call validates its scalar arguments and pointer alignment on the host, enqueues
- * its kernel(s) on `stream` (a hipStream_t; NULL = the null stream) and returns without waiting
+ * pointer owned by the caller. The library allocates no memory at call time and keeps no state
+ * between calls, with one stated exception: the process-wide kernel choice of
+ * pa_set_decode_kernel.
+ * Each call validates its scalar arguments and pointer alignment on the host, enqueues its
+ * kernel(s) on `stream` (a hipStream_t; NULL = the null stream) and returns without waiting
  * for completion. q, k_cache, v_cache, k_new and v_new must be 16-byte aligned; the workspace
  * 256-byte aligned; index arrays 4-byte aligned (PA_ERR_INVALID_ARG otherwise).
  *
@@ -48,8 +50,7 @@
  * PA_ERR_WORKSPACE for a workspace smaller than pa_decode_workspace_size; PA_ERR_HIP when the
  * HIP runtime reports an error at launch.
  *
- * Supported shapes: dtype f32, f16, bf16; head_dim 64 or 128;
- * block_size 8, 16 or 32.
+ * Supported shapes: dtype f32, f16, bf16; head_dim 64 or 128; block_size 8, 16, 32 or 64.
  */
 #ifndef PA_H
 #define PA_H
@@ -62,6 +63,9 @@ extern "C" {
 #endif
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* Decode kernel choice (pa_set_decode_kernel). */
+typedef enum { PA_DECODE_AUTO = 0, PA_DECODE_VALU = 1, PA_DECODE_MFMA = 2 } pa_decode_kernel;
 
 typedef enum {
   PA_OK = 0,
@@ -95,7 +99,7 @@ pa_status pa_write_kv(void *k_cache, void *v_cache, const void *k_new, const voi
  * output, fp32) of every (sequence, query head).
  * partition_tokens: 0 = let the library choose (the same choice pa_decode makes for the same
  * arguments); > 0 must be a multiple of 32 and at most 64*4*block_size tokens (fp32 and
- * single-head groups) or 8192 tokens (grouped heads).
+ * single-head groups; 4096 for block_size 64) or 8192 tokens (grouped heads).
  * Returns 0 when no workspace is needed (every sequence fits one partition) and for invalid
  * sizes.
  */
@@ -132,6 +136,18 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v
                     size_t workspace_bytes, pa_dtype dt, void *stream);
 
 /*
+ * pa_set_decode_kernel — which decode kernel pa_decode and pa_decode_workspace_size use
+ * from now on, process-wide. PA_DECODE_AUTO (the default): the
+ * MFMA kernel for f16/bf16 with at least two query heads per KV head, the vector-ALU kernel
+ * otherwise. PA_DECODE_VALU / PA_DECODE_MFMA force one kernel (the MFMA kernel takes no f32:
+ * PA_ERR_UNSUPPORTED then). Both kernels compute the same attention; the choice moves only the
+ * rounding of the intermediate weights. Change it only between calls, not between a
+ * pa_decode_workspace_size call and the pa_decode it sizes. PA_ERR_INVALID_ARG for any other
+ * value.
+ */
+pa_status pa_set_decode_kernel(pa_decode_kernel kernel);
+
+/*
  * pa_prefill — causal multi-query (prefill / chunked-prefill) attention over the same block
  * pool and tables.
  * [PA-summary] "The PagedAttention algorithm": the kernel walks the block table for each query
@@ -151,7 +167,7 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v
  * max_query_len: host-known bound on every n_s; max_context_len: on every T_s (they size the
  * grid; no device read on the host). n_s > T_s or n_s > max_query_len is a caller error: only
  * min(n_s, T_s, max_query_len) rows are computed.
- * Supported: dt f32, f16 or bf16, head_dim 64 or 128, block_size 8, 16 or 32; for f32,
+ * Supported: dt f32, f16 or bf16, head_dim 64 or 128, block_size 8, 16, 32 or 64; for f32,
  * num_q_tokens * num_q_heads <= 2^31 - 1 (PA_ERR_INVALID_ARG otherwise). No workspace. Device
  * indices are clamped as for pa_decode.
  */

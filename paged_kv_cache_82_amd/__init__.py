@@ -4,10 +4,10 @@ The compute lives in libpa.so (hand-written HIP kernels behind the C ABI in incl
 this package is its thin Python binding. Importing it never falls back to any other code
 path: if the library is missing, calls raise.
 """
-from ._binding import (PAError, lib_path, load, pa_copy_blocks, pa_decode,
-                       pa_decode_workspace_size, pa_prefill, pa_status_string, pa_swap_blocks,
-                       pa_write_kv)
+from ._binding import (DECODE_KERNELS, PAError, lib_path, load, pa_copy_blocks, pa_decode,
+                       pa_decode_workspace_size, pa_prefill, pa_set_decode_kernel,
+                       pa_status_string, pa_swap_blocks, pa_write_kv)
 
-__all__ = ["PAError", "lib_path", "load", "pa_copy_blocks", "pa_decode",
-           "pa_decode_workspace_size", "pa_prefill", "pa_status_string", "pa_swap_blocks",
-           "pa_write_kv"]
+__all__ = ["DECODE_KERNELS", "PAError", "lib_path", "load", "pa_copy_blocks",
+           "pa_decode", "pa_decode_workspace_size", "pa_prefill",
+           "pa_set_decode_kernel", "pa_status_string", "pa_swap_blocks", "pa_write_kv"]

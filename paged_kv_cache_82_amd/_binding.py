@@ -55,6 +55,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.pa_decode_workspace_size.restype = SZ
         lib.pa_decode.argtypes = [P, P, P, P, P, P, F, I, I, I, I, I, I, I64, I, I, P, SZ, I, P]
         lib.pa_decode.restype = I
+        lib.pa_set_decode_kernel.argtypes = [I]
+        lib.pa_set_decode_kernel.restype = I
         lib.pa_prefill.argtypes = [P, P, P, P, P, P, P, F, I, I, I, I, I, I, I, I64, I, I, I, P]
         lib.pa_prefill.restype = I
         lib.pa_copy_blocks.argtypes = [P, P, P, I, I, I, I, I64, I, P]
@@ -128,6 +130,14 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_c
         _ptr(context_lens), float(scale), S, Hq, Hkv, d, B, block_tables.shape[1], N,
         int(max_context_len), int(partition_tokens), _ptr(workspace), ws_bytes,
         _dtype_code(q), _stream(stream)))
+
+
+DECODE_KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
+
+
+def pa_set_decode_kernel(kernel: str) -> None:
+    """Process-wide decode kernel choice: "auto" (default), "valu" or "mfma"."""
+    _check("pa_set_decode_kernel", load().pa_set_decode_kernel(DECODE_KERNELS[kernel]))
 
 
 def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,

@@ -3,6 +3,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "pa.h"
 #include "pa_internal.h"
 
@@ -24,17 +26,18 @@ int64_t pool_elems(int64_t num_blocks, int heads, int block_size, int head_dim) 
   return num_blocks * per_block;
 }
 
-// Kernel path: grouped-query MFMA kernel for 16-bit inputs with at least two query heads per
-// KV head, the VALU kernel otherwise. PA_DECODE_PATH=valu|mfma overrides (tests use it to
-// exercise both kernels on one input).
+// Decode kernel choice, process-wide (pa_set_decode_kernel): PA_DECODE_AUTO picks the grouped-
+// query MFMA kernel for 16-bit inputs with at least two query heads per KV head and the VALU
+// kernel otherwise; the other values force one kernel for every later call.
+std::atomic<int> g_decode_kernel{PA_DECODE_AUTO};
+
 bool choose_path(pa_dtype dt, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                  DecodePath* path) {
   const int g = num_q_heads / num_kv_heads;
   DecodePath p = (dt != PA_F32 && g >= 2) ? DecodePath::Mfma : DecodePath::Valu;
-  if (const char* env = getenv("PA_DECODE_PATH")) {
-    if (strcmp(env, "valu") == 0) p = DecodePath::Valu;
-    else if (strcmp(env, "mfma") == 0) p = DecodePath::Mfma;
-  }
+  const int forced = g_decode_kernel.load(std::memory_order_relaxed);
+  if (forced == PA_DECODE_VALU) p = DecodePath::Valu;
+  else if (forced == PA_DECODE_MFMA) p = DecodePath::Mfma;
   *path = p;
   return pa::decode_supported(p, (int)dt, head_dim, block_size);
 }
@@ -68,6 +71,68 @@ int parts_for(int max_context_len, int P) {
 }
 
 pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+// pa_decode with the split-K partials in `workspace` (the caller's buffer).
+pa_status decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                      int max_context_len, int partition_tokens, void* workspace,
+                      size_t workspace_bytes, pa_dtype dt, void* stream) {
+  if (!valid_dtype(dt)) return PA_ERR_INVALID_ARG;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || max_blocks_per_seq < 0 || num_blocks <= 0 || max_context_len < 0 ||
+      partition_tokens < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads) return PA_ERR_INVALID_ARG;
+  if (partition_tokens % 32) return PA_ERR_INVALID_ARG;
+  if (pool_elems(num_blocks, num_kv_heads, block_size, head_dim) < 0) return PA_ERR_INVALID_ARG;
+  if (num_seqs > 65535 || num_q_heads > 65535) return PA_ERR_INVALID_ARG;  // grid limits
+  DecodePath path;
+  if (!choose_path(dt, num_q_heads, num_kv_heads, head_dim, block_size, &path))
+    return PA_ERR_UNSUPPORTED;
+  const int cap = pa::max_partition_tokens(path, block_size);
+  if (partition_tokens > cap) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(out, elem_bytes(dt)) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return PA_ERR_INVALID_ARG;
+
+  const int P = choose_partition(num_seqs,
+                                 pa::decode_units_per_seq(path, num_q_heads, num_kv_heads),
+                                 max_context_len, cap, partition_tokens);
+  const int max_parts = parts_for(max_context_len, P);
+  const pa::WorkspaceLayout L =
+      pa::workspace_layout(num_seqs, num_q_heads, head_dim, max_parts);
+  if (workspace_bytes < L.total || (L.total > 0 && !workspace)) return PA_ERR_WORKSPACE;
+  if (L.total > 0 && !aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
+
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.partition_tokens = P;
+  a.max_parts = max_parts;
+  char* ws = (char*)workspace;
+  a.part_m = L.total ? (float*)(ws + L.m_off) : nullptr;
+  a.part_l = L.total ? (float*)(ws + L.l_off) : nullptr;
+  a.part_o = L.total ? (float*)(ws + L.o_off) : nullptr;
+  return from_hip(pa::launch_decode(path, (int)dt, head_dim, block_size, a, (hipStream_t)stream));
+}
+
 
 }  // namespace
 
@@ -129,58 +194,17 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     int block_size, int max_blocks_per_seq, int64_t num_blocks,
                     int max_context_len, int partition_tokens, void* workspace,
                     size_t workspace_bytes, pa_dtype dt, void* stream) {
-  if (!valid_dtype(dt)) return PA_ERR_INVALID_ARG;
-  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-      block_size <= 0 || max_blocks_per_seq < 0 || num_blocks <= 0 || max_context_len < 0 ||
-      partition_tokens < 0)
-    return PA_ERR_INVALID_ARG;
-  if (num_q_heads % num_kv_heads) return PA_ERR_INVALID_ARG;
-  if (partition_tokens % 32) return PA_ERR_INVALID_ARG;
-  if (pool_elems(num_blocks, num_kv_heads, block_size, head_dim) < 0) return PA_ERR_INVALID_ARG;
-  if (num_seqs > 65535 || num_q_heads > 65535) return PA_ERR_INVALID_ARG;  // grid limits
-  DecodePath path;
-  if (!choose_path(dt, num_q_heads, num_kv_heads, head_dim, block_size, &path))
-    return PA_ERR_UNSUPPORTED;
-  const int cap = pa::max_partition_tokens(path, block_size);
-  if (partition_tokens > cap) return PA_ERR_INVALID_ARG;
-  if (num_seqs == 0) return PA_OK;
-  if (max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
-    return PA_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-      !aligned(out, elem_bytes(dt)) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
-    return PA_ERR_INVALID_ARG;
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                     num_blocks, max_context_len, partition_tokens, workspace, workspace_bytes,
+                     dt, stream);
+}
 
-  const int P = choose_partition(num_seqs,
-                                 pa::decode_units_per_seq(path, num_q_heads, num_kv_heads),
-                                 max_context_len, cap, partition_tokens);
-  const int max_parts = parts_for(max_context_len, P);
-  const pa::WorkspaceLayout L =
-      pa::workspace_layout(num_seqs, num_q_heads, head_dim, max_parts);
-  if (workspace_bytes < L.total || (L.total > 0 && !workspace)) return PA_ERR_WORKSPACE;
-  if (L.total > 0 && !aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
-
-  pa::DecodeArgs a{};
-  a.out = out;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.num_blocks = num_blocks;
-  a.max_context_len = max_context_len;
-  a.partition_tokens = P;
-  a.max_parts = max_parts;
-  char* ws = (char*)workspace;
-  a.part_m = L.total ? (float*)(ws + L.m_off) : nullptr;
-  a.part_l = L.total ? (float*)(ws + L.l_off) : nullptr;
-  a.part_o = L.total ? (float*)(ws + L.o_off) : nullptr;
-  return from_hip(pa::launch_decode(path, (int)dt, head_dim, block_size, a, (hipStream_t)stream));
+pa_status pa_set_decode_kernel(pa_decode_kernel kernel) {
+  if (kernel != PA_DECODE_AUTO && kernel != PA_DECODE_VALU && kernel != PA_DECODE_MFMA)
+    return PA_ERR_INVALID_ARG;
+  g_decode_kernel.store((int)kernel, std::memory_order_relaxed);
+  return PA_OK;
 }
 
 pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -133,27 +133,35 @@ __global__ __launch_bounds__(D) void merge_partitions_kernel(const DecodeArgs a)
 
 // ---- VALU kernel ------------------------------------------------------------------------
 
-template <DT dt, int D, int BS, int NW>
+// Tokens a wave of the VALU kernels takes at once (a "unit"): the whole block up to 32 tokens;
+// 16 tokens of a larger block, so that a unit's registers stay those of a 16-token block.
+template <int BS>
+constexpr int valu_unit_tokens() {
+  return BS > 32 ? 16 : BS;
+}
+
+template <DT dt, int D, int SB, int NW>
 struct ValuCfg {
   static constexpr int E = Elem<dt>::bytes;
   static constexpr int VEC = 16 / E;    // elements per 16-byte chunk
   static constexpr int R = D / VEC;     // lanes that share one token row
   static constexpr int TPI = 64 / R;    // token rows covered by one wave-wide load
-  static constexpr int NL = BS / TPI;   // loads per block per tensor
+  static constexpr int NL = SB / TPI;   // loads per unit per tensor
   static constexpr int NT = NW * 64;
   static_assert(64 % R == 0 && R >= 1, "row must split evenly over the wave");
-  static_assert(BS % TPI == 0, "block must cover whole wave loads");
+  static_assert(SB % TPI == 0, "a unit must cover whole wave loads");
   static_assert(D <= NT, "one thread per head dimension in the merge");
 };
 
-// One block of one wave: scores, running-state update and p.V accumulation. Lane (c, r) holds
-// head dimensions c*VEC.. of token rows i*TPI + r. TAIL masks tokens at or beyond t_end.
-template <DT dt, int D, int BS, int NW, bool TAIL>
-__device__ __forceinline__ void valu_block(const float (&qf)[ValuCfg<dt, D, BS, NW>::VEC],
+// One unit (SB tokens) of one wave: scores, running-state update and p.V accumulation. Lane
+// (c, r) holds head dimensions c*VEC.. of token rows i*TPI + r. TAIL masks tokens at or beyond
+// t_end.
+template <DT dt, int D, int SB, int NW, bool TAIL>
+__device__ __forceinline__ void valu_block(const float (&qf)[ValuCfg<dt, D, SB, NW>::VEC],
                                            const u32x4* kr, const u32x4* vr, int tok0,
                                            int t_end, int r, float& m, float& l,
-                                           float (&o)[ValuCfg<dt, D, BS, NW>::VEC]) {
-  using C = ValuCfg<dt, D, BS, NW>;
+                                           float (&o)[ValuCfg<dt, D, SB, NW>::VEC]) {
+  using C = ValuCfg<dt, D, SB, NW>;
   float sc[C::NL];
 #pragma unroll
   for (int i = 0; i < C::NL; ++i) {
@@ -194,13 +202,15 @@ __device__ __forceinline__ void valu_block(const float (&qf)[ValuCfg<dt, D, BS, 
   m = mn;
 }
 
-// Maximum blocks (VALU) or 32-token steps (MFMA) one wave handles in one partition: their
+// Maximum units (VALU) or 32-token steps (MFMA) one wave handles in one partition: their
 // physical ids sit one per lane of a single register.
 constexpr int kMaxPerWave = 64;
 
 template <DT dt, int D, int BS, int NW, int NBUF>
 __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a) {
-  using C = ValuCfg<dt, D, BS, NW>;
+  constexpr int SB = valu_unit_tokens<BS>();  // tokens per unit; a block holds NSUB units
+  constexpr int NSUB = BS / SB;
+  using C = ValuCfg<dt, D, SB, NW>;
   constexpr int E = C::E, VEC = C::VEC, R = C::R, TPI = C::TPI, NL = C::NL, NT = C::NT;
   __shared__ float lds_o[NW][D];
   __shared__ float lds_m[NW], lds_l[NW];
@@ -209,17 +219,18 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
   const int p = blockIdx.x, h = blockIdx.y;
   const int s = blockIdx.z;
   const int P = a.partition_tokens;
-  const int jb0 = p * (P / BS);
+  const int jb0 = p * (P / SB);  // first unit of the partition
   const int lane = threadIdx.x & 63;
   const int w = wave_id();
   const int c = lane % R, r = lane / R;
   // Issued before the context length is known, so the id, query and length loads overlap:
-  // lane k takes the id of this wave's k-th block of the partition (when inside the table).
+  // lane k takes the id of the block holding this wave's k-th unit of the partition (when
+  // inside the table).
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   int my_id = 0;
   {
-    const int j = jb0 + w + lane * NW;
-    if (lane < (P / BS + NW - 1) / NW && j < a.max_blocks_per_seq) my_id = bt[j];
+    const int j = (jb0 + w + lane * NW) / NSUB;
+    if (lane < (P / SB + NW - 1) / NW && j < a.max_blocks_per_seq) my_id = bt[j];
   }
   const u32x4 qraw =
       load16((const char*)a.q + (((int64_t)s * a.num_q_heads + h) * D + c * VEC) * E);
@@ -234,7 +245,7 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
   const int kvh = h / (a.num_q_heads / a.num_kv_heads);
   const int t0 = p * P;
   const int t1 = (T < t0 + P) ? T : t0 + P;
-  const int jb1 = (t1 + BS - 1) / BS;
+  const int jb1 = (t1 + SB - 1) / SB;
 
   float qf[VEC];
   {
@@ -248,7 +259,7 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
 #pragma unroll
   for (int e = 0; e < VEC; ++e) o[e] = 0.0f;
 
-  // This wave takes blocks jb0 + w + k*NW, k < nb; lane k holds the k-th physical id.
+  // This wave takes units jb0 + w + k*NW, k < nb; lane k holds the k-th unit's physical id.
   const int nb = (jb1 - jb0 - w + NW - 1) / NW;
   const char* kbase = (const char*)a.k_cache;
   const char* vbase = (const char*)a.v_cache;
@@ -256,15 +267,18 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
   // Per-lane byte offset inside a (block, head) tile: loop-invariant and 32-bit, so loads take
   // the form (wave-uniform 64-bit tile base) + (per-lane 32-bit offset).
   const uint32_t lane_off = (uint32_t)(r * row_bytes + c * 16);
-  // Fetch k >= nb is a prefetch past the wave's last block, never consumed. It reads the pool's
+  // Fetch k >= nb is a prefetch past the wave's last unit, never consumed. It reads the pool's
   // first tile, which such prefetches of every workgroup share, so it stays cached; the wave's
-  // own last block would not be, since the streaming loads evict it first.
+  // own last unit would not be, since the streaming loads evict it first.
   auto fetch = [&](int k, u32x4* kr, u32x4* vr) {
     const bool live = k < nb;
     const int32_t id = __builtin_amdgcn_readlane(my_id, live ? k : 0);
-    const int64_t tile =
+    int64_t tile =
         live ? (clamp_block(id, a.num_blocks) * a.num_kv_heads + kvh) * (int64_t)(BS * row_bytes)
              : 0;
+    if constexpr (NSUB > 1) {  // the unit's rows within its block
+      if (live) tile += (int64_t)(((jb0 + w + k * NW) % NSUB) * SB * row_bytes);
+    }
     const char* kt = kbase + tile;
     const char* vt = vbase + tile;
 #pragma unroll
@@ -275,11 +289,11 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
     __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the consume that follows
   };
   auto consume = [&](int k, const u32x4* kr, const u32x4* vr) {
-    const int tok0 = (jb0 + w + k * NW) * BS;
-    if (tok0 + BS <= t1)
-      valu_block<dt, D, BS, NW, false>(qf, kr, vr, tok0, t1, r, m, l, o);
+    const int tok0 = (jb0 + w + k * NW) * SB;
+    if (tok0 + SB <= t1)
+      valu_block<dt, D, SB, NW, false>(qf, kr, vr, tok0, t1, r, m, l, o);
     else
-      valu_block<dt, D, BS, NW, true>(qf, kr, vr, tok0, t1, r, m, l, o);
+      valu_block<dt, D, SB, NW, true>(qf, kr, vr, tok0, t1, r, m, l, o);
   };
   // A ring of NBUF register buffers: the loads of the next NBUF-1 blocks are in flight while
   // one block is consumed. Prefetches are unconditional (past the end they read the shared
@@ -354,7 +368,9 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
 // double-buffered in registers. No part of the 16-bit workloads runs here.
 template <DT dt, int D, int BS, int NW>
 __global__ __launch_bounds__(NW * 64) void prefill_valu_kernel(const PrefillArgs a) {
-  using C = ValuCfg<dt, D, BS, NW>;
+  constexpr int SB = valu_unit_tokens<BS>();  // tokens per unit; a block holds NSUB units
+  constexpr int NSUB = BS / SB;
+  using C = ValuCfg<dt, D, SB, NW>;
   constexpr int E = C::E, VEC = C::VEC, R = C::R, TPI = C::TPI, NL = C::NL, NT = C::NT;
   __shared__ float lds_o[NW][D];
   __shared__ float lds_m[NW], lds_l[NW];
@@ -382,7 +398,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_valu_kernel(const PrefillArgs
   const int i = row - q0;
   if (i < 0 || i >= n) return;  // uniform over the workgroup
   const int t_end = T - n + i + 1;  // the row sees tokens 0 .. t_end - 1
-  const int nblk = (t_end + BS - 1) / BS;
+  const int nunit = (t_end + SB - 1) / SB;
   const int kvh = h / (Hq / a.num_kv_heads);
 
   const int lane = threadIdx.x & 63;
@@ -405,17 +421,18 @@ __global__ __launch_bounds__(NW * 64) void prefill_valu_kernel(const PrefillArgs
   const uint32_t lane_off = (uint32_t)(r * row_bytes + c * 16);
   const char* kbase = (const char*)a.k_cache;
   const char* vbase = (const char*)a.v_cache;
-  // Chunks of 64 blocks per wave: wave w takes blocks base + w + k*NW, k < nb; lane k of
-  // my_id holds the k-th id.
-  for (int base = 0; base < nblk; base += 64 * NW) {
+  // Chunks of 64 units per wave: wave w takes units base + w + k*NW, k < nb; lane k of
+  // my_id holds the id of the block holding the k-th.
+  for (int base = 0; base < nunit; base += 64 * NW) {
     const int j = base + w + lane * NW;
-    const int my_id = (j < nblk) ? bt[j] : 0;  // nblk <= cap / BS <= max_blocks_per_seq
-    const int left = nblk - base < 64 * NW ? nblk - base : 64 * NW;
+    const int my_id = (j < nunit) ? bt[j / NSUB] : 0;  // j / NSUB < max_blocks_per_seq
+    const int left = nunit - base < 64 * NW ? nunit - base : 64 * NW;
     const int nb = (left - w + NW - 1) / NW;
     auto fetch = [&](int k, u32x4* kr, u32x4* vr) {
       const int32_t id = __builtin_amdgcn_readlane(my_id, k);
-      const int64_t tile =
+      int64_t tile =
           (clamp_block(id, a.num_blocks) * a.num_kv_heads + kvh) * (int64_t)(BS * row_bytes);
+      if constexpr (NSUB > 1) tile += (int64_t)(((base + w + k * NW) % NSUB) * SB * row_bytes);
 #pragma unroll
       for (int q = 0; q < NL; ++q) {
         kr[q] = load16(kbase + tile + lane_off + q * TPI * row_bytes);
@@ -423,11 +440,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_valu_kernel(const PrefillArgs
       }
     };
     auto consume = [&](int k, const u32x4* kr, const u32x4* vr) {
-      const int tok0 = (base + w + k * NW) * BS;
-      if (tok0 + BS <= t_end)
-        valu_block<dt, D, BS, NW, false>(qf, kr, vr, tok0, t_end, r, m, l, o);
+      const int tok0 = (base + w + k * NW) * SB;
+      if (tok0 + SB <= t_end)
+        valu_block<dt, D, SB, NW, false>(qf, kr, vr, tok0, t_end, r, m, l, o);
       else
-        valu_block<dt, D, BS, NW, true>(qf, kr, vr, tok0, t_end, r, m, l, o);
+        valu_block<dt, D, SB, NW, true>(qf, kr, vr, tok0, t_end, r, m, l, o);
     };
     if (nb <= 0) continue;  // uniform
     // Two buffers, unrolled so that both are register arrays; the fetch ahead is unconditional
@@ -522,14 +539,15 @@ __device__ __forceinline__ void lds_read_k(u32x4 (&t)[2][2], const uint32_t (&ka
 template <DT dt, int D, int BS, int NW, int NBUF, int MINB>
 __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const DecodeArgs a) {
   static_assert(dt != DT::F32, "MFMA path takes 16-bit inputs");
-  static_assert(BS <= 32 && 32 % BS == 0, "a 32-token step spans whole blocks");
+  static_assert(32 % BS == 0 || BS % 32 == 0, "a 32-token step spans whole blocks or part of one");
   using M = MfmaT<dt>;
   using vec8 = typename M::vec8;
   using VF = VFrag<D>;
   constexpr int E = 2;
   constexpr int KC = D / 32;  // q.K MFMAs per 16-token tile
   constexpr int MT = D / 16;  // p.V M-tiles; row r of tile mt is head dimension MT*r + mt
-  constexpr int NBS = 32 / BS;
+  constexpr int NBS = BS >= 32 ? 1 : 32 / BS;  // blocks a step touches
+  constexpr int SPB = BS > 32 ? BS / 32 : 1;    // steps per block
   constexpr int NT = NW * 64;
   __shared__ __attribute__((aligned(1024))) char lds_k[NW][NBUF][32 * D * 2];  // K ring
   __shared__ float lds_o[NW][16][D];
@@ -557,7 +575,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
 #pragma unroll
   for (int b = 0; b < NBS; ++b) {
     my_id[b] = 0;
-    const int j = (st0 + w + lane * NW) * (32 / BS) + b;
+    const int j = (st0 + w + lane * NW) * NBS / SPB + b;
     if (lane < (P / 32 + NW - 1) / NW && j < a.max_blocks_per_seq) my_id[b] = bt[j];
   }
   // Q^T operand: column hh = query head h0 + hh, k = head dims 32*kk + 8*gq + e.
@@ -643,7 +661,11 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
     constexpr int slot = decltype(slotc)::value;
     const bool live = k < ns;
     const int kq = live ? k : 0;
-    const int jfirst = (st0 + w + k * NW) * (32 / BS);
+    const int step = st0 + w + k * NW;
+    const int jfirst = step * NBS / SPB;  // block of the step's first token
+    // Blocks larger than a step: the step's 32 rows start (step % SPB) * 32 rows into its block,
+    // and its resources span those rows only.
+    constexpr int span = BS > 32 ? 32 * RB : (int)(BS * RB);
     __amdgpu_buffer_rsrc_t kr[NBS];
     int64_t tile[NBS];
     bool has[NBS];
@@ -651,8 +673,9 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
     for (int b = 0; b < NBS; ++b) {
       const int id = clamp_id(__builtin_amdgcn_readlane(my_id[b], kq), id_max);
       tile[b] = (int64_t)id * blk_stride;
+      if constexpr (SPB > 1) tile[b] += (int64_t)((step % SPB) * span);
       has[b] = live && jfirst + b <= jlast;
-      kr[b] = tile_rsrc(kbase + tile[b], has[b] ? (int)tile_bytes : 0);
+      kr[b] = tile_rsrc(kbase + tile[b], has[b] ? span : 0);
     }
     // K first, then V: 0.7% faster on the GQA batch than the other order (measured on MI355X).
 #pragma unroll
@@ -661,7 +684,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
     if constexpr (BS >= 16) {
       __amdgpu_buffer_rsrc_t vr[NBS];
 #pragma unroll
-      for (int b = 0; b < NBS; ++b) vr[b] = tile_rsrc(vbase + tile[b], has[b] ? (int)tile_bytes : 0);
+      for (int b = 0; b < NBS; ++b) vr[b] = tile_rsrc(vbase + tile[b], has[b] ? span : 0);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -719,14 +742,17 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
     const float mn = fmaxf(m, bm);
     const bool empty = (mn == kNegInf);
     const float corr = empty ? 1.0f : fast_exp2(m - mn);
-    vec8 pop;
+    // The weights are rounded to 16 bits for the p.V MFMA; the row sum adds those same rounded
+    // weights (dot2 of each packed pair with (1, 1)), so numerator and denominator agree.
+    float pe[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pe[e] = empty ? 0.0f : fast_exp2(sc[e] - mn);
+    const u32x4 pw = {pack2<dt>(pe[0], pe[1]), pack2<dt>(pe[2], pe[3]),
+                      pack2<dt>(pe[4], pe[5]), pack2<dt>(pe[6], pe[7])};
     float ps = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float pe = empty ? 0.0f : fast_exp2(sc[e] - mn);
-      ps += pe;
-      pop[e] = (typename M::scalar)pe;
-    }
+    for (int j = 0; j < 4; ++j) ps = sum2<dt>(pw[j], ps);
+    const vec8 pop = __builtin_bit_cast(vec8, pw);
     lsum = fmaf(lsum, corr, ps);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) oacc[mt] *= corr;
@@ -819,7 +845,9 @@ constexpr int kValuBuffers = 4;    // VALU kernel: blocks in registers (NBUF-1 i
 // decode took 174.9 against 169.9 us (measured on MI355X).
 template <DT dt, int D, int BS>
 constexpr int valu_buffers() {
-  return (dt == DT::F32 && ValuCfg<dt, D, BS, kWaves>::NL >= 8) ? 3 : kValuBuffers;
+  return (dt == DT::F32 && ValuCfg<dt, D, valu_unit_tokens<BS>(), kWaves>::NL >= 8)
+             ? 3
+             : kValuBuffers;
 }
 constexpr int kMfmaBuffers = 3;    // MFMA kernel: 32-token steps in registers
 constexpr int kMfmaMinBlocks = 1;  // MFMA kernel: workgroups per CU the registers must allow
@@ -859,16 +887,19 @@ hipError_t launch_prefill_valu(int head_dim, int block_size, const PrefillArgs& 
     case 6408: return launch_pf_valu_t<64, 8>(a, stream);
     case 6416: return launch_pf_valu_t<64, 16>(a, stream);
     case 6432: return launch_pf_valu_t<64, 32>(a, stream);
+    case 6464: return launch_pf_valu_t<64, 64>(a, stream);
     case 12808: return launch_pf_valu_t<128, 8>(a, stream);
     case 12816: return launch_pf_valu_t<128, 16>(a, stream);
     case 12832: return launch_pf_valu_t<128, 32>(a, stream);
+    case 12864: return launch_pf_valu_t<128, 64>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 int max_partition_tokens(DecodePath path, int block_size) {
-  // every wave's block (or step) ids must fit one register: kMaxPerWave per wave
-  return path == DecodePath::Valu ? kMaxPerWave * kWaves * block_size : kMaxPerWave * kWaves * 32;
+  // every wave's unit (or step) ids must fit one register: kMaxPerWave per wave
+  const int unit = block_size > 32 ? 16 : block_size;  // valu_unit_tokens
+  return path == DecodePath::Valu ? kMaxPerWave * kWaves * unit : kMaxPerWave * kWaves * 32;
 }
 
 // Launches report their own status (hipLaunchKernel), never a stale error left by an earlier,
@@ -910,6 +941,7 @@ static hipError_t launch_bs(DecodePath path, int bs, const DecodeArgs& a, hipStr
     case 8: return launch_t<dt, D, 8>(path, a, st);
     case 16: return launch_t<dt, D, 16>(path, a, st);
     case 32: return launch_t<dt, D, 32>(path, a, st);
+    case 64: return launch_t<dt, D, 64>(path, a, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -926,7 +958,7 @@ static hipError_t launch_d(DecodePath path, int d, int bs, const DecodeArgs& a, 
 bool decode_supported(DecodePath path, int dt, int head_dim, int block_size) {
   if (dt < 0 || dt > 2) return false;
   if (head_dim != 64 && head_dim != 128) return false;
-  if (block_size != 8 && block_size != 16 && block_size != 32) return false;
+  if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64) return false;
   if (path == DecodePath::Mfma && dt == 0) return false;
   return true;
 }

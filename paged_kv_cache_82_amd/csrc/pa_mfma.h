@@ -34,6 +34,32 @@ struct MfmaT<DT::F16> {
   }
 };
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to nearest-even 16-bit values, packed low/high (one v_cvt_pk_*_f32).
+template <DT dt>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (dt == DT::BF16) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+  }
+}
+
+// acc + lo + hi of a packed pair of 16-bit values (v_dot2c_f32_{f16,bf16} against (1, 1)):
+// the softmax row sum taken over the weights exactly as the p.V MFMA sees them.
+template <DT dt>
+__device__ __forceinline__ float sum2(uint32_t pair, float acc) {
+  if constexpr (dt == DT::BF16) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+  } else {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
+  }
+}
+
 // V row fragment of one token: D/16 consecutive head dimensions (16 bytes for D = 128,
 // 8 bytes for D = 64).
 template <int D>

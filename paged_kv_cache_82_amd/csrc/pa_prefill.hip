@@ -119,31 +119,6 @@ __device__ __forceinline__ float max8f(const f32x4& x, const f32x4& y) {
       : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]));
   return r;
 }
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Two floats rounded to nearest-even 16-bit values, packed low/high (one v_cvt_pk_*_f32).
-template <DT dt>
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  if constexpr (dt == DT::BF16) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
-  } else {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
-  }
-}
-
-// acc + lo + hi of a packed pair of 16-bit values (v_dot2c_f32_{f16,bf16} against (1, 1)).
-template <DT dt>
-__device__ __forceinline__ float sum2(uint32_t pair, float acc) {
-  if constexpr (dt == DT::BF16) {
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
-  } else {
-    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
-  }
-}
-
 }  // namespace
 
 // Three workgroups per CU (12 waves, 144 KB of LDS at d = 128): the kernel fits 168 VGPRs by
@@ -361,9 +336,13 @@ __global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillA
       ids = load_ids(st >> 6);
       __builtin_amdgcn_s_waitcnt(0x0F70 & ~0x0F);  // vmcnt(0): ids is never pending past here
     }
-    const uint64_t t = (uint64_t)(uint32_t)__builtin_amdgcn_readlane(ids, st & 63) * blk_bytes;
-    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kbase + t, (int)tile_bytes);
-    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vbase + t, (int)tile_bytes);
+    uint64_t t = (uint64_t)(uint32_t)__builtin_amdgcn_readlane(ids, st & 63) * blk_bytes;
+    // Blocks larger than a stage: the stage's rows start (st % (BS / KT)) * KT rows into the
+    // block, and the resources span those KT rows only.
+    if constexpr (BS > KT) t += (uint64_t)((st % (BS / KT)) * TILE);
+    constexpr int span = BS > KT ? TILE : (int)(BS * RB);
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kbase + t, span);
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vbase + t, span);
 #pragma unroll
     for (int k = 0; k < WLW; ++k) {
       const int mload = w * WLW + k;  // wave-wide load index within the tensor
@@ -604,7 +583,7 @@ int prefill_rows_per_workgroup() { return kPrefillWaves * kPrefillColTiles * 16;
 bool prefill_supported(int dt, int head_dim, int block_size) {
   if (dt < 0 || dt > 2) return false;  // 16-bit inputs on MFMA, fp32 on the vector ALU
   if (head_dim != 64 && head_dim != 128) return false;
-  return block_size == 8 || block_size == 16 || block_size == 32;
+  return block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64;
 }
 
 template <DT dt, int D, int BS>
@@ -625,6 +604,7 @@ static hipError_t launch_pf_bs(int bs, const PrefillArgs& a, hipStream_t st) {
     case 8: return launch_pf<dt, D, 8>(a, st);
     case 16: return launch_pf<dt, D, 16>(a, st);
     case 32: return launch_pf<dt, D, 32>(a, st);
+    case 64: return launch_pf<dt, D, 64>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -11,6 +11,11 @@ from workloads import to_float64
 TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 ATOL16, RTOL16, ATOL32 = 2e-2, 1e-2, 1e-5
 
+# Unit roundoff of the 16-bit formats (half an ulp, relative): 11 and 8 significant bits.
+UNIT_ROUNDOFF = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+# Observed errors of the full-size runs, printed at the end of the session (conftest).
+PARITY_LOG: list = []
+
 
 def to_dev(a: np.ndarray, dtype: str | None = None, device="cuda"):
     if dtype == "bf16":
@@ -167,3 +172,75 @@ def make_dominant_token(step, gap_log2: float = 15.0):
     q[..., 0] = 4.0
     step.q[...] = to_storage(q, dt)
     return step
+
+
+def uses_mfma_decode(step) -> bool:
+    """Whether pa_decode's automatic choice takes the MFMA kernel (16-bit weights) here."""
+    return step.dtype != "f32" and step.num_q_heads // step.num_kv_heads >= 2
+
+
+def tight_bound(ref64: np.ndarray, dtype: str, visible: np.ndarray, weights16: bool):
+    """A regression bound for 16-bit outputs over N(0,1) keys, values and queries, per element,
+    far below the pass rule (2e-2 + 1e-2 |ref|) and derived from where the kernels round:
+      - the output is rounded once to the 16-bit format: at most u |ref| (u the unit roundoff);
+        twice that allows for the fp32 result itself sitting off the exact value;
+      - with 16-bit softmax weights (the MFMA kernels), each weight carries a relative rounding
+        error of at most u, and the numerator and the row sum see the same rounded weights, so
+        the output moves by sum_t w_t d_t (v_t - out) / W. With independent errors uniform in
+        [-u, u] its standard deviation is (u / sqrt 3) sqrt(sum_t w_t^2 (v_t - out)^2) / W,
+        about (u / sqrt 3) sqrt(e / T) for N(0,1) scores and values (the weights' effective
+        count is T / e); eight of those are allowed;
+      - 1e-5 absolute for the fp32 accumulation and exp2.
+    visible: visible tokens per output row (broadcast over heads and dims)."""
+    u = UNIT_ROUNDOFF[dtype]
+    T = np.maximum(np.asarray(visible, np.float64), 1.0).reshape(-1, *([1] * (ref64.ndim - 1)))
+    b = 2.0 * u * np.abs(ref64) + 1e-5
+    if weights16:
+        b = b + 8.0 * (u / np.sqrt(3.0)) * np.sqrt(np.e / T)
+    return b
+
+
+def check_full_size(gpu: np.ndarray, ref64: np.ndarray, dtype: str, visible, weights16: bool,
+                    what: str) -> float:
+    """The pass rule (north-star tolerance) and, for 16-bit outputs, the tight regression bound;
+    logs the observed maximum error and its ratio to each bound."""
+    err = assert_attention_close(gpu, ref64, dtype, what)
+    g = to_float64(gpu, dtype)
+    e = np.abs(g - ref64)
+    if dtype == "f32":
+        PARITY_LOG.append(f"{what}: max|err| {err:.2e} (pass rule 1e-05: {err / ATOL32:.3f}x)")
+        return err
+    loose = float((e / (ATOL16 + RTOL16 * np.abs(ref64))).max())
+    bound = tight_bound(ref64, dtype, visible, weights16)
+    ratio = e / bound
+    tight = float(ratio.max())
+    PARITY_LOG.append(f"{what}: max|err| {err:.2e} (pass rule {loose:.3f}x, tight bound "
+                      f"{tight:.3f}x)")
+    if tight > 1.0:
+        idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+        raise AssertionError(f"{what}: outside the tight bound, {int((ratio > 1).sum())} of "
+                             f"{ratio.size}; worst {idx}: err {e[idx]:.3g} > {bound[idx]:.3g}")
+    return err
+
+
+def tight_failures(gpu: np.ndarray, ref64: np.ndarray, dtype: str, visible, weights16: bool):
+    """(elements outside the tight bound, elements outside the pass rule)."""
+    g = to_float64(gpu, dtype)
+    e = np.abs(g - ref64)
+    bound = tight_bound(ref64, dtype, visible, weights16)
+    loose = ATOL16 + RTOL16 * np.abs(ref64)
+    return int((e > bound).sum()), int((e > loose).sum())
+
+
+def pools_equal(dev_pool: torch.Tensor, host_pool: np.ndarray, dtype: str,
+                chunk_bytes: int = 1 << 30) -> bool:
+    """Bit-exact comparison of a device pool with a host array, a chunk of blocks at a time on
+    the device (for pools too large to copy back whole)."""
+    n = host_pool.shape[0]
+    per = max(1, chunk_bytes // max(1, host_pool[0].nbytes))
+    ity = torch.int32 if dtype == "f32" else torch.int16
+    for i in range(0, n, per):
+        want = to_dev(host_pool[i:i + per], dtype, dev_pool.device)
+        if not torch.equal(dev_pool[i:i + per].view(ity), want.view(ity)):
+            return False
+    return True

@@ -40,9 +40,10 @@ def declared_functions(header=HEADER):
 
 
 def test_header_declares_the_calls():
-    assert declared_functions() == ["pa_copy_blocks", "pa_decode", "pa_decode_workspace_size",
-                                    "pa_prefill", "pa_status_string", "pa_swap_blocks",
-                                    "pa_write_kv"]
+    assert declared_functions() == ["pa_copy_blocks", "pa_decode",
+                                    "pa_decode_workspace_size", "pa_prefill",
+                                    "pa_set_decode_kernel", "pa_status_string",
+                                    "pa_swap_blocks", "pa_write_kv"]
 
 
 def test_block_manager_header_declares_the_calls():
@@ -101,7 +102,7 @@ def test_write_kv_argument_checks(lib):
     assert f(BAD, BAD, BAD, BAD, BAD, 4, 8, 128, 16, 1 << 62, F16, None) == PA_ERR_INVALID_ARG
 
 
-def test_decode_argument_checks(lib, monkeypatch):
+def test_decode_argument_checks(lib):
     f = lib.pa_decode
     args = [BAD, BAD, BAD, BAD, BAD, BAD, 0.125, 4, 8, 8, 128, 16, 4, 64, 50, 0, None, 0, F16,
             None]
@@ -119,7 +120,7 @@ def test_decode_argument_checks(lib, monkeypatch):
     assert call(q=None) == PA_ERR_INVALID_ARG
     assert call(Hq=8, Hkv=3) == PA_ERR_INVALID_ARG
     assert call(d=96) == PA_ERR_UNSUPPORTED
-    assert call(B=64) == PA_ERR_UNSUPPORTED
+    assert call(B=128) == PA_ERR_UNSUPPORTED
     assert call(P=48) == PA_ERR_INVALID_ARG
     assert call(dt=9) == PA_ERR_INVALID_ARG
     assert call(M=0) == PA_ERR_INVALID_ARG
@@ -132,8 +133,14 @@ def test_decode_argument_checks(lib, monkeypatch):
     assert need > 0
     assert call(maxT=4096, P=1024, ws=V(0x1010), wsb=need) == PA_ERR_INVALID_ARG  # misaligned
     # the MFMA path does not take fp32
-    monkeypatch.setenv("PA_DECODE_PATH", "mfma")
-    assert call(dt=F32) == PA_ERR_UNSUPPORTED
+    assert lib.pa_set_decode_kernel(2) == PA_OK
+    try:
+        assert call(dt=F32) == PA_ERR_UNSUPPORTED
+        assert lib.pa_decode_workspace_size(4, 8, 8, 128, 16, 4096, 1024, F32) == 0
+    finally:
+        assert lib.pa_set_decode_kernel(0) == PA_OK
+    assert lib.pa_set_decode_kernel(3) == PA_ERR_INVALID_ARG
+    assert lib.pa_set_decode_kernel(-1) == PA_ERR_INVALID_ARG
 
 
 def test_prefill_argument_checks(lib):
@@ -157,7 +164,7 @@ def test_prefill_argument_checks(lib):
     assert call(dt=F32, d=96) == PA_ERR_UNSUPPORTED
     assert call(dt=F32, Nq=1 << 29, Hq=8, Hkv=8) == PA_ERR_INVALID_ARG
     assert call(d=96) == PA_ERR_UNSUPPORTED
-    assert call(B=64) == PA_ERR_UNSUPPORTED
+    assert call(B=128) == PA_ERR_UNSUPPORTED
     assert call(M=0) == PA_ERR_INVALID_ARG
     assert call(maxn=-1) == PA_ERR_INVALID_ARG
     assert call(N=1 << 62) == PA_ERR_INVALID_ARG

@@ -1,65 +1,96 @@
-"""GPU parity at the full sizes of the four large workloads, in the launch configuration the
-benchmark times (automatic partition size).
+"""GPU parity at the full sizes of the large decode workloads, in the launch configuration the
+benchmark times (automatic partition size), every output against the oracle:
 
-  13B-shape fp16 MHA    (64 seqs, 40 heads, d=128, B=16, lognormal lengths)  all outputs
-  GQA bf16              (256 seqs, 64/8 heads, uniform 128..4096)            all outputs
-  long-context bf16     (8 seqs, 32 heads, uniform 32k..128k)                2 sampled seqs
-  shared-prefix fp16    (16 prompts x 4 samples, B=32)                       in test_gpu_parity
+  13B-shape fp16 MHA    (64 seqs, 40 heads, d=128, B=16, lognormal lengths)   and its fp32 twin
+  GQA bf16              (256 seqs, 64/8 heads, uniform 128..4096)
+  long-context bf16     (8 seqs, 32 heads, uniform 32k..128k, split-K)       and its fp32 twin
+  shared-prefix fp16    (16 prompts x 4 samples, B=32)                        in test_gpu_parity
 
-The KV writes are checked bit-exactly: the whole pool for the first two, and for the long-
-context pool (13+ GB) the written rows plus a count of changed elements, on the device."""
+The KV writes are checked bit-exactly over the whole K and V pools. Attention must meet the
+pass rule (2e-2 + 1e-2 |ref| for 16-bit data, 1e-5 for fp32) and, for 16-bit data, a tight
+regression bound derived from where the kernels round (gpu_harness.tight_bound), which a single
+misplaced block fails: a negative control redirects one block-table entry of the longest
+sequence and must land outside it. Observed errors are printed at the end of the session."""
+import math
+
 import numpy as np
 import pytest
 
 torch = pytest.importorskip("torch")
 
 import oracle
-from gpu_harness import DevStep, assert_attention_close, to_dev, to_host
-from workloads import mha13b_f16, gqa_bf16, long_bf16
+import paged_kv_cache_82_amd as pa
+from gpu_harness import (PARITY_LOG, DevStep, check_full_size, pools_equal, tight_failures,
+                         to_host, uses_mfma_decode)
+from workloads import gqa_bf16, long_bf16, long_lengths, make_step, mha13b_f16, mha13b_lengths
 
 pytestmark = pytest.mark.gpu
 
 
-def _full(step):
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu-test] {request.node.name}", flush=True)
+    yield
+    torch.cuda.empty_cache()
+
+
+def _full(step, negative_control: bool = False):
     dev = DevStep(step)
     got = dev.run()
     ref, kc, vc = oracle.run_step(step, in_place=True)
-    assert np.array_equal(to_host(dev.k_cache, step.dtype).view(np.uint8), kc.view(np.uint8))
-    assert np.array_equal(to_host(dev.v_cache, step.dtype).view(np.uint8), vc.view(np.uint8))
-    return assert_attention_close(got, ref, step.dtype, step.name)
+    assert pools_equal(dev.k_cache, kc, step.dtype), "K pool after the step's writes"
+    assert pools_equal(dev.v_cache, vc, step.dtype), "V pool after the step's writes"
+    w16 = uses_mfma_decode(step)
+    err = check_full_size(got, ref, step.dtype, step.context_lens, w16, step.name)
+    print(f"{step.name} max abs err {err:.3g}", flush=True)
+    if negative_control:
+        _negative_control(step, dev, ref, w16)
+    return err
+
+
+def _negative_control(step, dev, ref, w16):
+    """Point one block-table entry of the longest sequence at another sequence's first block
+    (valid, fully written data) and decode again: that sequence's outputs must fall outside the
+    tight bound. Logs how many elements each bound catches."""
+    B = step.block_size
+    s = int(np.argmax(step.context_lens))
+    T = int(step.context_lens[s])
+    other = (s + 1) % step.num_seqs
+    assert step.context_lens[other] >= B
+    j = math.ceil(T / B) // 2
+    bt = dev.block_tables.clone()
+    bt[s, j] = int(step.block_tables[other, 0])
+    out = torch.empty_like(dev.out)
+    pa.pa_decode(out, dev.q, dev.k_cache, dev.v_cache, bt, dev.context_lens, float(step.scale),
+                 step.max_context_len, dev.workspace, 0)
+    torch.cuda.synchronize()
+    got = to_host(out, step.dtype)[s:s + 1]
+    n_tight, n_loose = tight_failures(got, ref[s:s + 1], step.dtype, step.context_lens[s:s + 1],
+                                      w16)
+    PARITY_LOG.append(f"{step.name} negative control (block {j} of the {T}-token sequence "
+                      f"redirected): {n_tight} of {got.size} outside the tight bound, {n_loose} "
+                      f"outside the pass rule")
+    assert n_tight > 0, "a redirected block went unnoticed by the tight bound"
 
 
 def test_mha13b_f16_full():
-    print("\n[gpu-test] mha13b_f16 full", flush=True)
-    err = _full(mha13b_f16())
-    print(f"mha13b_f16 max abs err {err:.3g}", flush=True)
+    _full(mha13b_f16(), negative_control=True)
 
 
 def test_gqa_bf16_full():
-    print("\n[gpu-test] gqa_bf16 full", flush=True)
-    err = _full(gqa_bf16())
-    print(f"gqa_bf16 max abs err {err:.3g}", flush=True)
+    _full(gqa_bf16(), negative_control=True)
 
 
-def test_long_bf16_sampled():
-    print("\n[gpu-test] long_bf16 sampled", flush=True)
-    step = long_bf16()
-    dev = DevStep(step)
-    k_before = dev.k_cache.clone()
-    got = dev.run()
-    # writes: exactly the written rows changed, to the new values
-    w = step.writes[0]
-    B = step.block_size
-    slots = w.slot_mapping.astype(np.int64)
-    blk = torch.from_numpy(slots // B).cuda()
-    off = torch.from_numpy(slots % B).cuda()
-    rows = dev.k_cache[blk, :, off, :]  # [n, Hkv, d]
-    assert torch.equal(rows.view(torch.int16), to_dev(w.k_new, step.dtype).view(torch.int16))
-    changed = (dev.k_cache.view(torch.int16) != k_before.view(torch.int16)).sum().item()
-    assert changed <= rows.numel()
-    del k_before
-    sample = [int(np.argmin(step.context_lens)), int(np.argmax(step.context_lens))]
-    ref, _, _ = oracle.run_step(step, seq_list=sample, in_place=True)
-    err = assert_attention_close(got[sample], ref, step.dtype, "long_bf16 sample")
-    print(f"long_bf16 sample {sample} lens {step.context_lens[sample].tolist()} max abs err {err:.3g}",
-          flush=True)
+def test_long_bf16_full():
+    # all 8 sequences (32k..128k tokens each, 2048-token partitions and the merge kernel)
+    _full(long_bf16())
+
+
+def test_mha13b_f32_full():
+    # the 13B-shape batch in fp32 (vector-ALU kernel): max-abs 1e-5
+    _full(make_step("mha13b-f32", 2, mha13b_lengths(), 40, 40, 128, 16, "f32"))
+
+
+def test_long_f32_full():
+    # the long-context batch in fp32 (vector-ALU kernel, split-K): max-abs 1e-5
+    _full(make_step("long-f32", 4, long_lengths(), 32, 32, 128, 16, "f32"))

@@ -27,13 +27,13 @@ def _decode_case(i):
     rng = np.random.default_rng(7000 + i)
     dt = ["f32", "f16", "bf16"][rng.integers(3)]
     d = int(rng.choice([64, 128]))
-    B = int(rng.choice([8, 16, 32]))
+    B = int(rng.choice([8, 16, 32, 64]))
     Hkv = int(rng.choice([1, 2, 4]))
     g = int(rng.choice([1, 2, 4, 8, 16]))
     S = int(rng.integers(1, 13))
     lens = [int(x) for x in rng.choice([0, 1, 2, 15, 16, 17, 100, 333, 1024, 2500], size=S)]
     lens[0] = max(lens[0], 1)
-    cap = 64 * 4 * B if (dt == "f32" or g == 1) else 8192
+    cap = 64 * 4 * (B if B <= 32 else 16) if (dt == "f32" or g == 1) else 8192
     P = int(rng.choice([0, 0, 32, 64, 96, 512]))
     P = P if P <= cap else 0
     scale = float(rng.choice([1 / np.sqrt(d), 1 / np.sqrt(d), 0.5, -0.07]))
@@ -44,7 +44,7 @@ def _prefill_case(i):
     rng = np.random.default_rng(8000 + i)
     dt = ["f16", "bf16"][rng.integers(2)]
     d = int(rng.choice([64, 128]))
-    B = int(rng.choice([8, 16, 32]))
+    B = int(rng.choice([8, 16, 32, 64]))
     Hkv = int(rng.choice([1, 2]))
     g = int(rng.choice([1, 2, 4, 8, 16]))
     S = int(rng.integers(1, 7))

@@ -9,7 +9,8 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import oracle
-from gpu_harness import DevStep, assert_attention_close, make_dominant_token, to_host
+from gpu_harness import (DevStep, assert_attention_close, check_full_size, make_dominant_token,
+                         to_host, uses_mfma_decode)
 from workloads import tiny_f32, shared_prefix_f16, make_step, to_float64, to_storage
 
 pytestmark = pytest.mark.gpu
@@ -43,7 +44,7 @@ def test_tiny_f32():
 
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("B", [8, 16, 32])
+@pytest.mark.parametrize("B", [8, 16, 32, 64])
 def test_shapes_mha(dt, d, B):
     step = make_step("mha", 31 + B + d, [1, 7, B, B + 1, 3 * B - 1, 200], 4, 4, d, B, dt)
     _run_and_check(step, what=f"mha {dt} d{d} B{B}")
@@ -51,25 +52,25 @@ def test_shapes_mha(dt, d, B):
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 @pytest.mark.parametrize("g", [2, 4, 8, 16, 32])
-@pytest.mark.parametrize("d,B", [(128, 16), (64, 8), (128, 32)])
+@pytest.mark.parametrize("d,B", [(128, 16), (64, 8), (128, 32), (128, 64), (64, 64)])
 def test_shapes_gqa(dt, g, d, B):
     step = make_step("gqa", 41 + g, [1, 5, 16, 33, 130, 257], 2 * g, 2, d, B, dt)
     _run_and_check(step, what=f"gqa {dt} g{g} d{d} B{B}")
 
 
 @pytest.mark.parametrize("path", ["valu", "mfma"])
-def test_both_decode_paths_on_gqa(path, monkeypatch):
-    monkeypatch.setenv("PA_DECODE_PATH", path)
+def test_both_decode_paths_on_gqa(path, decode_kernel):
+    decode_kernel(path)
     step = make_step("paths", 50, [3, 64, 100, 511, 700], 16, 2, 128, 16, "bf16")
     _run_and_check(step, what=path)
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 @pytest.mark.parametrize("g,path", [(1, "valu"), (4, "valu"), (4, "mfma")])
-def test_small_weights_below_fp16_normal(dt, g, path, monkeypatch):
+def test_small_weights_below_fp16_normal(dt, g, path, decode_kernel):
     # one token outweighs 3999 others by 2^15: their weights are below fp16's smallest normal
     # number and together add 12% to the row sum; both kernels, whole and split
-    monkeypatch.setenv("PA_DECODE_PATH", path)
+    decode_kernel(path)
     for P in (0, 512):
         step = make_dominant_token(make_step("ddom", 481, [4000], 2 * g, 2, 128, 16, dt))
         _run_and_check(step, partition_tokens=P, what=f"dominant token {dt} g{g} {path} P{P}")
@@ -136,14 +137,24 @@ def test_placement_invariance_bit_exact():
         assert np.array_equal(o, outs[0])
 
 
-def test_block_size_change_within_tolerance():
+@pytest.mark.parametrize("Hq,Hkv,dt", [(8, 8, "f16"), (16, 2, "bf16"), (4, 4, "f32")])
+def test_block_size_change_within_tolerance(Hq, Hkv, dt):
+    # the same tokens cut into blocks of 8, 16, 32 and 64 (both decode kernels and fp32)
     ref = None
-    for B in (8, 16, 32):
-        step = make_step("bs", 82, [50, 7, 300], 8, 8, 128, B, "f16")
+    for B in (8, 16, 32, 64):
+        step = make_step("bs", 82, [50, 7, 300, 64, 65], Hq, Hkv, 128, B, dt)
         got = DevStep(step).run()
         if ref is None:
             ref = oracle.run_step(step)[0]
-        assert_attention_close(got, ref, "f16", f"B={B}")
+        assert_attention_close(got, ref, dt, f"B={B}")
+
+
+@pytest.mark.parametrize("Hq,Hkv,dt", [(8, 8, "f16"), (16, 2, "bf16"), (4, 4, "f32")])
+@pytest.mark.parametrize("P", [32, 64, 96, 0])
+def test_block_size_64_split(Hq, Hkv, dt, P):
+    # 64-token blocks split into partitions of 32..96 tokens (partition edges inside blocks)
+    step = make_step("b64", 83, [1, 63, 64, 65, 200, 1000], Hq, Hkv, 128, 64, dt)
+    _run_and_check(step, partition_tokens=P, what=f"B=64 {dt} g{Hq // Hkv} P={P}")
 
 
 def test_repeated_calls_reuse_workspace():
@@ -182,7 +193,9 @@ def test_shared_prefix_small_shared_vs_private():
 
 def test_shared_prefix_full():
     shared = shared_prefix_f16()
-    a, _ = _run_and_check(shared, what="shared_prefix_f16 shared")
+    a, ref = _run_and_check(shared, what="shared_prefix_f16 shared")
+    check_full_size(a, ref, shared.dtype, shared.context_lens, uses_mfma_decode(shared),
+                    shared.name)
     b = DevStep(shared_prefix_f16(private=True)).run()
     assert np.array_equal(a, b)
 

@@ -10,8 +10,8 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import oracle
-from gpu_harness import (DevPrefill, DevStep, assert_attention_close, make_dominant_token,
-                         prefill_rows_reference, to_host)
+from gpu_harness import (DevPrefill, DevStep, assert_attention_close, check_full_size,
+                         make_dominant_token, prefill_rows_reference, to_host)
 from workloads import make_prefill_step, make_step, to_float64
 
 pytestmark = pytest.mark.gpu
@@ -41,7 +41,7 @@ def _check(step, what=""):
 
 @pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("B", [8, 16, 32])
+@pytest.mark.parametrize("B", [8, 16, 32, 64])
 def test_prefill_shapes_mha(dt, d, B):
     # whole prompts, chunks after a cached prefix, a single-token chunk, an empty chunk; 300
     # query rows span three row tiles of 128 with a ragged tail
@@ -53,7 +53,7 @@ def test_prefill_shapes_mha(dt, d, B):
 
 @pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("g", [2, 4, 8, 16])
-@pytest.mark.parametrize("d,B", [(128, 16), (64, 8), (128, 32)])
+@pytest.mark.parametrize("d,B", [(128, 16), (64, 8), (128, 32), (128, 64)])
 def test_prefill_shapes_gqa(dt, g, d, B):
     T = [33, 130, 257, 5]
     n = [33, 50, 17, 5]
@@ -175,5 +175,7 @@ def test_prefill_full_size_sampled_rows(name):
     rows.update(rng.integers(0, step.num_q_tokens, size=96 - len(rows)).tolist())
     rows = np.array(sorted(rows))
     ref = prefill_rows_reference(step, kc, vc, rows)
-    assert_attention_close(got[rows], ref, step.dtype, name)
+    seq = np.searchsorted(qs, rows, side="right") - 1
+    visible = step.context_lens[seq] - (qs[seq + 1] - qs[seq]) + (rows - qs[seq]) + 1
+    check_full_size(got[rows], ref, step.dtype, visible, True, f"{step.name} (96 rows)")
     assert np.isfinite(to_float64(got, step.dtype)).all()
