@@ -31,8 +31,9 @@
  *
  * Ownership and execution: every pointer except the return of pa_status_string is a DEVICE
  * pointer owned by the caller. The library allocates no memory at call time and keeps no state
- * between calls, with one stated exception: the process-wide kernel choice of
- * pa_set_decode_kernel.
+ * between calls, with two stated exceptions: the process-wide kernel choice of
+ * pa_set_decode_kernel, and the static per-GPU scratch array of pa_decode_noalloc (part of the
+ * library's device image, PA_DECODE_SCRATCH_BYTES per GPU, held until the process ends).
  * Each call validates its scalar arguments and pointer alignment on the host, enqueues its
  * kernel(s) on `stream` (a hipStream_t; NULL = the null stream) and returns without waiting
  * for completion. q, k_cache, v_cache, k_new and v_new must be 16-byte aligned; the workspace
@@ -66,6 +67,9 @@ typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
 
 /* Decode kernel choice (pa_set_decode_kernel). */
 typedef enum { PA_DECODE_AUTO = 0, PA_DECODE_VALU = 1, PA_DECODE_MFMA = 2 } pa_decode_kernel;
+
+/* Size of the static per-GPU split-K scratch array that pa_decode_noalloc uses (16 MiB). */
+#define PA_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
 
 typedef enum {
   PA_OK = 0,
@@ -136,8 +140,32 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v
                     size_t workspace_bytes, pa_dtype dt, void *stream);
 
 /*
- * pa_set_decode_kernel — which decode kernel pa_decode and pa_decode_workspace_size use
- * from now on, process-wide. PA_DECODE_AUTO (the default): the
+ * pa_decode_noalloc — pa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments, layouts,
+ * result (bit for bit: the same kernels with the same partition choice) and errors as
+ * pa_decode, without the workspace arguments: the split-K partials go to a static array of
+ * PA_DECODE_SCRATCH_BYTES in the library's device image, one per GPU, held until the process
+ * ends. The call allocates nothing (no hipMalloc, no allocating library routine).
+ * Limit: a call whose partition plan needs more partial-state bytes than
+ * PA_DECODE_SCRATCH_BYTES (pa_decode_workspace_size of the same arguments) returns
+ * PA_ERR_WORKSPACE and launches nothing; 16 MiB holds, for example, 8 sequences x 32 heads x 64
+ * partitions at head_dim 128. Nothing in the array needs clearing between calls (every partial
+ * is written before it is read).
+ * Every call on one GPU shares that GPU's array: calls that may overlap in time on one GPU
+ * (different streams, or different host threads without ordering) race and must not be issued.
+ * The array's device address is looked up once per GPU (hipGetSymbolAddress, on the first call
+ * on that GPU that splits a sequence); PA_ERR_HIP if that lookup fails.
+ */
+pa_status pa_decode_noalloc(void *out, const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *block_tables, const int32_t *context_lens,
+                            float scale, int num_seqs, int num_q_heads, int num_kv_heads,
+                            int head_dim, int block_size, int max_blocks_per_seq,
+                            int64_t num_blocks, int max_context_len, int partition_tokens,
+                            pa_dtype dt, void *stream);
+
+/*
+ * pa_set_decode_kernel — which decode kernel pa_decode, pa_decode_noalloc and
+ * pa_decode_workspace_size use from now on, process-wide. PA_DECODE_AUTO (the default): the
  * MFMA kernel for f16/bf16 with at least two query heads per KV head, the vector-ALU kernel
  * otherwise. PA_DECODE_VALU / PA_DECODE_MFMA force one kernel (the MFMA kernel takes no f32:
  * PA_ERR_UNSUPPORTED then). Both kernels compute the same attention; the choice moves only the

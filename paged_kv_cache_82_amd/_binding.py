@@ -55,6 +55,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.pa_decode_workspace_size.restype = SZ
         lib.pa_decode.argtypes = [P, P, P, P, P, P, F, I, I, I, I, I, I, I64, I, I, P, SZ, I, P]
         lib.pa_decode.restype = I
+        lib.pa_decode_noalloc.argtypes = [P, P, P, P, P, P, F, I, I, I, I, I, I, I64, I, I, I, P]
+        lib.pa_decode_noalloc.restype = I
         lib.pa_set_decode_kernel.argtypes = [I]
         lib.pa_set_decode_kernel.restype = I
         lib.pa_prefill.argtypes = [P, P, P, P, P, P, P, F, I, I, I, I, I, I, I, I64, I, I, I, P]
@@ -130,6 +132,19 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_c
         _ptr(context_lens), float(scale), S, Hq, Hkv, d, B, block_tables.shape[1], N,
         int(max_context_len), int(partition_tokens), _ptr(workspace), ws_bytes,
         _dtype_code(q), _stream(stream)))
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                      max_context_len, partition_tokens=0, stream=None) -> None:
+    """pa_decode with the split-K partials in the library's static per-GPU scratch array (no
+    workspace argument, no allocation); raises PAError(PA_ERR_WORKSPACE) when the partition
+    plan needs more than PA_DECODE_SCRATCH_BYTES."""
+    S, Hq, d = q.shape
+    N, Hkv, B, _ = k_cache.shape
+    _check("pa_decode_noalloc", load().pa_decode_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), float(scale), S, Hq, Hkv, d, B, block_tables.shape[1], N,
+        int(max_context_len), int(partition_tokens), _dtype_code(q), _stream(stream)))
 
 
 DECODE_KERNELS = {"auto": 0, "valu": 1, "mfma": 2}

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "pa.h"
 #include "pa_internal.h"
@@ -72,13 +73,43 @@ int parts_for(int max_context_len, int P) {
 
 pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
-// pa_decode with the split-K partials in `workspace` (the caller's buffer).
+// ---- the allocation-free decode: split-K partials in a static device array -----------------
+// `scratch` is a file-scope device array; every GPU the library runs on holds its own copy,
+// at its own address, until the process ends. Host code never uses the array's name as an
+// address (on the host it is only a stand-in symbol): the per-device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and only that address
+// is passed to kernels. No region of it needs initialising: each partition's workgroup writes
+// its (max, sum, output) before the merge kernel reads them, and the merge reads only the
+// partitions that exist.
+static __device__ __align__(256) unsigned char scratch[PA_DECODE_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_dev[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+pa_status scratch_ptr(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_dev[dev] = (g_scratch_err[dev] == hipSuccess) ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_dev[dev]) return PA_ERR_HIP;
+  *ptr = g_scratch_dev[dev];
+  return PA_OK;
+}
+
+// pa_decode with the split-K partials in `workspace` (the caller's buffer), or, with
+// use_scratch, in the library's static scratch array (pa_decode_noalloc; workspace ignored).
 pa_status decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, const int32_t* context_lens, float scale,
                       int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                       int block_size, int max_blocks_per_seq, int64_t num_blocks,
                       int max_context_len, int partition_tokens, void* workspace,
-                      size_t workspace_bytes, pa_dtype dt, void* stream) {
+                      size_t workspace_bytes, bool use_scratch, pa_dtype dt, void* stream) {
   if (!valid_dtype(dt)) return PA_ERR_INVALID_ARG;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       block_size <= 0 || max_blocks_per_seq < 0 || num_blocks <= 0 || max_context_len < 0 ||
@@ -107,6 +138,15 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   const int max_parts = parts_for(max_context_len, P);
   const pa::WorkspaceLayout L =
       pa::workspace_layout(num_seqs, num_q_heads, head_dim, max_parts);
+  if (use_scratch) {
+    workspace = nullptr;
+    workspace_bytes = PA_DECODE_SCRATCH_BYTES;
+    if (L.total > workspace_bytes) return PA_ERR_WORKSPACE;
+    if (L.total > 0) {
+      const pa_status st = scratch_ptr(&workspace);
+      if (st != PA_OK) return st;
+    }
+  }
   if (workspace_bytes < L.total || (L.total > 0 && !workspace)) return PA_ERR_WORKSPACE;
   if (L.total > 0 && !aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
 
@@ -197,7 +237,19 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_seqs,
                      num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                      num_blocks, max_context_len, partition_tokens, workspace, workspace_bytes,
-                     dt, stream);
+                     false, dt, stream);
+}
+
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            float scale, int num_seqs, int num_q_heads, int num_kv_heads,
+                            int head_dim, int block_size, int max_blocks_per_seq,
+                            int64_t num_blocks, int max_context_len, int partition_tokens,
+                            pa_dtype dt, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                     num_blocks, max_context_len, partition_tokens, nullptr, 0, true, dt,
+                     stream);
 }
 
 pa_status pa_set_decode_kernel(pa_decode_kernel kernel) {

@@ -40,7 +40,7 @@ def declared_functions(header=HEADER):
 
 
 def test_header_declares_the_calls():
-    assert declared_functions() == ["pa_copy_blocks", "pa_decode",
+    assert declared_functions() == ["pa_copy_blocks", "pa_decode", "pa_decode_noalloc",
                                     "pa_decode_workspace_size", "pa_prefill",
                                     "pa_set_decode_kernel", "pa_status_string",
                                     "pa_swap_blocks", "pa_write_kv"]
@@ -141,6 +141,35 @@ def test_decode_argument_checks(lib):
         assert lib.pa_set_decode_kernel(0) == PA_OK
     assert lib.pa_set_decode_kernel(3) == PA_ERR_INVALID_ARG
     assert lib.pa_set_decode_kernel(-1) == PA_ERR_INVALID_ARG
+
+
+def test_decode_noalloc_argument_checks(lib):
+    """The allocation-free decode shares pa_decode's checks and rejects a partition plan whose
+    partials exceed its static scratch array before touching any device state."""
+    f = lib.pa_decode_noalloc
+    args = [BAD, BAD, BAD, BAD, BAD, BAD, 0.125, 4, 8, 8, 128, 16, 4, 64, 50, 0, F16, None]
+    names = ["out", "q", "k", "v", "bt", "cl", "scale", "S", "Hq", "Hkv", "d", "B", "M", "N",
+             "maxT", "P", "dt", "stream"]
+
+    def call(**kw):
+        a = list(args)
+        for k, val in kw.items():
+            a[names.index(k)] = val
+        return f(*a)
+
+    assert call(S=0) == PA_OK
+    assert call(q=None) == PA_ERR_INVALID_ARG
+    assert call(Hq=8, Hkv=3) == PA_ERR_INVALID_ARG
+    assert call(d=96) == PA_ERR_UNSUPPORTED
+    assert call(P=48) == PA_ERR_INVALID_ARG
+    assert call(dt=9) == PA_ERR_INVALID_ARG
+    # 8 sequences x 32 heads x 64 partitions of head_dim 128 fit 16 MiB; 16 sequences do not
+    need8 = lib.pa_decode_workspace_size(8, 32, 32, 128, 16, 131072, 2048, BF16)
+    need16 = lib.pa_decode_workspace_size(16, 32, 32, 128, 16, 131072, 2048, BF16)
+    assert need8 <= pa.SCRATCH_BYTES < need16
+    assert call(S=16, Hq=32, Hkv=32, M=8192, N=1 << 16, maxT=131072, P=2048,
+                dt=BF16) == PA_ERR_WORKSPACE
+    assert call(S=65535, Hq=64, Hkv=64, M=512, N=1 << 16, maxT=8192, P=256) == PA_ERR_WORKSPACE
 
 
 def test_prefill_argument_checks(lib):
