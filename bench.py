@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, vendor figure
 PEAK_MFMA_TFLOPS_16 = 2500.0  # MI355X dense fp16/bf16 matrix peak, vendor figure
+PEAK_VALU_TFLOPS_32 = 157.3  # MI355X fp32 vector peak, vendor figure (256 CUs at 2.4 GHz)
 
 WORKLOADS = {
     "mha13b": ("mha13b_f16", "13B-shape fp16 MHA decode: 64 seqs, 40 heads, d=128, B=16, "
@@ -48,6 +49,9 @@ WORKLOADS = {
                        "clipped to [0,1536]"),
     "prefill-gqa": ("prefill_gqa", "chunked prefill, GQA bf16: 16 seqs, 64 query / 8 KV heads, "
                     "d=128, B=16, 1024-token chunks after prefixes uniform in [0,3072]"),
+    "prefill-f32": ("prefill_mha13b_f32", "chunked prefill, 13B shape fp32 (vector-ALU kernel): "
+                    "16 seqs, 40 heads, d=128, B=16, 64-token chunks after lognormal (median "
+                    "512) prefixes clipped to [0,1536]"),
     "copy": (None, "plain copy calibration: pa_copy_blocks of 4096 blocks of 256 KiB"),
     "sharing": (None, "KV memory accounting on the host block manager (no GPU): prompt sharing "
                 "in parallel sampling and beam search, paged vs contiguous waste"),
@@ -366,6 +370,8 @@ def run_prefill(args):
     att_s = e0.elapsed_time(e1) / 1e3 / n_roof
     fl = prefill_flops(step)
     n_new = step.num_q_tokens
+    f32 = step.dtype == "f32"
+    peak = PEAK_VALU_TFLOPS_32 if f32 else PEAK_MFMA_TFLOPS_16
     res = {
         "metric": "paged prefill attention: achieved TFLOP/s (% of MFMA peak) + query tokens/s",
         "value": round(fl / (wall / args.steps) / 1e12, 3),
@@ -387,13 +393,15 @@ def run_prefill(args):
         "execution": "eager" if args.no_graph else f"HIP graph of {ncopy} steps, replayed",
         "eager_ms_per_step": round(eager_wall / args.steps * 1e3, 5),
         "roofline": {
-            "kernel": "pa_prefill: prefill_mfma_kernel",
-            "bound": "mfma",
+            "kernel": ("pa_prefill: prefill_valu_kernel" if f32 else
+                       "pa_prefill: prefill_mfma_kernel"),
+            "bound": "alu" if f32 else "mfma",
             "achieved": round(fl / att_s / 1e12, 3),
-            "peak": PEAK_MFMA_TFLOPS_16,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(fl / att_s / 1e12 / PEAK_MFMA_TFLOPS_16, 4),
-            "traffic": measured_traffic("prefill", args.workload[len("prefill-"):]),
+            "frac": round(fl / att_s / 1e12 / peak, 4),
+            "traffic": (None if f32 else
+                        measured_traffic("prefill", args.workload[len("prefill-"):])),
             "algorithmic_flops_per_launch": fl,
             "algorithmic_bytes_per_launch": prefill_bytes(step),
             "avg_launch_us": round(att_s * 1e6, 3),
@@ -593,7 +601,8 @@ def main():
         res["workloads"] = {"mha13b": summary(res)}
         for name in EXTRA_WORKLOADS:
             t0 = time.perf_counter()
-            res["workloads"][name] = summary(measure_decode(name, args, cpu=False))
+            res["workloads"][name] = summary(measure_decode(name, args, cpu=False,
+                                                            compare_plain=True))
             print(f"bench: {name} measured in {time.perf_counter() - t0:.1f} s", file=sys.stderr,
                   flush=True)
     print(json.dumps(res))
@@ -612,16 +621,19 @@ def summary(res: dict) -> dict:
            "roofline": {k: r[k] for k in ("kernel", "bound", "achieved", "peak", "unit", "frac",
                                           "traffic", "algorithmic_bytes_per_launch",
                                           "avg_launch_us")}}
-    for k in ("logical_bytes_per_launch", "logical_GB_per_s"):
+    for k in ("logical_bytes_per_launch", "logical_GB_per_s", "pa_decode_avg_launch_us",
+              "pa_decode_GB_per_s"):
         if k in r:
             out["roofline"][k] = r[k]
     return out
 
 
-def measure_decode(workload: str, args, cpu: bool) -> dict:
+def measure_decode(workload: str, args, cpu: bool, compare_plain: bool = False) -> dict:
     """One decode workload: inputs generated and uploaded, W warmup steps, K timed steps (graph
-    replay unless --no-graph), then K back-to-back decode launches between HIP events on the
-    launch stream for the roofline. Frees its device memory before returning."""
+    replay unless --no-graph), then back-to-back decode launches between HIP events on the
+    launch stream for the roofline. The shared-prefix workload decodes with
+    pa_decode_shared_prefix, its groups read off the step's tables (compare_plain: plain
+    pa_decode timed the same way beside it). Frees its device memory before returning."""
     import numpy as np
     import torch
 
@@ -655,6 +667,27 @@ def measure_decode(workload: str, args, cpu: bool) -> dict:
     split = ws_bytes > 0  # partial states are needed only when some sequence splits
     scale = float(step.scale)
     maxT = step.max_context_len
+    shared_api = workload == "shared"
+    if shared_api:
+        # the sharing structure as the block manager reports it (pa_bm_prefix_groups): runs of
+        # consecutive sequences holding the same leading blocks
+        from workloads import prefix_groups
+
+        gs_np, pl_np = prefix_groups(step.block_tables, step.context_lens, step.block_size)
+        gs, pl = up(gs_np), up(pl_np)
+        max_group, max_prefix = int(np.diff(gs_np).max()), int(pl_np.max())
+        ws_sh_bytes = pa.pa_decode_shared_prefix_workspace_size(
+            step.num_seqs, len(gs_np) - 1, step.num_q_heads, step.num_kv_heads, step.head_dim,
+            step.block_size, maxT, max_prefix, max_group, P, tdt)
+        ws_sh = torch.zeros(max(ws_sh_bytes, 256), dtype=torch.uint8, device=dev)
+
+    def decode(kc, vc):
+        if shared_api:
+            pa.pa_decode_shared_prefix(out, q, kc, vc, bt, cl, pl, gs, scale, maxT, max_prefix,
+                                       max_group, ws_sh, P)
+        else:
+            pa.pa_decode(out, q, kc, vc, bt, cl, scale, maxT, ws, P)
+
     torch.cuda.synchronize()
 
     def one_step(i, ev=None):
@@ -665,7 +698,7 @@ def measure_decode(workload: str, args, cpu: bool) -> dict:
             pa.pa_write_kv(kc, vc, kn, vn, sm)
         if ev is not None:
             ev[0].record()
-        pa.pa_decode(out, q, kc, vc, bt, cl, scale, maxT, ws, P)
+        decode(kc, vc)
         if ev is not None:
             ev[1].record()
 
@@ -719,10 +752,19 @@ def measure_decode(workload: str, args, cpu: bool) -> dict:
     e0.record()
     for i in range(n_roof):
         kc, vc = pools[i % ncopy]
-        pa.pa_decode(out, q, kc, vc, bt, cl, scale, maxT, ws, P)
+        decode(kc, vc)
     e1.record()
     torch.cuda.synchronize()
     dec_s = e0.elapsed_time(e1) / 1e3 / n_roof
+    plain_s = None
+    if shared_api and compare_plain:  # the same launches without the sharing description
+        e0.record()
+        for i in range(n_roof):
+            kc, vc = pools[i % ncopy]
+            pa.pa_decode(out, q, kc, vc, bt, cl, scale, maxT, ws, P)
+        e1.record()
+        torch.cuda.synchronize()
+        plain_s = e0.elapsed_time(e1) / 1e3 / n_roof
 
     nb = algorithmic_bytes(step)
     ms_per_step = wall / args.steps * 1e3
@@ -760,7 +802,9 @@ def measure_decode(workload: str, args, cpu: bool) -> dict:
         "seq_tokens_per_s": round(nb["tokens"] / (wall / args.steps), 1),
         "decode_seq_tokens_per_s": round(nb["tokens"] / dec_s, 1),
         "roofline": {
-            "kernel": ("pa_decode: decode kernel (every sequence in one partition, no merge)"
+            "kernel": ("pa_decode_shared_prefix: group kernel (each shared tile scored once "
+                       "for all samples, then their own tokens; one launch)" if shared_api else
+                       "pa_decode: decode kernel (every sequence in one partition, no merge)"
                        if not split else
                        "pa_decode: decode kernel + partition-merge kernel (split sequences)"),
             "bound": "hbm",
@@ -781,6 +825,9 @@ def measure_decode(workload: str, args, cpu: bool) -> dict:
         # sequence's tokens, shared prefixes once per sequence) beside them
         res["roofline"]["logical_bytes_per_launch"] = nb["decode_logical"]
         res["roofline"]["logical_GB_per_s"] = round(nb["decode_logical"] / dec_s / 1e9, 2)
+    if plain_s is not None:
+        res["roofline"]["pa_decode_avg_launch_us"] = round(plain_s * 1e6, 3)
+        res["roofline"]["pa_decode_GB_per_s"] = round(nb["decode"] / plain_s / 1e9, 2)
     if cpu:
         res["cpu_baseline"] = cpu_baseline(step)
     del pools, kc0, vc0, q, bt, cl, copies, writes, out, ws

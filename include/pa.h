@@ -176,6 +176,53 @@ pa_status pa_decode_noalloc(void *out, const void *q, const void *k_cache, const
 pa_status pa_set_decode_kernel(pa_decode_kernel kernel);
 
 /*
+ * pa_decode_shared_prefix — pa_decode for a batch in which groups of sequences share the KV
+ * blocks of a common prefix, as the samples of one prompt do after fork.
+ * [PA-summary] "Memory sharing: copy-on-write for parallel decoding": the samples of a prompt
+ * hold its blocks by reference (the block manager raises their counts; pa_copy_blocks splits a
+ * shared block only when one of them writes into it). Every member's query heads attend to the
+ * same keys and values over the shared prefix, so each of the prefix's tiles is read and scored
+ * once per group (one matrix-core column per member and query head) instead of once per
+ * member; each member's own tokens follow in the same pass, and the running (max, sum, output)
+ * state of the block-wise attention equation carries from one to the other. The result is the
+ * attention pa_decode computes (within the attention tolerance; not bit for bit, the order of
+ * the sums differs).
+ * Groups: sequences group_start[i] .. group_start[i+1]-1 form group i (group_start: int32
+ * [num_groups + 1], device, group_start[0] = 0, non-decreasing, group_start[num_groups] =
+ * num_seqs; a group of one is allowed; pa_bm_prefix_groups computes it). prefix_lens: int32
+ * [num_seqs], device: the tokens each sequence shares with its group, the same value for every
+ * member of a group, at most each member's context length and at most max_prefix_len; the
+ * first ceil(prefix_lens[s]/B) entries of every member's block-table row must name the same
+ * physical blocks (0 for a sequence that shares nothing). A violation of these rules is a caller
+ * error: the result is undefined, but no access leaves the caller's buffers. The prefix is
+ * scored once in whole 32-token steps; the part short of a whole step is scored with each
+ * member's own tokens.
+ * max_group_size, max_prefix_len: host-known bounds (grid and workspace sizing).
+ * partition_tokens: 0 = automatic; > 0 (a multiple of 32, at most 8192) forces the tokens one
+ * workgroup covers of its list (the prefix, then the own tokens of the members it serves).
+ * workspace: >= pa_decode_shared_prefix_workspace_size(...) bytes, 256-byte aligned, any
+ * contents (may be NULL when that size is 0). f16/bf16 run on MFMA; f32 (and a forced
+ * vector-ALU kernel, see pa_set_decode_kernel) run pa_decode's path and ignore the groups.
+ */
+pa_status pa_decode_shared_prefix(void *out, const void *q, const void *k_cache,
+                                  const void *v_cache, const int32_t *block_tables,
+                                  const int32_t *context_lens, const int32_t *prefix_lens,
+                                  const int32_t *group_start, float scale, int num_seqs,
+                                  int num_groups, int num_q_heads, int num_kv_heads,
+                                  int head_dim, int block_size, int max_blocks_per_seq,
+                                  int64_t num_blocks, int max_context_len, int max_prefix_len,
+                                  int max_group_size, int partition_tokens, void *workspace,
+                                  size_t workspace_bytes, pa_dtype dt, void *stream);
+
+/* Bytes of workspace pa_decode_shared_prefix needs for these sizes (0 when none is needed, and
+ * for invalid sizes). */
+size_t pa_decode_shared_prefix_workspace_size(int num_seqs, int num_groups, int num_q_heads,
+                                              int num_kv_heads, int head_dim, int block_size,
+                                              int max_context_len, int max_prefix_len,
+                                              int max_group_size, int partition_tokens,
+                                              pa_dtype dt);
+
+/*
  * pa_prefill — causal multi-query (prefill / chunked-prefill) attention over the same block
  * pool and tables.
  * [PA-summary] "The PagedAttention algorithm": the kernel walks the block table for each query

@@ -120,6 +120,21 @@ int pa_bm_num_seq_blocks(const pa_bm *bm, int64_t seq);
 pa_status pa_bm_tables(const pa_bm *bm, const int64_t *seqs, int n, int32_t *out, int width,
                        int32_t pad);
 
+/*
+ * The prefix groups of a batch, for pa_decode_shared_prefix. [PA-summary] "Memory sharing:
+ * copy-on-write": forked sequences hold their parent's blocks by reference until one writes.
+ * Consecutive sequences of seqs[0..n) whose tables start with the same physical block form a
+ * group (every sequence is in exactly one; a sequence with no block, or whose first block
+ * differs from its predecessor's, starts a new group). A group's shared prefix is the number of
+ * leading table entries identical in every member, times block_size, capped by its shortest
+ * member's length (0 for a group of one).
+ * group_start: [n + 1] out (group i = positions group_start[i] .. group_start[i+1]-1 of seqs);
+ * *num_groups receives the group count; prefix_lens: [n] out, each sequence's shared tokens.
+ * An unknown sequence id: PA_ERR_INVALID_ARG, outputs unchanged.
+ */
+pa_status pa_bm_prefix_groups(const pa_bm *bm, const int64_t *seqs, int n, int32_t *group_start,
+                              int *num_groups, int32_t *prefix_lens);
+
 /* Reference count of a physical block (-1 outside the pool). */
 int32_t pa_bm_refcount(const pa_bm *bm, int64_t block);
 

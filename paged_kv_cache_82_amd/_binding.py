@@ -57,6 +57,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.pa_decode.restype = I
         lib.pa_decode_noalloc.argtypes = [P, P, P, P, P, P, F, I, I, I, I, I, I, I64, I, I, I, P]
         lib.pa_decode_noalloc.restype = I
+        lib.pa_decode_shared_prefix.argtypes = [P, P, P, P, P, P, P, P, F, I, I, I, I, I, I, I,
+                                                I64, I, I, I, I, P, SZ, I, P]
+        lib.pa_decode_shared_prefix.restype = I
+        lib.pa_decode_shared_prefix_workspace_size.argtypes = [I] * 10 + [I]
+        lib.pa_decode_shared_prefix_workspace_size.restype = SZ
         lib.pa_set_decode_kernel.argtypes = [I]
         lib.pa_set_decode_kernel.restype = I
         lib.pa_prefill.argtypes = [P, P, P, P, P, P, P, F, I, I, I, I, I, I, I, I64, I, I, I, P]
@@ -145,6 +150,34 @@ def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scal
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         _ptr(context_lens), float(scale), S, Hq, Hkv, d, B, block_tables.shape[1], N,
         int(max_context_len), int(partition_tokens), _dtype_code(q), _stream(stream)))
+
+
+def pa_decode_shared_prefix_workspace_size(num_seqs, num_groups, num_q_heads, num_kv_heads,
+                                           head_dim, block_size, max_context_len,
+                                           max_prefix_len, max_group_size, partition_tokens,
+                                           dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _DTYPE_NAMES[str(dtype).replace("torch.", "")]
+    return int(load().pa_decode_shared_prefix_workspace_size(
+        num_seqs, num_groups, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+        max_prefix_len, max_group_size, partition_tokens, code))
+
+
+def pa_decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens, prefix_lens,
+                            group_start, scale, max_context_len, max_prefix_len, max_group_size,
+                            workspace=None, partition_tokens=0, stream=None) -> None:
+    """pa_decode for groups of sequences sharing a prefix. prefix_lens int32 [S] (tokens each
+    sequence shares with its group), group_start int32 [G + 1] (group i = sequences
+    group_start[i] .. group_start[i+1]-1), both on the device; max_* are host-known bounds."""
+    S, Hq, d = q.shape
+    N, Hkv, B, _ = k_cache.shape
+    G = group_start.shape[0] - 1
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pa_decode_shared_prefix", load().pa_decode_shared_prefix(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), _ptr(prefix_lens), _ptr(group_start), float(scale), S, G, Hq, Hkv,
+        d, B, block_tables.shape[1], N, int(max_context_len), int(max_prefix_len),
+        int(max_group_size), int(partition_tokens), _ptr(workspace), ws_bytes, _dtype_code(q),
+        _stream(stream)))
 
 
 DECODE_KERNELS = {"auto": 0, "valu": 1, "mfma": 2}

@@ -49,6 +49,7 @@ def _lib():
             "pa_bm_tables": ([P, P, I, P, I, I32], I),
             "pa_bm_refcount": ([P, I64], I32),
             "pa_bm_get_stats": ([P, P], I),
+            "pa_bm_prefix_groups": ([P, P, I, P, P, P], I),
         }
         for name, (args, res) in sig.items():
             f = getattr(lib, name)
@@ -155,6 +156,18 @@ class BlockManager:
         _check("pa_bm_tables", self._lib.pa_bm_tables(self._h, _p(ids), len(ids), _p(out),
                                                       width, pad))
         return out
+
+    def prefix_groups(self, seqs):
+        """(group_start int32 [G + 1], prefix_lens int32 [len(seqs)]): consecutive sequences
+        whose tables start with the same block, and the tokens each shares with its group (the
+        inputs of pa_decode_shared_prefix)."""
+        ids = np.ascontiguousarray(seqs, np.int64)
+        gs = np.empty(len(ids) + 1, np.int32)
+        pl = np.empty(len(ids), np.int32)
+        ng = ctypes.c_int(0)
+        _check("pa_bm_prefix_groups", self._lib.pa_bm_prefix_groups(
+            self._h, _p(ids), len(ids), _p(gs), ctypes.byref(ng), _p(pl)))
+        return gs[: ng.value + 1].copy(), pl
 
     def refcount(self, block: int) -> int:
         return int(self._lib.pa_bm_refcount(self._h, block))

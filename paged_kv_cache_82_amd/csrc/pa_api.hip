@@ -174,6 +174,48 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
 }
 
 
+// Partition plan of pa_decode_shared_prefix (16-bit inputs, MFMA kernel). A workgroup serves
+// one (group, KV head, 16-column tile) and walks that tile's list of 32-token steps: the
+// group's shared prefix, then the own tokens of each member with a column in the tile. A list
+// longer than a partition (at most 256 steps, 64 per wave) is split; partitions shrink (to 32
+// steps) only while the grid would have fewer workgroups than the GPU has compute units.
+struct SharedPlan {
+  int ctiles, max_shared, steps, parts;
+  int64_t wgs;
+};
+
+bool shared_plan(int num_groups, int num_q_heads, int num_kv_heads, int max_context_len,
+                 int max_prefix_len, int max_group_size, int partition_tokens, SharedPlan* out) {
+  constexpr int kMaxSteps = 256;  // steps per partition: 64 per wave, one register of ids
+  constexpr int kCUs = 256;
+  if (num_groups < 0 || max_context_len < 0 || max_prefix_len < 0 || max_group_size < 1 ||
+      partition_tokens < 0 || partition_tokens % 32 || partition_tokens > 32 * kMaxSteps)
+    return false;
+  const int g = num_q_heads / num_kv_heads;
+  if ((int64_t)max_group_size * g > 16 * 4096) return false;
+  SharedPlan P{};
+  P.ctiles = (max_group_size * g + 15) / 16;
+  const int lmax = max_prefix_len < max_context_len ? max_prefix_len : max_context_len;
+  P.max_shared = num_groups > 0 ? (lmax / 32) * 32 : 0;  // no group: nothing is shared
+  // members with a column in one tile, and the longest list a tile can have
+  const int per_tile = max_group_size < (15 + g - 1) / g + 1 ? max_group_size
+                                                             : (15 + g - 1) / g + 1;
+  const int64_t bound = P.max_shared / 32 + (int64_t)per_tile * ((max_context_len + 31) / 32);
+  const int64_t units = (int64_t)num_groups * num_kv_heads * P.ctiles;
+  if (partition_tokens > 0) {
+    P.steps = partition_tokens / 32;
+  } else {
+    P.steps = kMaxSteps;
+    while (P.steps > 32 && units * ((bound + P.steps - 1) / P.steps) < kCUs) P.steps /= 2;
+  }
+  const int64_t parts = bound > 0 ? (bound + P.steps - 1) / P.steps : 1;
+  if (parts > (1 << 20)) return false;
+  P.parts = (int)parts;
+  P.wgs = units * P.parts;
+  *out = P;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -257,6 +299,103 @@ pa_status pa_set_decode_kernel(pa_decode_kernel kernel) {
     return PA_ERR_INVALID_ARG;
   g_decode_kernel.store((int)kernel, std::memory_order_relaxed);
   return PA_OK;
+}
+
+size_t pa_decode_shared_prefix_workspace_size(int num_seqs, int num_groups, int num_q_heads,
+                                              int num_kv_heads, int head_dim, int block_size,
+                                              int max_context_len, int max_prefix_len,
+                                              int max_group_size, int partition_tokens,
+                                              pa_dtype dt) {
+  if (!valid_dtype(dt) || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads || head_dim <= 0 || block_size <= 0 || max_context_len < 0)
+    return 0;
+  DecodePath path;
+  if (!choose_path(dt, num_q_heads, num_kv_heads, head_dim, block_size, &path)) return 0;
+  if (dt == PA_F32 || g_decode_kernel.load(std::memory_order_relaxed) == PA_DECODE_VALU)
+    return pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                    max_context_len, partition_tokens, dt);
+  SharedPlan P;
+  if (!shared_plan(num_groups, num_q_heads, num_kv_heads, max_context_len, max_prefix_len,
+                   max_group_size, partition_tokens, &P))
+    return 0;
+  return pa::workspace_layout(num_seqs, num_q_heads, head_dim, P.parts, true).total;
+}
+
+pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_tables,
+                                  const int32_t* context_lens, const int32_t* prefix_lens,
+                                  const int32_t* group_start, float scale, int num_seqs,
+                                  int num_groups, int num_q_heads, int num_kv_heads,
+                                  int head_dim, int block_size, int max_blocks_per_seq,
+                                  int64_t num_blocks, int max_context_len, int max_prefix_len,
+                                  int max_group_size, int partition_tokens, void* workspace,
+                                  size_t workspace_bytes, pa_dtype dt, void* stream) {
+  if (!valid_dtype(dt)) return PA_ERR_INVALID_ARG;
+  if (num_seqs < 0 || num_groups < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || block_size <= 0 || max_blocks_per_seq < 0 || num_blocks <= 0 ||
+      max_context_len < 0 || max_prefix_len < 0 || max_group_size < 1)
+    return PA_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads) return PA_ERR_INVALID_ARG;
+  if (pool_elems(num_blocks, num_kv_heads, block_size, head_dim) < 0) return PA_ERR_INVALID_ARG;
+  if (num_seqs > 65535 || num_q_heads > 65535) return PA_ERR_INVALID_ARG;
+  DecodePath path;
+  if (!choose_path(dt, num_q_heads, num_kv_heads, head_dim, block_size, &path))
+    return PA_ERR_UNSUPPORTED;
+  // fp32 (and a forced vector-ALU kernel): the same attention, through pa_decode's path
+  if (dt == PA_F32 || g_decode_kernel.load(std::memory_order_relaxed) == PA_DECODE_VALU)
+    return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_seqs,
+                       num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                       num_blocks, max_context_len, partition_tokens, workspace,
+                       workspace_bytes, false, dt, stream);
+  SharedPlan P;
+  if (!shared_plan(num_groups, num_q_heads, num_kv_heads, max_context_len, max_prefix_len,
+                   max_group_size, partition_tokens, &P))
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !prefix_lens ||
+      (num_groups > 0 && !group_start))
+    return PA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(out, elem_bytes(dt)) || !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
+      !aligned(prefix_lens, 4) || !aligned(group_start, 4))
+    return PA_ERR_INVALID_ARG;
+  if (P.wgs > 0xffffffffLL) return PA_ERR_INVALID_ARG;  // one-dimensional grid
+  const pa::WorkspaceLayout L =
+      pa::workspace_layout(num_seqs, num_q_heads, head_dim, P.parts, true);
+  if (workspace_bytes < L.total || (L.total > 0 && !workspace)) return PA_ERR_WORKSPACE;
+  if (L.total > 0 && !aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
+
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.partition_tokens = 32 * P.steps;
+  a.max_parts = P.parts;
+  char* ws = (char*)workspace;
+  a.part_m = L.total ? (float*)(ws + L.m_off) : nullptr;
+  a.part_l = L.total ? (float*)(ws + L.l_off) : nullptr;
+  a.part_o = L.total ? (float*)(ws + L.o_off) : nullptr;
+  a.part_n = L.total ? (int32_t*)(ws + L.n_off) : nullptr;
+  a.prefix_lens = prefix_lens;
+  a.group_start = group_start;
+  a.num_groups = num_groups;
+  a.group_steps = P.steps;
+  a.group_parts = P.parts;
+  a.shared_ctiles = P.ctiles;
+  a.max_shared = P.max_shared;
+  return from_hip(pa::launch_decode_shared((int)dt, head_dim, block_size, a,
+                                           (hipStream_t)stream));
 }
 
 pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,

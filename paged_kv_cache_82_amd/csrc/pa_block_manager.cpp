@@ -227,6 +227,46 @@ pa_status pa_bm_tables(const pa_bm* bm, const int64_t* seqs, int n, int32_t* out
   return PA_OK;
 }
 
+pa_status pa_bm_prefix_groups(const pa_bm* bm, const int64_t* seqs, int n, int32_t* group_start,
+                              int* num_groups, int32_t* prefix_lens) {
+  if (!bm || n < 0 || !num_groups || !group_start || (n > 0 && (!seqs || !prefix_lens)))
+    return PA_ERR_INVALID_ARG;
+  for (int i = 0; i < n; ++i)
+    if (!bm->find(seqs[i])) return PA_ERR_INVALID_ARG;
+  const int64_t B = bm->block_size;
+  int ng = 0;
+  for (int i = 0; i < n;) {
+    const pa_bm::Seq* lead = bm->find(seqs[i]);
+    // the run of sequences whose tables start with the leader's first block
+    int j = i + 1;
+    while (j < n && !lead->table.empty()) {
+      const pa_bm::Seq* t = bm->find(seqs[j]);
+      if (t->table.empty() || t->table[0] != lead->table[0]) break;
+      ++j;
+    }
+    int64_t shared = 0;
+    if (j - i > 1) {
+      // leading table entries common to every member, and the shortest member's length
+      size_t common = lead->table.size();
+      int64_t min_len = lead->len;
+      for (int k = i + 1; k < j; ++k) {
+        const pa_bm::Seq* t = bm->find(seqs[k]);
+        size_t c = 0;
+        while (c < common && c < t->table.size() && t->table[c] == lead->table[c]) ++c;
+        common = c;
+        min_len = std::min(min_len, t->len);
+      }
+      shared = std::min<int64_t>((int64_t)common * B, min_len);
+    }
+    group_start[ng++] = i;
+    for (int k = i; k < j; ++k) prefix_lens[k] = (int32_t)shared;
+    i = j;
+  }
+  group_start[ng] = n;
+  *num_groups = ng;
+  return PA_OK;
+}
+
 int32_t pa_bm_refcount(const pa_bm* bm, int64_t block) {
   if (!bm || block < 0 || block >= bm->num_blocks) return -1;
   return bm->ref[(size_t)block];

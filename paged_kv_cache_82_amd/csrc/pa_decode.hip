@@ -85,11 +85,29 @@ __device__ void store_zeros(const DecodeArgs& a, int s, int h0, int nh) {
 // Merge kernel: one workgroup of D threads per (query head, sequence) whose context spans more
 // than one partition. With M = max_p m_p and w_p = 2^(m_p - M):
 //   out = sum_p w_p o_p / sum_p w_p l_p          (the equation's rescaling, over partitions)
-template <DT dt, int D, int BS>
+// Tokens of sequence s that its group's shared pass covers (shared-prefix decode): its prefix
+// length within [0, T], rounded down to whole 32-token steps (the rest of the prefix is scored
+// with the sequence's own tokens).
+__device__ __forceinline__ int shared_len(const DecodeArgs& a, int s, int T) {
+  int L = a.prefix_lens[s];
+  L = L < 0 ? 0 : (L < T ? L : T);
+  L = (L / 32) * 32;
+  return L < a.max_shared ? L : a.max_shared;  // keeps every partial slot inside the workspace
+}
+
+// GROUP = false: sequence s is split into partitions of partition_tokens tokens. GROUP = true
+// (shared-prefix decode): the partition count its workgroups recorded, kept within the
+// workspace's slots.
+template <DT dt, int D, int BS, bool GROUP>
 __global__ __launch_bounds__(D) void merge_partitions_kernel(const DecodeArgs a) {
   const int h = blockIdx.x, s = blockIdx.y;
-  const int T = seq_len(a, s, BS);
-  const int nparts = (T + a.partition_tokens - 1) / a.partition_tokens;
+  int nparts;
+  if constexpr (GROUP) {
+    nparts = clampi(a.part_n[(int64_t)s * a.num_q_heads + h], 0, a.max_parts);
+  } else {
+    const int T = seq_len(a, s, BS);
+    nparts = (T + a.partition_tokens - 1) / a.partition_tokens;
+  }
   if (nparts <= 1) return;
   const int64_t base = ((int64_t)s * a.num_q_heads + h) * a.max_parts;
   // Partitions are read 8 at a time, so that their loads are in flight together (one at a
@@ -128,7 +146,8 @@ __global__ __launch_bounds__(D) void merge_partitions_kernel(const DecodeArgs a)
     acc = fmaf(wgt, a.part_o[(base + p) * D + dim], acc);
     L = fmaf(wgt, a.part_l[base + p], L);
   }
-  store_elem<dt>(a.out, ((int64_t)s * a.num_q_heads + h) * D + dim, acc / L);
+  // L == 0: no partition saw a token (a column of the shared-prefix decode); the output is 0
+  store_elem<dt>(a.out, ((int64_t)s * a.num_q_heads + h) * D + dim, L > 0.0f ? acc / L : 0.0f);
 }
 
 // ---- VALU kernel ------------------------------------------------------------------------
@@ -536,8 +555,98 @@ __device__ __forceinline__ void lds_read_k(u32x4 (&t)[2][2], const uint32_t (&ka
       : "v"(ka[0]), "v"(ka[1]), "i"(OFF), "i"(OFF + UOFF));
 }
 
-template <DT dt, int D, int BS, int NW, int NBUF, int MINB>
-__global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const DecodeArgs a) {
+// One workgroup of the MFMA decode: up to 16 query columns (lane hh's column reads its query
+// row at qrow, null for an empty column) against the tokens of one table row `bt`, KV head
+// kvh, in 32-token steps st0, st0 + 1, ... The block ids of at most max_steps steps are loaded
+// first, with the queries; end_fn() then returns the token at which the workgroup's range ends
+// (a range ending at or before token 32 * st0 means no work: the workgroup returns). The
+// workgroup's waves take the steps in turn, merge their (max, sum, output) states in LDS and
+// hand the merged state of each column to store(fm, fl, fo) (fo: [16][D]).
+// The LDS of one MFMA decode workgroup, declared once per kernel (a kernel may run the core
+// from more than one place).
+template <int D, int NW, int NBUF>
+struct MfmaSmem {
+  __attribute__((aligned(1024))) char k[NW][NBUF][32 * D * 2];  // K ring, one per wave
+  float o[NW][16][D];
+  float m[NW][16], l[NW][16];
+  float fm[16], fl[16];
+};
+
+// One 32-token step of an MFMA decode workgroup, as its step source describes it: `index`
+// (token / 32 of its first token; also its place in a block larger than a step), `valid` (the
+// tokens of the step that count, from its start; past 32 all do) and the columns of the tile it
+// serves, [clo, chi).
+struct StepDesc {
+  int index, valid, clo, chi;
+};
+
+// Consecutive steps st0, st0 + 1, ... of one table row, up to the token end_fn() returns,
+// every column; the wave takes steps st0 + w + k*NW.
+template <int BS, int NW, class EndFn>
+struct RangeSteps {
+  static constexpr int NBS = BS >= 32 ? 1 : 32 / BS;
+  static constexpr int SPB = BS > 32 ? BS / 32 : 1;
+  static constexpr bool kAllColumns = true;
+  const int32_t* bt;
+  int st0, max_steps, max_blocks, w;
+  EndFn end_fn;
+  int t1 = 0, ns = 0;
+  // Issued before the range's end is known, so the id, query and length loads overlap: lane k
+  // takes the NBS block ids of this wave's k-th step (when inside the table).
+  __device__ __forceinline__ void load_ids(int (&my_id)[NBS], int lane) const {
+#pragma unroll
+    for (int b = 0; b < NBS; ++b) {
+      my_id[b] = 0;
+      const int j = (st0 + w + lane * NW) * NBS / SPB + b;
+      if (lane < (max_steps + NW - 1) / NW && j < max_blocks) my_id[b] = bt[j];
+    }
+  }
+  // The range's end, after the id and query loads are issued; false: no work.
+  __device__ __forceinline__ bool finalize() {
+    // Uniform by construction; said so explicitly, because a value the callback returns past a
+    // divergent loop (the zero stores of an empty sequence) is otherwise taken as per-lane, and
+    // every buffer resource built from it would be loaded through a waterfall loop.
+    t1 = __builtin_amdgcn_readfirstlane(end_fn());
+    if (t1 <= 32 * st0) return false;
+    ns = ((t1 + 31) / 32 - st0 - w + NW - 1) / NW;
+    return true;
+  }
+  __device__ __forceinline__ StepDesc step(int k) const {
+    const int index = st0 + w + k * NW;
+    return {index, t1 - 32 * index, 0, 16};
+  }
+};
+
+// A step list given per lane: lane k describes the wave's k-th step (its table row, its token
+// index, and `meta` = valid << 10 | clo << 5 | chi); ns steps.
+template <int BS>
+struct ListSteps {
+  static constexpr int NBS = BS >= 32 ? 1 : 32 / BS;
+  static constexpr int SPB = BS > 32 ? BS / 32 : 1;
+  static constexpr bool kAllColumns = false;
+  const int32_t* row;  // lane k: the step's table row (null past the wave's steps)
+  int index, meta, ns, max_blocks;
+  __device__ __forceinline__ void load_ids(int (&my_id)[NBS], int lane) const {
+#pragma unroll
+    for (int b = 0; b < NBS; ++b) {
+      my_id[b] = 0;
+      const int j = index * NBS / SPB + b;
+      if (row && j < max_blocks) my_id[b] = row[j];
+    }
+  }
+  // Never an early return: ns is per wave, and a wave with no step must still hand its empty
+  // state to the workgroup's merge (the caller returns for a workgroup with no step at all).
+  __device__ __forceinline__ bool finalize() const { return true; }
+  __device__ __forceinline__ StepDesc step(int k) const {
+    const int mk = __builtin_amdgcn_readlane(meta, k);
+    return {__builtin_amdgcn_readlane(index, k), mk >> 10, (mk >> 5) & 31, mk & 31};
+  }
+};
+
+template <DT dt, int D, int BS, int NW, int NBUF, class Steps, class StoreFn>
+__device__ __forceinline__ void mfma_decode_run(MfmaSmem<D, NW, NBUF>& sm, const DecodeArgs& a,
+                                                int kvh, const char* qrow, Steps& steps,
+                                                StoreFn store) {
   static_assert(dt != DT::F32, "MFMA path takes 16-bit inputs");
   static_assert(32 % BS == 0 || BS % 32 == 0, "a 32-token step spans whole blocks or part of one");
   using M = MfmaT<dt>;
@@ -549,64 +658,36 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
   constexpr int NBS = BS >= 32 ? 1 : 32 / BS;  // blocks a step touches
   constexpr int SPB = BS > 32 ? BS / 32 : 1;    // steps per block
   constexpr int NT = NW * 64;
-  __shared__ __attribute__((aligned(1024))) char lds_k[NW][NBUF][32 * D * 2];  // K ring
-  __shared__ float lds_o[NW][16][D];
-  __shared__ float lds_m[NW][16], lds_l[NW][16];
-  __shared__ float lds_fm[16], lds_fl[16];
+  auto& lds_k = sm.k;
+  auto& lds_o = sm.o;
+  auto& lds_m = sm.m;
+  auto& lds_l = sm.l;
+  auto& lds_fm = sm.fm;
+  auto& lds_fl = sm.fl;
 
-  const int p = blockIdx.x, unit = blockIdx.y;
-  const int s = blockIdx.z;
-  const int Hq = a.num_q_heads;
-  const int g = Hq / a.num_kv_heads;
-  const int ntile = (g + 15) / 16;
-  const int kvh = unit / ntile, ht = unit % ntile;
-  const int h0 = kvh * g + ht * 16;
-  const int nh = (g - ht * 16 < 16) ? g - ht * 16 : 16;
-  const int P = a.partition_tokens;
-  const int st0 = p * (P / 32);
   const int lane = threadIdx.x & 63;
   const int w = wave_id();
   const int hh = lane & 15, gq = lane >> 4;
 
-  // Issued before the context length is known, so the id, query and length loads overlap:
-  // lane k takes the NBS block ids of this wave's k-th 32-token step (when inside the table).
-  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   int my_id[NBS];
-#pragma unroll
-  for (int b = 0; b < NBS; ++b) {
-    my_id[b] = 0;
-    const int j = (st0 + w + lane * NW) * NBS / SPB + b;
-    if (lane < (P / 32 + NW - 1) / NW && j < a.max_blocks_per_seq) my_id[b] = bt[j];
-  }
-  // Q^T operand: column hh = query head h0 + hh, k = head dims 32*kk + 8*gq + e.
+  steps.load_ids(my_id, lane);
+  // Q^T operand: column hh, k = head dims 32*kk + 8*gq + e.
   vec8 qop[KC];
 #pragma unroll
   for (int kk = 0; kk < KC; ++kk) {
     u32x4 raw = {0u, 0u, 0u, 0u};
-    if (hh < nh)
-      raw = load16((const char*)a.q +
-                   (((int64_t)s * Hq + h0 + hh) * D + 32 * kk + 8 * gq) * E);
+    if (qrow) raw = load16(qrow + (32 * kk + 8 * gq) * E);
     qop[kk] = __builtin_bit_cast(vec8, raw);
   }
-
-  const int T = seq_len(a, s, BS);
-  const int nparts = (T + P - 1) / P;
-  if (T == 0) {
-    if (p == 0) store_zeros<dt, D, NT>(a, s, h0, nh);
-    return;
-  }
-  if (p >= nparts) return;
-  const int t1 = (T < (p + 1) * P) ? T : (p + 1) * P;
-  const int st1 = (t1 + 31) / 32;
-  const int jlast = (t1 - 1) / BS;  // last block of this partition
+  if (!steps.finalize()) return;  // a step source returns false for the whole workgroup only
 
   f32x4 oacc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = kNegInf, lsum = 0.0f;
 
-  // This wave takes steps st0 + w + k*NW, k < ns; lane k holds the NBS physical ids of step k.
-  const int ns = (st1 - st0 - w + NW - 1) / NW;
+  // This wave's steps k < ns; lane k holds the NBS physical ids of step k.
+  const int ns = steps.ns;
   const int64_t Hkv = a.num_kv_heads;
 
   constexpr int RB = D * E;  // bytes per token row
@@ -661,9 +742,8 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
     constexpr int slot = decltype(slotc)::value;
     const bool live = k < ns;
     const int kq = live ? k : 0;
-    const int step = st0 + w + k * NW;
-    const int jfirst = step * NBS / SPB;  // block of the step's first token
-    // Blocks larger than a step: the step's 32 rows start (step % SPB) * 32 rows into its block,
+    const StepDesc sd = steps.step(kq);
+    // Blocks larger than a step: the step's 32 rows start (index % SPB) * 32 rows into its block,
     // and its resources span those rows only.
     constexpr int span = BS > 32 ? 32 * RB : (int)(BS * RB);
     __amdgpu_buffer_rsrc_t kr[NBS];
@@ -673,8 +753,8 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
     for (int b = 0; b < NBS; ++b) {
       const int id = clamp_id(__builtin_amdgcn_readlane(my_id[b], kq), id_max);
       tile[b] = (int64_t)id * blk_stride;
-      if constexpr (SPB > 1) tile[b] += (int64_t)((step % SPB) * span);
-      has[b] = live && jfirst + b <= jlast;
+      if constexpr (SPB > 1) tile[b] += (int64_t)((sd.index % SPB) * span);
+      has[b] = live && b * BS < sd.valid;  // the block holds a token the step uses
       kr[b] = tile_rsrc(kbase + tile[b], has[b] ? span : 0);
     }
     // K first, then V: 0.7% faster on the GQA batch than the other order (measured on MI355X).
@@ -709,7 +789,9 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
 
   auto consume = [&](int k, auto slotc, VRegs<D>& R) {
     constexpr int slot = decltype(slotc)::value;
-    const int tau0 = (st0 + w + k * NW) * 32;
+    const StepDesc sd = steps.step(k);
+    // token r of the step counts for this lane's column: r < valid, and the column is served
+    const bool col_ok = Steps::kAllColumns || (hh >= sd.clo && hh < sd.chi);
     // This step's K loads (and all loads issued before them) are done once at most its own 8 V
     // loads and those of the NBUF - 1 later fetches (8 V and KD K loads each) are outstanding.
     wait_vmcnt<(NBUF - 1) * (8 + KD) + 8>();
@@ -724,14 +806,14 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
       for (int kk = 0; kk < KC; ++kk)
         sacc[u] = M::mma(__builtin_bit_cast(vec8, kf[u][kk]), qop[kk], sacc[u]);
     }
-    const bool tail = tau0 + 32 > t1;
+    const bool tail = sd.valid < 32 || (!Steps::kAllColumns && (sd.clo > 0 || sd.chi < 16));
     float sc[8];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float x = sacc[u][i] * a.scale_log2;
-        if (tail && tau0 + 16 * u + 4 * gq + i >= t1) x = kNegInf;
+        if (tail && (16 * u + 4 * gq + i >= sd.valid || !col_ok)) x = kNegInf;
         sc[4 * u + i] = x;
       }
     float bm = sc[0];
@@ -756,12 +838,12 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
     lsum = fmaf(lsum, corr, ps);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) oacc[mt] *= corr;
-    if (tail) {
+    if (tail) {  // V rows past the step's valid tokens may hold anything, NaN included
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (tau0 + 16 * u + 4 * gq + i >= t1) R.v[u][i] = typename VF::T{};  // select
+          if (16 * u + 4 * gq + i >= sd.valid) R.v[u][i] = typename VF::T{};  // select
     }
     // O^T += V^T P^T with k element e <-> token 16*(e/4) + 4*gq + (e%4).
 #pragma unroll
@@ -830,7 +912,193 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
     fo[idx] = acc;
   }
   __syncthreads();
-  finish_partition<dt, D, NT>(a, s, h0, nh, p, nparts, lds_fm, lds_fl, fo);
+  store(lds_fm, lds_fl, fo);
+}
+
+template <DT dt, int D, int BS, int NW, int NBUF, int MINB>
+__global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const DecodeArgs a) {
+  constexpr int NT = NW * 64;
+  const int p = blockIdx.x, unit = blockIdx.y;
+  const int s = blockIdx.z;
+  const int Hq = a.num_q_heads;
+  const int g = Hq / a.num_kv_heads;
+  const int ntile = (g + 15) / 16;
+  const int kvh = unit / ntile, ht = unit % ntile;
+  const int h0 = kvh * g + ht * 16;
+  const int nh = (g - ht * 16 < 16) ? g - ht * 16 : 16;
+  const int P = a.partition_tokens;
+  const int hh = threadIdx.x & 15;
+  // column hh = query head h0 + hh of sequence s
+  const char* qrow =
+      hh < nh ? (const char*)a.q + ((int64_t)s * Hq + h0 + hh) * D * 2 : nullptr;
+  int nparts = 0;
+  __shared__ MfmaSmem<D, NW, NBUF> sm;
+  auto end_fn = [&]() -> int {
+    const int T = seq_len(a, s, BS);
+    nparts = (T + P - 1) / P;
+    if (T == 0) {
+      if (p == 0) store_zeros<dt, D, NT>(a, s, h0, nh);
+      return 0;
+    }
+    if (p >= nparts) return 0;
+    return (T < (p + 1) * P) ? T : (p + 1) * P;
+  };
+  RangeSteps<BS, NW, decltype(end_fn)> steps{a.block_tables + (int64_t)s * a.max_blocks_per_seq,
+                                             p * (P / 32), P / 32, a.max_blocks_per_seq,
+                                             wave_id(), end_fn};
+  mfma_decode_run<dt, D, BS, NW, NBUF>(
+      sm, a, kvh, qrow, steps, [&](const float* fm, const float* fl, const float* fo) {
+        finish_partition<dt, D, NT>(a, s, h0, nh, p, nparts, fm, fl, fo);
+      });
+}
+
+// ---- shared-prefix decode ------------------------------------------------------------------
+// [PA-summary] "Memory sharing: copy-on-write for parallel decoding": the samples of one prompt
+// hold the prompt's blocks by reference, so the same K/V tiles serve every sample. Against one
+// such tile the members' query heads form a dense [members*g x d] . [d x B] contraction: one
+// MFMA column per (member, query head). A workgroup serves one (group, KV head, 16-column tile)
+// and walks a list of 32-token steps: the group's shared prefix through the first member's table
+// (every column), then each member's own tokens through its own table (that member's columns
+// only; the others take -inf scores and are left unchanged by the rescaled update). Every
+// column's running (max, sum, output) state simply continues from one part of the list to the
+// next, so a list that fits one workgroup needs no partials and no merge. Longer lists are cut
+// into partitions whose partials the merge kernel combines.
+
+// The merged state of a group workgroup: column k is (member c / g, query head c % g of KV head
+// kvh), c = 16*ct + k. With one partition the final output (0 for a column that saw no token);
+// otherwise a partial in slot p. Partition 0 records the partition count for the merge.
+template <DT dt, int D, int NT>
+__device__ void finish_group(const DecodeArgs& a, int s0, int ncols, int ct, int kvh, int p,
+                             int nparts, const float* fm, const float* fl, const float* fo) {
+  const int Hq = a.num_q_heads, g = Hq / a.num_kv_heads;
+  const int nk = ncols - 16 * ct < 16 ? ncols - 16 * ct : 16;
+  const int tid = threadIdx.x;
+  const int MP = a.max_parts;
+  for (int idx = tid; idx < nk * D; idx += NT) {
+    const int k = idx / D, dim = idx % D;
+    const int c = 16 * ct + k;
+    const int64_t row = (int64_t)(s0 + c / g) * Hq + kvh * g + c % g;
+    if (nparts == 1)
+      store_elem<dt>(a.out, row * D + dim, fl[k] > 0.0f ? fo[idx] / fl[k] : 0.0f);
+    else
+      a.part_o[(row * MP + p) * D + dim] = fo[idx];
+  }
+  if (tid < nk) {
+    const int c = 16 * ct + tid;
+    const int64_t row = (int64_t)(s0 + c / g) * Hq + kvh * g + c % g;
+    if (nparts > 1) {
+      a.part_m[row * MP + p] = fm[tid];
+      a.part_l[row * MP + p] = fl[tid];
+    }
+    if (p == 0 && a.part_n) a.part_n[row] = nparts;
+  }
+}
+
+template <DT dt, int D, int BS, int NW, int NBUF, int MINB>
+__global__ __launch_bounds__(NW * 64, MINB) void decode_group_kernel(const DecodeArgs a) {
+  constexpr int NT = NW * 64;
+  __shared__ MfmaSmem<D, NW, NBUF> sm;
+  // grid: (partition, KV head x column tile, group), partition fastest
+  const int64_t L = blockIdx.x;
+  const int np = a.group_parts;
+  const int p = (int)(L % np);
+  const int64_t rest = L / np;
+  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+  const int g = Hq / Hkv;
+  const int units = Hkv * a.shared_ctiles;
+  const int unit = (int)(rest % units);
+  const int gi = (int)(rest / units);
+  const int kvh = unit / a.shared_ctiles, ct = unit % a.shared_ctiles;
+  const int S = a.num_seqs;
+  const int s0 = clampi(a.group_start[gi], 0, S);
+  const int s1 = clampi(a.group_start[gi + 1], s0, S);
+  const int ncols = (s1 - s0) * g;
+  if (16 * ct >= ncols) return;  // uniform: the tile serves no column
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id();
+  const int hh = lane & 15;
+  // Members with a column in this tile: m0 .. m1 - 1, at most 16.
+  const int m0 = (16 * ct) / g;
+  const int m1 = (s1 - s0) < (16 * ct + 15) / g + 1 ? (s1 - s0) : (16 * ct + 15) / g + 1;
+  const int nm = m1 - m0;
+  // Lane j < nm: member m0 + j's length and its own steps; the shared prefix from the first
+  // member (whole 32-token steps).
+  const int Tj = lane < nm ? seq_len(a, s0 + m0 + lane, BS) : 0;
+  const int Lg = shared_len(a, s0, seq_len(a, s0, BS));
+  const int nS = Lg / 32;
+  const int nPj = (lane < nm && Tj > Lg) ? (Tj - Lg + 31) / 32 : 0;
+  // offj: first step of member j's own tokens in the list (lane j); total: the list's length
+  int offj = nS, total = nS;
+  for (int j = 0; j < nm; ++j) {  // uniform, at most 16
+    const int nj = __builtin_amdgcn_readlane(nPj, j);
+    if (lane == j) offj = total;
+    total += nj;
+  }
+  // Uniform by construction; said so, because the loop that sums it also takes a per-lane
+  // branch, after which the compiler takes it as per-lane (and would load every buffer
+  // resource built from it through a waterfall loop).
+  total = __builtin_amdgcn_readfirstlane(total);
+  const int SP = a.group_steps;
+  const int nparts = (total + SP - 1) / SP < np ? (total + SP - 1) / SP : np;
+  const int c = 16 * ct + hh;
+  if (total == 0) {  // no token in the whole tile (every member empty): zero outputs
+    if (p == 0) {
+      const int nk = ncols - 16 * ct < 16 ? ncols - 16 * ct : 16;
+      for (int idx = threadIdx.x; idx < nk * D; idx += NT) {
+        const int k = idx / D, cc = 16 * ct + k;
+        store_elem<dt>(a.out, ((int64_t)(s0 + cc / g) * Hq + kvh * g + cc % g) * D + idx % D,
+                       0.0f);
+      }
+      if (threadIdx.x < nk && a.part_n) {
+        const int cc = 16 * ct + threadIdx.x;
+        a.part_n[(int64_t)(s0 + cc / g) * Hq + kvh * g + cc % g] = 1;
+      }
+    }
+    return;
+  }
+  const int pbeg = p * SP;
+  const int pend = total < pbeg + SP ? total : pbeg + SP;
+  if (pbeg >= pend) return;  // uniform: a partition past the list
+  // Lane k: the wave's k-th step of this partition, list position pbeg + w + k*NW.
+  const int gs = pbeg + w + lane * NW;
+  const int M = a.max_blocks_per_seq;
+  // The member whose own tokens hold list position gs (the last one starting at or before it;
+  // members with no own tokens share their start with the next), found by every lane in uniform
+  // control flow so that the lane shuffle reads only active lanes.
+  int jj = 0, off = nS;
+  for (int j = 0; j < nm; ++j) {  // uniform loop, per-lane choice
+    const int oj = __builtin_amdgcn_readlane(offj, j);
+    if (gs >= oj) {
+      jj = j;
+      off = oj;
+    }
+  }
+  const int Tjj = __shfl(Tj, jj);
+  const int32_t* row = nullptr;
+  int index = 0, meta = 0;
+  if (gs < pend) {
+    if (gs < nS) {  // the shared prefix: every column
+      row = a.block_tables + (int64_t)s0 * M;
+      index = gs;
+      meta = (32 << 10) | (0 << 5) | 16;
+    } else {  // member jj's own tokens: its columns only
+      const int tau0 = Lg + 32 * (gs - off);
+      const int valid = Tjj - tau0 < 32 ? Tjj - tau0 : 32;
+      const int lo = (m0 + jj) * g - 16 * ct, hi = lo + g;
+      row = a.block_tables + (int64_t)(s0 + m0 + jj) * M;
+      index = tau0 / 32;
+      meta = (valid << 10) | ((lo > 0 ? lo : 0) << 5) | (hi < 16 ? hi : 16);
+    }
+  }
+  ListSteps<BS> steps{row, index, meta, (pend - pbeg - w + NW - 1) / NW, M};
+  if (steps.ns < 0) steps.ns = 0;
+  const char* qrow = c < ncols ? (const char*)a.q +
+                                     ((int64_t)(s0 + c / g) * Hq + kvh * g + c % g) * D * 2
+                               : nullptr;
+  mfma_decode_run<dt, D, BS, NW, NBUF>(
+      sm, a, kvh, qrow, steps, [&](const float* fm, const float* fl, const float* fo) {
+        finish_group<dt, D, NT>(a, s0, ncols, ct, kvh, p, nparts, fm, fl, fo);
+      });
 }
 
 // ---- host launchers -----------------------------------------------------------------------
@@ -852,7 +1120,8 @@ constexpr int valu_buffers() {
 constexpr int kMfmaBuffers = 3;    // MFMA kernel: 32-token steps in registers
 constexpr int kMfmaMinBlocks = 1;  // MFMA kernel: workgroups per CU the registers must allow
 
-WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_parts) {
+WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_parts,
+                                 bool with_counts) {
   WorkspaceLayout L{};
   if (max_parts <= 1 || num_seqs <= 0) return L;  // a single partition needs no workspace
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -860,7 +1129,8 @@ WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int head_dim, in
   L.m_off = 0;
   L.l_off = up(L.m_off + sh * max_parts * sizeof(float));
   L.o_off = up(L.l_off + sh * max_parts * sizeof(float));
-  L.total = up(L.o_off + sh * max_parts * (size_t)head_dim * sizeof(float));
+  L.n_off = up(L.o_off + sh * max_parts * (size_t)head_dim * sizeof(float));
+  L.total = with_counts ? up(L.n_off + sh * sizeof(int32_t)) : L.n_off;
   return L;
 }
 
@@ -930,7 +1200,7 @@ static hipError_t launch_t(DecodePath path, const DecodeArgs& a, hipStream_t str
   }
   hipError_t e = hipLaunchKernel(fn, grid, block, args, 0, stream);
   if (e != hipSuccess || a.max_parts <= 1) return e;
-  return hipLaunchKernel((const void*)merge_partitions_kernel<dt, D, BS>,
+  return hipLaunchKernel((const void*)merge_partitions_kernel<dt, D, BS, false>,
                          dim3((unsigned)a.num_q_heads, (unsigned)a.num_seqs), dim3(D), args, 0,
                          stream);
 }
@@ -951,6 +1221,52 @@ static hipError_t launch_d(DecodePath path, int d, int bs, const DecodeArgs& a, 
   switch (d) {
     case 64: return launch_bs<dt, 64>(path, bs, a, st);
     case 128: return launch_bs<dt, 128>(path, bs, a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <DT dt, int D, int BS>
+static hipError_t launch_shared_t(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t total = (int64_t)a.num_groups * a.num_kv_heads * a.shared_ctiles * a.group_parts;
+  if (total == 0) return hipSuccess;
+  if (total > 0xffffffffLL) return hipErrorInvalidValue;  // the API checks this first
+  DecodeArgs args_copy = a;
+  void* args[] = {&args_copy};
+  hipError_t e = hipLaunchKernel(
+      (const void*)decode_group_kernel<dt, D, BS, kWaves, kMfmaBuffers, kMfmaMinBlocks>,
+      dim3((unsigned)total), dim3(kWaves * 64), args, 0, stream);
+  if (e != hipSuccess || a.max_parts <= 1) return e;
+  return hipLaunchKernel((const void*)merge_partitions_kernel<dt, D, BS, true>,
+                         dim3((unsigned)a.num_q_heads, (unsigned)a.num_seqs), dim3(D), args, 0,
+                         stream);
+}
+
+template <DT dt, int D>
+static hipError_t launch_shared_bs(int bs, const DecodeArgs& a, hipStream_t st) {
+  switch (bs) {
+    case 8: return launch_shared_t<dt, D, 8>(a, st);
+    case 16: return launch_shared_t<dt, D, 16>(a, st);
+    case 32: return launch_shared_t<dt, D, 32>(a, st);
+    case 64: return launch_shared_t<dt, D, 64>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <DT dt>
+static hipError_t launch_shared_d(int d, int bs, const DecodeArgs& a, hipStream_t st) {
+  switch (d) {
+    case 64: return launch_shared_bs<dt, 64>(bs, a, st);
+    case 128: return launch_shared_bs<dt, 128>(bs, a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_shared(int dt, int head_dim, int block_size, const DecodeArgs& a,
+                                hipStream_t stream) {
+  if (a.num_seqs == 0) return hipSuccess;
+  switch (dt) {
+    case 1: return launch_shared_d<DT::F16>(head_dim, block_size, a, stream);
+    case 2: return launch_shared_d<DT::BF16>(head_dim, block_size, a, stream);
     default: return hipErrorInvalidValue;
   }
 }

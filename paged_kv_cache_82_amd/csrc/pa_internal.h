@@ -27,19 +27,40 @@ struct DecodeArgs {
   float* part_m;         // [S][Hq][max_parts]   running maxima (base-2 domain)
   float* part_l;         // [S][Hq][max_parts]   running sums
   float* part_o;         // [S][Hq][max_parts][D] unnormalised partial outputs
+  // Shared-prefix decode only (pa_decode_shared_prefix; null / 0 otherwise). Sequences
+  // group_start[i] .. group_start[i+1]-1 form group i and share their first prefix_lens[s]
+  // tokens. A workgroup serves one (group, KV head, 16-column tile): its steps are the group's
+  // prefix (32-token steps through the first member's table, every column of the tile), then
+  // each member's own tokens (through its table, its columns only), cut into partitions of
+  // group_steps steps when longer.
+  const int32_t* prefix_lens;  // [S]
+  const int32_t* group_start;  // [num_groups + 1]
+  int num_groups;
+  int group_steps;       // steps per partition (at most 64 per wave)
+  int group_parts;       // partitions per (group, KV head, column tile)
+  int shared_ctiles;     // 16-column tiles of the largest group (members x query heads per KV head)
+  int max_shared;        // host bound on the shared tokens of any sequence (a multiple of 32)
+  int32_t* part_n;       // [S][Hq] partitions each (sequence, query head) was split into
 };
 
 // Workspace layout for a given problem: byte offsets of each region.
 struct WorkspaceLayout {
-  size_t m_off, l_off, o_off, total;
+  size_t m_off, l_off, o_off, n_off, total;
 };
-WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_parts);
+// with_counts: a [S][Hq] int32 partition count per (sequence, query head) after the partials
+// (the shared-prefix decode, whose partition counts the merge kernel cannot derive).
+WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_parts,
+                                 bool with_counts = false);
 
 enum class DecodePath : int { Valu = 0, Mfma = 1 };
 
 // Launchers return hipSuccess or the launch error. `dt` uses pa_dtype codes.
 hipError_t launch_decode(DecodePath path, int dt, int head_dim, int block_size,
                          const DecodeArgs& a, hipStream_t stream);
+// Shared-prefix decode (16-bit inputs): the shared pass and every sequence's own tokens in one
+// MFMA launch, then the merge of each (sequence, query head)'s partials.
+hipError_t launch_decode_shared(int dt, int head_dim, int block_size, const DecodeArgs& a,
+                                hipStream_t stream);
 bool decode_supported(DecodePath path, int dt, int head_dim, int block_size);
 int decode_units_per_seq(DecodePath path, int num_q_heads, int num_kv_heads);
 // Largest partition (tokens) a launch supports: a wave keeps its block ids in one register.

@@ -244,3 +244,39 @@ def pools_equal(dev_pool: torch.Tensor, host_pool: np.ndarray, dtype: str,
         if not torch.equal(dev_pool[i:i + per].view(ity), want.view(ity)):
             return False
     return True
+
+
+def share_prefixes(step, groups):
+    """Make runs of consecutive sequences of a DecodeStep share leading blocks: groups is a list
+    of (first, count, blocks); members first+1 .. first+count-1 point their first `blocks` table
+    entries at the first member's blocks (so their first blocks*B tokens become the first
+    member's). The shared blocks must end before every member's last token (which the step
+    writes). Returns (group_start, prefix_lens) covering every sequence (a sequence in no listed
+    group is a group of one with prefix 0). Test infrastructure."""
+    S, B = step.num_seqs, step.block_size
+    pl = np.zeros(S, np.int32)
+    starts, covered = [], np.zeros(S, bool)
+    spec = {first: (count, blocks) for first, count, blocks in groups}
+    s = 0
+    while s < S:
+        starts.append(s)
+        if s in spec:
+            count, blocks = spec[s]
+            T = step.context_lens[s:s + count]
+            assert blocks * B <= int(T.min()) - 1, "shared blocks must end before every last token"
+            for m in range(s + 1, s + count):
+                step.block_tables[m, :blocks] = step.block_tables[s, :blocks]
+            pl[s:s + count] = blocks * B
+            covered[s:s + count] = True
+            s += count
+        else:
+            s += 1
+    starts.append(S)
+    return np.asarray(starts, np.int32), pl
+
+
+
+def groups_from_tables(block_tables, context_lens, B):
+    from workloads import prefix_groups
+
+    return prefix_groups(block_tables, context_lens, B)

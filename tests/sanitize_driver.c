@@ -225,6 +225,15 @@ static void check_block_manager(int B) {
   for (int j = 0; j < 2; ++j) CHECK(pa_bm_refcount(bm, tables[j]) == 3);
   CHECK(pa_bm_refcount(bm, N) == -1);
 
+  int32_t gstart[4], pls[3];
+  int ng = -1;
+  CHECK(pa_bm_prefix_groups(bm, seqs, 3, gstart, &ng, pls) == PA_OK);
+  CHECK(ng == 1 && gstart[0] == 0 && gstart[1] == 3);
+  CHECK(pls[0] == pls[1] && pls[1] == pls[2] && pls[0] >= 2 * B);
+  const int64_t unknown[2] = {10, 99};
+  CHECK(pa_bm_prefix_groups(bm, unknown, 2, gstart, &ng, pls) == PA_ERR_INVALID_ARG);
+  CHECK(pa_bm_prefix_groups(bm, NULL, 0, gstart, &ng, NULL) == PA_OK && ng == 0 && gstart[0] == 0);
+
   pa_bm_stats st;
   CHECK(pa_bm_get_stats(bm, &st) == PA_OK);
   CHECK(st.free_blocks + st.used_blocks == N);

@@ -41,6 +41,8 @@ def declared_functions(header=HEADER):
 
 def test_header_declares_the_calls():
     assert declared_functions() == ["pa_copy_blocks", "pa_decode", "pa_decode_noalloc",
+                                    "pa_decode_shared_prefix",
+                                    "pa_decode_shared_prefix_workspace_size",
                                     "pa_decode_workspace_size", "pa_prefill",
                                     "pa_set_decode_kernel", "pa_status_string",
                                     "pa_swap_blocks", "pa_write_kv"]
@@ -50,7 +52,7 @@ def test_block_manager_header_declares_the_calls():
     assert declared_functions(BM_HEADER) == [
         "pa_bm_add", "pa_bm_append", "pa_bm_blocks_needed", "pa_bm_create", "pa_bm_destroy",
         "pa_bm_fork", "pa_bm_get_stats", "pa_bm_length", "pa_bm_move", "pa_bm_num_seq_blocks",
-        "pa_bm_refcount", "pa_bm_release", "pa_bm_tables"]
+        "pa_bm_prefix_groups", "pa_bm_refcount", "pa_bm_release", "pa_bm_tables"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -245,3 +247,41 @@ def test_binding_shares_torchs_hip_runtime():
             "libs = set(re.findall(r'\\S*libamdhip64\\S*', maps)); print(libs)\n"
             "assert len(libs) == 1, libs\n") % ROOT
     subprocess.run([__import__("sys").executable, "-c", code], check=True)
+
+
+def test_decode_shared_prefix_argument_checks(lib):
+    f = lib.pa_decode_shared_prefix
+    names = ["out", "q", "k", "v", "bt", "cl", "pl", "gs", "scale", "S", "G", "Hq", "Hkv", "d",
+             "B", "M", "N", "maxT", "maxL", "maxG", "P", "ws", "wsb", "dt", "stream"]
+    args = [BAD, BAD, BAD, BAD, BAD, BAD, BAD, BAD, 0.125, 8, 2, 8, 8, 128, 16, 64, 512, 1000,
+            512, 4, 0, None, 0, F16, None]
+
+    def call(**kw):
+        a = list(args)
+        for k, val in kw.items():
+            a[names.index(k)] = val
+        return f(*a)
+
+    assert call(S=0) == PA_OK
+    assert call(pl=None) == PA_ERR_INVALID_ARG
+    assert call(gs=None) == PA_ERR_INVALID_ARG
+    assert call(maxG=0) == PA_ERR_INVALID_ARG
+    assert call(P=48) == PA_ERR_INVALID_ARG
+    assert call(P=16384) == PA_ERR_INVALID_ARG
+    assert call(d=96) == PA_ERR_UNSUPPORTED
+    assert call(Hq=8, Hkv=3) == PA_ERR_INVALID_ARG
+    ws = lib.pa_decode_shared_prefix_workspace_size
+    # lists of up to 16 + 4 x 32 steps fit one partition of 8192 tokens: no workspace (the
+    # automatic plan cuts them smaller here, to give this small grid more workgroups)
+    assert ws(8, 2, 8, 8, 128, 16, 1000, 512, 4, 8192, F16) == 0
+    assert ws(8, 2, 8, 8, 128, 16, 1000, 512, 4, 0, F16) > 0
+    # forced 256-token partitions: the list splits, the partials and counts need a workspace
+    need = ws(8, 2, 8, 8, 128, 16, 1000, 512, 4, 256, F16)
+    parts = -(-(512 // 32 + 4 * 32) // 8)
+    assert need >= 8 * 8 * parts * (128 + 2) * 4 + 8 * 8 * 4
+    assert call(P=256) == PA_ERR_WORKSPACE
+    assert call(P=256, ws=V(0x1010), wsb=need) == PA_ERR_INVALID_ARG  # misaligned
+    # fp32 takes pa_decode's path and needs what pa_decode needs
+    assert ws(8, 2, 8, 8, 128, 16, 1000, 512, 4, 0, F32) == lib.pa_decode_workspace_size(
+        8, 8, 8, 128, 16, 1000, 0, F32)
+    assert ws(8, 2, 8, 8, 128, 16, 1000, 512, 0, 0, F16) == 0  # invalid group bound

@@ -204,3 +204,68 @@ def test_tutorial_workflow_allocation():
         bm.append(1, 1)
         if str(step) in fx["pages_in_use_after_step"]:
             assert bm.num_seq_blocks(1) == fx["pages_in_use_after_step"][str(step)]
+
+
+def _groups_by_hand(tables, lens, B):
+    """Runs of consecutive sequences with the same first block; shared tokens = common leading
+    entries x B, capped by the shortest member (0 for a run of one)."""
+    starts, pl, i, n = [], [0] * len(tables), 0, len(tables)
+    while i < n:
+        j = i + 1
+        while j < n and len(tables[i]) and len(tables[j]) and tables[j][0] == tables[i][0]:
+            j += 1
+        shared = 0
+        if j - i > 1:
+            c = 0
+            while all(c < len(tables[k]) and tables[k][c] == tables[i][c] for k in range(i, j)):
+                c += 1
+            shared = min(c * B, min(lens[i:j]))
+        starts.append(i)
+        for k in range(i, j):
+            pl[k] = shared
+        i = j
+    return starts + [n], pl
+
+
+def test_prefix_groups_of_forked_samples():
+    rng = np.random.default_rng(5)
+    for trial in range(30):
+        B = int(rng.choice([1, 4, 16, 32]))
+        bm = BlockManager(4000, B, rng.permutation(4000))
+        order, sid = [], 0
+        for prompt in range(int(rng.integers(1, 6))):
+            root = sid
+            sid += 1
+            bm.add(root)
+            bm.append(root, int(rng.integers(0, 5 * B + 3)))
+            group = [root]
+            for _ in range(int(rng.integers(0, 5))):
+                bm.fork(root, sid)
+                group.append(sid)
+                sid += 1
+            for s in group:  # samples write their own tokens (copy-on-write of a partial block)
+                bm.append(s, int(rng.integers(0, 2 * B)))
+            order.extend(group)
+        if rng.random() < 0.3:
+            order = list(rng.permutation(order))
+        gs, pl = bm.prefix_groups(order)
+        tables = [list(bm.tables([s])[0][: bm.num_seq_blocks(s)]) for s in order]
+        lens = [bm.length(s) for s in order]
+        want_gs, want_pl = _groups_by_hand(tables, lens, B)
+        assert gs.tolist() == want_gs and pl.tolist() == want_pl
+        # the shared tokens are the same physical blocks in every member
+        for g in range(len(gs) - 1):
+            members = range(gs[g], gs[g + 1])
+            for k in members:
+                assert pl[k] <= lens[k]
+                nb = -(-int(pl[k]) // B)
+                assert tables[k][:nb] == tables[gs[g]][:nb]
+
+
+def test_prefix_groups_rejects_unknown_ids():
+    bm = BlockManager(10, 4)
+    bm.add(0)
+    with pytest.raises(Exception):
+        bm.prefix_groups([0, 7])
+    gs, pl = bm.prefix_groups([])
+    assert gs.tolist() == [0] and pl.tolist() == []

@@ -4,18 +4,19 @@ Input plumbing only: random content, storage formats, block placement and the ho
 manager that decides slots and copy-on-write pairs. No attention arithmetic lives here.
 """
 from .alloc import (BlockAllocator, InOrder, PoolExhausted, Sequence, append_tokens, block_tables_array,
-                    fork, release, wasted_slots)
+                    fork, prefix_groups, release, wasted_slots)
 from .configs import (DecodeStep, KVWrite, PrefillStep, gqa_bf16, gqa_lengths, logical_kv,
                       long_bf16, long_lengths, make_prefill_step, make_step, mha13b_f16,
-                      mha13b_lengths, prefill_gqa, prefill_mha13b, shared_prefix_f16, tiny_f32)
+                      mha13b_lengths, prefill_gqa, prefill_mha13b, prefill_mha13b_f32,
+                      shared_prefix_f16, tiny_f32)
 from .numfmt import (DTYPE_CODE, DTYPES, ELEM_BYTES, STORAGE, bf16_bits_to_f32, f32_to_bf16_bits,
                      full, inf_value, nan_value, to_float64, to_storage)
 
 __all__ = [
     "BlockAllocator", "InOrder", "PoolExhausted", "Sequence", "append_tokens", "block_tables_array", "fork",
-    "release", "wasted_slots", "DecodeStep", "KVWrite", "PrefillStep", "tiny_f32",
+    "prefix_groups", "release", "wasted_slots", "DecodeStep", "KVWrite", "PrefillStep", "tiny_f32",
     "mha13b_f16", "mha13b_lengths", "gqa_bf16", "gqa_lengths", "long_bf16", "long_lengths", "shared_prefix_f16", "logical_kv", "make_prefill_step",
-    "make_step", "prefill_gqa", "prefill_mha13b", "DTYPE_CODE",
+    "make_step", "prefill_gqa", "prefill_mha13b", "prefill_mha13b_f32", "DTYPE_CODE",
     "DTYPES", "ELEM_BYTES", "STORAGE", "bf16_bits_to_f32", "f32_to_bf16_bits", "full",
     "inf_value", "nan_value", "to_float64", "to_storage",
 ]

@@ -132,3 +132,29 @@ def block_tables_array(seqs, pad: int = -1, min_width: int = 1) -> np.ndarray:
 def wasted_slots(seq: Sequence) -> int:
     """Reserved-but-unused token slots of one sequence (internal fragmentation)."""
     return len(seq.table) * seq.block_size - seq.length
+
+
+def prefix_groups(block_tables, context_lens, block_size):
+    """The sharing structure of a batch, read off its block tables: runs of consecutive
+    sequences whose tables start with the same physical block form a group; a group's shared
+    tokens are its members' common leading table entries times the block size, capped by its
+    shortest member (0 for a group of one). Returns (group_start int32 [G + 1], prefix_lens
+    int32 [S]), the description pa_decode_shared_prefix takes."""
+    S = len(context_lens)
+    nblk = [-(-int(t) // block_size) for t in context_lens]
+    starts, pl, i = [], np.zeros(S, np.int32), 0
+    while i < S:
+        j = i + 1
+        while (j < S and nblk[i] > 0 and nblk[j] > 0
+               and block_tables[j, 0] == block_tables[i, 0]):
+            j += 1
+        if j - i > 1:
+            c = 0
+            while all(c < nblk[k] and block_tables[k, c] == block_tables[i, c]
+                      for k in range(i, j)):
+                c += 1
+            pl[i:j] = min(c * block_size, int(min(context_lens[i:j])))
+        starts.append(i)
+        i = j
+    starts.append(S)
+    return np.asarray(starts, np.int32), pl

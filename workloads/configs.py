@@ -328,6 +328,16 @@ def prefill_mha13b(**kw) -> PrefillStep:
     return make_prefill_step("prefill-mha13b-f16", 6, prefix + n, n, 40, 40, 128, 16, "f16", **kw)
 
 
+def prefill_mha13b_f32(**kw) -> PrefillStep:
+    """Chunked prefill in fp32 (the vector-ALU prefill kernel), 13B shape: 16 sequences, 40
+    heads, d=128, B=16; each appends a 64-token chunk to the same lognormal prefixes as the fp16
+    workload."""
+    rng = np.random.default_rng(6)
+    prefix = np.clip(np.rint(rng.lognormal(math.log(512.0), 1.0, size=16)), 0, 1536)
+    n = np.full(16, 64)
+    return make_prefill_step("prefill-mha13b-f32", 6, prefix + n, n, 40, 40, 128, 16, "f32", **kw)
+
+
 def prefill_gqa(**kw) -> PrefillStep:
     """Chunked prefill, GQA bf16: 16 sequences, 64 query heads over 8 KV heads, d=128, B=16;
     each appends a 1024-token chunk to a cached prefix of length uniform in [0, 3072]."""
