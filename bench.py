@@ -39,6 +39,8 @@ WORKLOADS = {
                "lognormal lengths (median 512) clipped to [16,2048]"),
     "gqa": ("gqa_bf16", "GQA bf16 decode: 256 seqs, 64 query / 8 KV heads, d=128, B=16, "
             "lengths uniform in [128,4096]"),
+    "gqa32": ("gqa32_bf16", "wide-group GQA bf16 decode: 128 seqs, 64 query / 2 KV heads (32 per "
+              "KV head), d=128, B=16, lengths uniform in [128,4096]"),
     "long": ("long_bf16", "long-context bf16 split-K decode: 8 seqs, 32 heads, d=128, B=16, "
              "lengths uniform in [32768,131072]"),
     "shared": ("shared_prefix_f16", "shared-prefix fp16 decode: 16 prompts x 4 samples, 32 heads, "

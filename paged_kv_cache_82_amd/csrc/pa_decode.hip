@@ -918,11 +918,37 @@ __device__ __forceinline__ void mfma_decode_run(MfmaSmem<D, NW, NBUF>& sm, const
 template <DT dt, int D, int BS, int NW, int NBUF, int MINB>
 __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const DecodeArgs a) {
   constexpr int NT = NW * 64;
-  const int p = blockIdx.x, unit = blockIdx.y;
-  const int s = blockIdx.z;
+  int p = blockIdx.x, unit = blockIdx.y;
+  int s = blockIdx.z;
   const int Hq = a.num_q_heads;
   const int g = Hq / a.num_kv_heads;
   const int ntile = (g + 15) / 16;
+  if (ntile > 1) {
+    // More than 16 query heads per KV head: the ntile head tiles of one (partition, KV head,
+    // sequence) read the same K/V tiles. The hardware deals workgroups round-robin over the 8
+    // XCDs by linear id, so the tiles take consecutive slots on one XCD: they run side by side
+    // and the second reader finds the lines in that XCD's L2. Ids past the last whole round of
+    // 8 * ntile keep a plain order.
+    const int64_t gx = gridDim.x, units = gridDim.y;
+    const int64_t L = blockIdx.x + gx * (blockIdx.y + units * blockIdx.z);
+    const int64_t span = 8 * (int64_t)ntile;
+    const int64_t full = gx * units * gridDim.z / span * span;
+    int64_t W;  // work index over (partition, KV head, sequence)
+    int ht;
+    if (L < full) {
+      const int64_t slot = L / 8;
+      ht = (int)(slot % ntile);
+      W = (slot / ntile) * 8 + L % 8;
+    } else {
+      ht = (int)((L - full) % ntile);
+      W = full / ntile + (L - full) / ntile;
+    }
+    p = (int)(W % gx);
+    const int64_t rest = W / gx;
+    const int Hkv = a.num_kv_heads;
+    unit = (int)(rest % Hkv) * ntile + ht;
+    s = (int)(rest / Hkv);
+  }
   const int kvh = unit / ntile, ht = unit % ntile;
   const int h0 = kvh * g + ht * 16;
   const int nh = (g - ht * 16 < 16) ? g - ht * 16 : 16;

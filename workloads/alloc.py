@@ -1,6 +1,8 @@
 """Host toy block manager that builds block tables, slot mappings and copy-on-write pairs.
 
-It follows the block manager the pages describe:
+Its semantics are those of the block manager the pages describe (the structure is this
+project's own: batched requests checked against the pool before anything changes, as the
+native manager does):
   - [PA-summary] azimuth.plus, "Efficient Memory Management for Large Language Model Serving
     with PagedAttention", sections "Key idea: virtual memory for the KV cache" (blocks are
     allocated one at a time, on demand, as tokens are generated), "vLLM" (the block manager
@@ -37,41 +39,50 @@ class InOrder:
 
 
 class BlockAllocator:
-    """Free list (LIFO) and reference counts over `num_blocks` physical blocks.
+    """Reference counts and a stack of free block ids over `num_blocks` physical blocks.
 
-    With `rng`, the free list is a seeded permutation of the block ids, so consecutive
-    allocations land at scattered physical positions."""
+    Blocks are handed out from the top of the stack. It starts as the seeded permutation
+    (first element on top), so consecutive requests land at scattered physical positions, and a
+    block whose count falls to zero goes back on top (the last freed is the next handed out)."""
 
     def __init__(self, num_blocks: int, rng: np.random.Generator | None = None):
         if num_blocks < 0:
             raise ValueError("num_blocks must be >= 0")
         self.num_blocks = int(num_blocks)
-        order = np.arange(num_blocks) if rng is None else rng.permutation(num_blocks)
-        # pop() takes from the end: reverse so the first allocation is order[0].
-        self.free = [int(b) for b in order[::-1]]
+        order = np.arange(num_blocks) if rng is None else np.asarray(rng.permutation(num_blocks))
+        self._stack = np.asarray(order[::-1], dtype=np.int64).copy()  # top = last element
+        self._top = self.num_blocks
         self.ref = np.zeros(num_blocks, dtype=np.int64)
-
-    def allocate(self) -> int:
-        if not self.free:
-            raise PoolExhausted("no free physical blocks")
-        b = self.free.pop()
-        assert self.ref[b] == 0
-        self.ref[b] = 1
-        return b
-
-    def incref(self, b: int) -> None:
-        assert self.ref[b] > 0
-        self.ref[b] += 1
-
-    def decref(self, b: int) -> None:
-        assert self.ref[b] > 0
-        self.ref[b] -= 1
-        if self.ref[b] == 0:
-            self.free.append(b)
 
     @property
     def num_free(self) -> int:
-        return len(self.free)
+        return self._top
+
+    def take(self, count: int) -> np.ndarray:
+        """`count` blocks off the top of the stack, in hand-out order, each with count 1."""
+        if count > self._top:
+            raise PoolExhausted("no free physical blocks")
+        got = self._stack[self._top - count: self._top][::-1].copy()
+        self._top -= count
+        assert (self.ref[got] == 0).all()
+        self.ref[got] = 1
+        return got
+
+    def share(self, blocks) -> None:
+        """One more holder for each of `blocks`."""
+        b = np.asarray(blocks, dtype=np.int64)
+        assert (self.ref[b] > 0).all()
+        np.add.at(self.ref, b, 1)
+
+    def drop(self, blocks) -> None:
+        """One holder less for each of `blocks`, in order; blocks left with none go back on the
+        stack in that order."""
+        for b in (int(x) for x in blocks):
+            assert self.ref[b] > 0
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self._stack[self._top] = b
+                self._top += 1
 
 
 @dataclass
@@ -84,38 +95,44 @@ class Sequence:
 
 
 def append_tokens(alloc: BlockAllocator, seq: Sequence, n: int):
-    """Reserve slots for `n` new tokens of `seq`.
+    """Reserve slots for `n` new tokens of `seq` ([PA-summary] "Key idea": a block is taken when
+    a token starts it; "Memory sharing: copy-on-write": a write into a block that other
+    sequences still hold goes to a private copy of that block alone).
 
-    Returns (slots, cow_pairs): slots[i] = phys*B + offset of token seq.length+i; cow_pairs are
-    (src, dst) whole-block copies that must run before the tokens are written."""
+    What the request needs is worked out first: a copy of the partly filled last block when
+    others hold it too, and the blocks that the new length adds. It is taken from the pool in
+    one step (PoolExhausted, with nothing changed, if the pool cannot cover it). Returns (slots,
+    cow_pairs): slots[i] = physical block * B + offset of token seq.length + i; cow_pairs are
+    the (src, dst) whole-block copies that must run before the tokens are written."""
     B = seq.block_size
-    slots, pairs = [], []
-    for _ in range(n):
-        pos = seq.length
-        j, off = divmod(pos, B)
-        if j == len(seq.table):
-            seq.table.append(alloc.allocate())
-        elif alloc.ref[seq.table[j]] > 1:
-            old = seq.table[j]
-            new = alloc.allocate()
-            pairs.append((old, new))
-            alloc.decref(old)
-            seq.table[j] = new
-        slots.append(seq.table[j] * B + off)
-        seq.length += 1
+    if n <= 0:
+        return [], []
+    last = seq.length // B
+    copy_last = seq.length % B != 0 and alloc.ref[seq.table[last]] > 1
+    grow = -(-(seq.length + n) // B) - len(seq.table)
+    got = alloc.take(int(copy_last) + grow)
+    pairs = []
+    if copy_last:  # the writer repoints to its copy; the others keep the original
+        old = seq.table[last]
+        seq.table[last] = int(got[0])
+        alloc.drop([old])
+        pairs.append((old, int(got[0])))
+    seq.table.extend(int(b) for b in got[int(copy_last):])
+    pos = seq.length + np.arange(n)
+    slots = (np.asarray(seq.table, dtype=np.int64)[pos // B] * B + pos % B).tolist()
+    seq.length += n
     return slots, pairs
 
 
 def fork(alloc: BlockAllocator, seq: Sequence) -> Sequence:
-    """A child that shares every block of `seq` (reference counts raised)."""
-    for b in seq.table:
-        alloc.incref(b)
+    """A child that shares every block of `seq` ([PA-tutorial] §5.1: the page table is copied
+    and every page gains a holder)."""
+    alloc.share(seq.table)
     return Sequence(seq.block_size, list(seq.table), seq.length)
 
 
 def release(alloc: BlockAllocator, seq: Sequence) -> None:
-    for b in seq.table:
-        alloc.decref(b)
+    alloc.drop(seq.table)
     seq.table.clear()
     seq.length = 0
 

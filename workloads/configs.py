@@ -376,6 +376,13 @@ def gqa_bf16(**kw) -> DecodeStep:
     return make_step("gqa-bf16", 3, gqa_lengths(), 64, 8, 128, 16, "bf16", **kw)
 
 
+def gqa32_bf16(**kw) -> DecodeStep:
+    """Wide-group GQA bf16 (32 query heads per KV head, two 16-head MFMA tiles): 128 sequences,
+    64 query heads over 2 KV heads, d=128, B=16, lengths uniform in [128, 4096] (a measurement
+    of K/V re-reads across head tiles, not one of the headline workloads)."""
+    return make_step("gqa32-bf16", 8, gqa_lengths(8, 128), 64, 2, 128, 16, "bf16", **kw)
+
+
 def long_lengths(seed: int = 4, S: int = 8) -> np.ndarray:
     return np.random.default_rng(seed).integers(32768, 131072 + 1, size=S)
 
