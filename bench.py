@@ -111,16 +111,17 @@ def source_hash(kind: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kind: str, workload: str):
+def measured_traffic(kind: str, workload: str, sources: str | None = None):
     """HBM bytes (read + written) per launch of the `kind` kernel from the committed rocprofv3
-    counter summary, if it was taken on the current sources of that kernel; else None."""
+    counter summary, if it was taken on the current sources of that kernel (`sources`: the
+    KERNEL_SOURCES entry it is built from, `kind` by default); else None."""
     path = os.path.join(ROOT, "profiles", f"pa_{kind}_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     src = re.search(r"source_sha256_16:\s*(\w+)", text)
     val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not src or not val or src.group(1) != source_hash(kind):
+    if not src or not val or src.group(1) != source_hash(sources or kind):
         return None
     return float(val.group(1))
 
@@ -402,8 +403,9 @@ def run_prefill(args):
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(fl / att_s / 1e12 / peak, 4),
-            "traffic": (None if f32 else
-                        measured_traffic("prefill", args.workload[len("prefill-"):])),
+            # the fp32 kernel is built from the decode sources
+            "traffic": measured_traffic("prefill", args.workload[len("prefill-"):],
+                                        "decode" if f32 else "prefill"),
             "algorithmic_flops_per_launch": fl,
             "algorithmic_bytes_per_launch": prefill_bytes(step),
             "avg_launch_us": round(att_s * 1e6, 3),

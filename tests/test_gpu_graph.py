@@ -82,3 +82,42 @@ def test_prefill_step_graph_replay():
         dev.attend()
 
     _replays_match(run_step, [dev.out, dev.k_cache, dev.v_cache], step.dtype)
+
+
+@pytest.mark.parametrize("P", [0, 64])
+def test_grouped_shared_prefix_decode_graph_replay(P):
+    # pa_decode_shared_prefix (the group kernel; with P = 64 its lists split and the merge kernel
+    # is in the graph too) after the step's copy-on-write and writes
+    from workloads import prefix_groups
+
+    step = shared_prefix_f16(prompts=2, samples=3, prompt_len=100, tail_len=40, heads=4)
+    dev = DevStep(step)
+    gs_np, pl_np = prefix_groups(step.block_tables, step.context_lens, step.block_size)
+    gs = torch.from_numpy(gs_np).cuda()
+    pl = torch.from_numpy(pl_np).cuda()
+    mg, mp = int(np.diff(gs_np).max()), int(pl_np.max())
+    nbytes = pa.pa_decode_shared_prefix_workspace_size(
+        step.num_seqs, len(gs_np) - 1, step.num_q_heads, step.num_kv_heads, step.head_dim,
+        step.block_size, step.max_context_len, mp, mg, P, torch.float16)
+    ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+
+    def run_step():
+        dev.apply_updates()
+        pa.pa_decode_shared_prefix(dev.out, dev.q, dev.k_cache, dev.v_cache, dev.block_tables,
+                                   dev.context_lens, pl, gs, float(step.scale),
+                                   step.max_context_len, mp, mg, ws, P)
+
+    _replays_match(run_step, [dev.out, dev.k_cache, dev.v_cache], step.dtype)
+
+
+def test_noalloc_decode_graph_replay():
+    # the allocation-free decode (split-K partials in the library's static array) in a graph
+    step = make_step("gnoalloc", 520, [300, 17, 1200, 1], 16, 2, 128, 16, "bf16")
+    dev = DevStep(step)
+
+    def run_step():
+        dev.apply_updates()
+        pa.pa_decode_noalloc(dev.out, dev.q, dev.k_cache, dev.v_cache, dev.block_tables,
+                             dev.context_lens, float(step.scale), step.max_context_len, 64)
+
+    _replays_match(run_step, [dev.out, dev.k_cache, dev.v_cache], step.dtype)
