@@ -102,8 +102,8 @@ pa_status pa_write_kv(void *k_cache, void *v_cache, const void *k_new, const voi
  * The workspace holds the per-partition partial results (running max, running sum and partial
  * output, fp32) of every (sequence, query head).
  * partition_tokens: 0 = let the library choose (the same choice pa_decode makes for the same
- * arguments); > 0 must be a multiple of 32 and at most 64*4*block_size tokens (fp32 and
- * single-head groups; 4096 for block_size 64) or 8192 tokens (grouped heads).
+ * arguments); > 0 must be a multiple of 32 and at most 64*4*min(block_size, 16) tokens
+ * (fp32 and single-head groups) or 8192 tokens (grouped heads).
  * Returns 0 when no workspace is needed (every sequence fits one partition) and for invalid
  * sizes.
  */

@@ -46,25 +46,28 @@ bool choose_path(pa_dtype dt, int num_q_heads, int num_kv_heads, int head_dim, i
 // Tokens per partition. A workgroup covers P tokens of one (sequence, head unit); each extra
 // partition costs a partial-state write, a read in the merge kernel and a short-lived
 // workgroup, so sequences are split only when there are too few (sequence, head) units to fill
-// the GPU: with at least kManyUnits units every sequence stays whole; otherwise partitions of
-// 2048 tokens (halved while the grid would be smaller than kManyUnits workgroups, down to
-// 256). Measured on MI355X: unsplit 13B-shape and GQA batches ran 25-35% faster than with
-// 512-token partitions; long contexts peaked at 2048. 0 = automatic.
-constexpr int kManyUnits = 1024;
-
+// the GPU: with at least `many` units every sequence stays whole; otherwise partitions of 2048
+// tokens (halved while the grid would be smaller than `many` workgroups, down to 256). `many` is
+// 1024 for the vector-ALU kernel (several workgroups per CU) and 256 for the MFMA kernel (one
+// per CU, 100-132 KB of LDS). Measured on MI355X: unsplit 13B-shape and GQA batches ran 25-35%
+// faster than with 512-token partitions; long contexts peaked at 2048; a batch of 256
+// (sequence, 32-head) units (128 sequences, 64 query / 2 KV heads, lengths 128..4096) took 59.9
+// us whole against 69.6 / 78.6 / 98.8 us with 2048 / 1024 / 512-token partitions. 0 = automatic.
 int choose_partition(int num_seqs, int units_per_seq, int max_context_len, int cap,
-                     int requested) {
+                     int requested, int many) {
   if (requested > 0) return requested;
   const int64_t units = (int64_t)num_seqs * units_per_seq;
   const int whole = ((max_context_len + 31) / 32) * 32;
   if (whole <= 0) return 32;
-  if (units >= kManyUnits && whole <= cap) return whole;
+  if (units >= many && whole <= cap) return whole;
   int P = 2048 < cap ? 2048 : cap;
   // workgroups if lengths average half the maximum
   auto est = [&](int p) { return units * ((max_context_len / 2 + p - 1) / p); };
-  while (P > 256 && est(P) < kManyUnits) P /= 2;
+  while (P > 256 && est(P) < many) P /= 2;
   return P < whole ? P : whole;
 }
+
+int many_units(pa::DecodePath path) { return path == pa::DecodePath::Mfma ? 256 : 1024; }
 
 int parts_for(int max_context_len, int P) {
   const int n = (max_context_len + P - 1) / P;
@@ -134,7 +137,7 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
 
   const int P = choose_partition(num_seqs,
                                  pa::decode_units_per_seq(path, num_q_heads, num_kv_heads),
-                                 max_context_len, cap, partition_tokens);
+                                 max_context_len, cap, partition_tokens, many_units(path));
   const int max_parts = parts_for(max_context_len, P);
   const pa::WorkspaceLayout L =
       pa::workspace_layout(num_seqs, num_q_heads, head_dim, max_parts);
@@ -211,7 +214,7 @@ bool shared_plan(int num_groups, int num_q_heads, int num_kv_heads, int max_cont
   const int64_t parts = bound > 0 ? (bound + P.steps - 1) / P.steps : 1;
   if (parts > (1 << 20)) return false;
   P.parts = (int)parts;
-  P.wgs = units * P.parts;
+  P.wgs = units * (P.parts > 1 ? (P.parts | 1) : 1);  // the grid pads partitions to an odd count
   *out = P;
   return true;
 }
@@ -265,7 +268,7 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
   if (partition_tokens > cap) return 0;
   const int P = choose_partition(num_seqs,
                                  pa::decode_units_per_seq(path, num_q_heads, num_kv_heads),
-                                 max_context_len, cap, partition_tokens);
+                                 max_context_len, cap, partition_tokens, many_units(path));
   return pa::workspace_layout(num_seqs, num_q_heads, head_dim, parts_for(max_context_len, P))
       .total;
 }

@@ -152,11 +152,14 @@ __global__ __launch_bounds__(D) void merge_partitions_kernel(const DecodeArgs a)
 
 // ---- VALU kernel ------------------------------------------------------------------------
 
-// Tokens a wave of the VALU kernels takes at once (a "unit"): the whole block up to 32 tokens;
-// 16 tokens of a larger block, so that a unit's registers stay those of a 16-token block.
+// Tokens a wave of the VALU kernels takes at once (a "unit"): the whole block up to 16 tokens;
+// 16 tokens of a larger block, so that a unit's registers stay those of a 16-token block (two
+// waves per SIMD for 16-bit data). Measured on MI355X with 32-token blocks, against whole-block
+// units (one wave per SIMD): 13B-shape batch 154.4 against 160.6 us, unshared 64 x 1297-token
+// batch 206.8 against 219.8 us.
 template <int BS>
 constexpr int valu_unit_tokens() {
-  return BS > 32 ? 16 : BS;
+  return BS > 16 ? 16 : BS;
 }
 
 template <DT dt, int D, int SB, int NW>
@@ -555,21 +558,26 @@ __device__ __forceinline__ void lds_read_k(u32x4 (&t)[2][2], const uint32_t (&ka
       : "v"(ka[0]), "v"(ka[1]), "i"(OFF), "i"(OFF + UOFF));
 }
 
-// One workgroup of the MFMA decode: up to 16 query columns (lane hh's column reads its query
-// row at qrow, null for an empty column) against the tokens of one table row `bt`, KV head
-// kvh, in 32-token steps st0, st0 + 1, ... The block ids of at most max_steps steps are loaded
-// first, with the queries; end_fn() then returns the token at which the workgroup's range ends
-// (a range ending at or before token 32 * st0 means no work: the workgroup returns). The
-// workgroup's waves take the steps in turn, merge their (max, sum, output) states in LDS and
-// hand the merged state of each column to store(fm, fl, fo) (fo: [16][D]).
+// One workgroup of the MFMA decode: NC tiles of 16 query columns (column 16c + hh, lane hh of
+// tile c, reads its query row at qrow[c], null for an empty column) against the tokens of one
+// table row `bt`, KV head kvh, in 32-token steps st0, st0 + 1, ... The block ids of at most
+// max_steps steps are loaded first, with the queries; end_fn() then returns the token at which
+// the workgroup's range ends (a range ending at or before token 32 * st0 means no work: the
+// workgroup returns). The workgroup's waves take the steps in turn, merge their (max, sum,
+// output) states in LDS and hand the merged state of each column to store(fm, fl, fo) (fo:
+// [16 NC][D]). Each K/V step is read once for all NC tiles.
 // The LDS of one MFMA decode workgroup, declared once per kernel (a kernel may run the core
-// from more than one place).
-template <int D, int NW, int NBUF>
+// from more than one place). A wave's output state for the merge, [16][D] floats, takes the
+// place of its own K ring once its steps are done (no other wave touches that ring).
+template <int D, int NW, int NBUF, int NC = 1>
 struct MfmaSmem {
   __attribute__((aligned(1024))) char k[NW][NBUF][32 * D * 2];  // K ring, one per wave
-  float o[NW][16][D];
-  float m[NW][16], l[NW][16];
-  float fm[16], fl[16];
+  float m[NW][16 * NC], l[NW][16 * NC];
+  float fm[16 * NC], fl[16 * NC];
+  static_assert(16 * NC * D * sizeof(float) <= NBUF * 32 * D * 2, "an output state fits a ring");
+  __device__ __forceinline__ float (*o(int w))[D] {
+    return reinterpret_cast<float (*)[D]>(&k[w][0][0]);
+  }
 };
 
 // One 32-token step of an MFMA decode workgroup, as its step source describes it: `index`
@@ -643,11 +651,13 @@ struct ListSteps {
   }
 };
 
-template <DT dt, int D, int BS, int NW, int NBUF, class Steps, class StoreFn>
-__device__ __forceinline__ void mfma_decode_run(MfmaSmem<D, NW, NBUF>& sm, const DecodeArgs& a,
-                                                int kvh, const char* qrow, Steps& steps,
+template <DT dt, int D, int BS, int NW, int NBUF, int NC, class Steps, class StoreFn>
+__device__ __forceinline__ void mfma_decode_run(MfmaSmem<D, NW, NBUF, NC>& sm,
+                                                const DecodeArgs& a, int kvh,
+                                                const char* const (&qrow)[NC], Steps& steps,
                                                 StoreFn store) {
   static_assert(dt != DT::F32, "MFMA path takes 16-bit inputs");
+  static_assert(NC == 1 || Steps::kAllColumns, "per-step column ranges take one tile");
   static_assert(32 % BS == 0 || BS % 32 == 0, "a 32-token step spans whole blocks or part of one");
   using M = MfmaT<dt>;
   using vec8 = typename M::vec8;
@@ -659,7 +669,6 @@ __device__ __forceinline__ void mfma_decode_run(MfmaSmem<D, NW, NBUF>& sm, const
   constexpr int SPB = BS > 32 ? BS / 32 : 1;    // steps per block
   constexpr int NT = NW * 64;
   auto& lds_k = sm.k;
-  auto& lds_o = sm.o;
   auto& lds_m = sm.m;
   auto& lds_l = sm.l;
   auto& lds_fm = sm.fm;
@@ -671,20 +680,27 @@ __device__ __forceinline__ void mfma_decode_run(MfmaSmem<D, NW, NBUF>& sm, const
 
   int my_id[NBS];
   steps.load_ids(my_id, lane);
-  // Q^T operand: column hh, k = head dims 32*kk + 8*gq + e.
-  vec8 qop[KC];
+  // Q^T operand of tile c: column 16c + hh, k = head dims 32*kk + 8*gq + e.
+  vec8 qop[NC][KC];
 #pragma unroll
-  for (int kk = 0; kk < KC; ++kk) {
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (qrow) raw = load16(qrow + (32 * kk + 8 * gq) * E);
-    qop[kk] = __builtin_bit_cast(vec8, raw);
-  }
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (qrow[c]) raw = load16(qrow[c] + (32 * kk + 8 * gq) * E);
+      qop[c][kk] = __builtin_bit_cast(vec8, raw);
+    }
   if (!steps.finalize()) return;  // a step source returns false for the whole workgroup only
 
-  f32x4 oacc[MT];
+  f32x4 oacc[NC][MT];
+  float m[NC], lsum[NC];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = kNegInf, lsum = 0.0f;
+  for (int c = 0; c < NC; ++c) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) oacc[c][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[c] = kNegInf;
+    lsum[c] = 0.0f;
+  }
 
   // This wave's steps k < ns; lane k holds the NBS physical ids of step k.
   const int ns = steps.ns;
@@ -797,47 +813,58 @@ __device__ __forceinline__ void mfma_decode_run(MfmaSmem<D, NW, NBUF>& sm, const
     wait_vmcnt<(NBUF - 1) * (8 + KD) + 8>();
     u32x4 kf[2][KC];
     lds_read_k<slot * KSTEP, 16 * RB>(kf, ka);
-    // S^T = K Q^T: sacc[u][i] = score of token tau0 + 16u + 4*gq + i for head hh.
-    f32x4 sacc[2];
+    // S^T = K Q^T: sacc[c][u][i] = score of token tau0 + 16u + 4*gq + i for column 16c + hh;
+    // 2 NC independent accumulation chains.
+    f32x4 sacc[NC][2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      sacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int kk = 0; kk < KC; ++kk)
-        sacc[u] = M::mma(__builtin_bit_cast(vec8, kf[u][kk]), qop[kk], sacc[u]);
-    }
+      for (int u = 0; u < 2; ++u) sacc[c][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          sacc[c][u] = M::mma(__builtin_bit_cast(vec8, kf[u][kk]), qop[c][kk], sacc[c][u]);
     const bool tail = sd.valid < 32 || (!Steps::kAllColumns && (sd.clo > 0 || sd.chi < 16));
-    float sc[8];
+    vec8 pop[NC];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int c = 0; c < NC; ++c) {
+      float sc[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = sacc[u][i] * a.scale_log2;
-        if (tail && (16 * u + 4 * gq + i >= sd.valid || !col_ok)) x = kNegInf;
-        sc[4 * u + i] = x;
-      }
-    float bm = sc[0];
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sc[e]);
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float mn = fmaxf(m, bm);
-    const bool empty = (mn == kNegInf);
-    const float corr = empty ? 1.0f : fast_exp2(m - mn);
-    // The weights are rounded to 16 bits for the p.V MFMA; the row sum adds those same rounded
-    // weights (dot2 of each packed pair with (1, 1)), so numerator and denominator agree.
-    float pe[8];
+        for (int i = 0; i < 4; ++i) {
+          float x = sacc[c][u][i] * a.scale_log2;
+          if (tail && (16 * u + 4 * gq + i >= sd.valid || !col_ok)) x = kNegInf;
+          sc[4 * u + i] = x;
+        }
+      float bm = sc[0];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pe[e] = empty ? 0.0f : fast_exp2(sc[e] - mn);
-    const u32x4 pw = {pack2<dt>(pe[0], pe[1]), pack2<dt>(pe[2], pe[3]),
-                      pack2<dt>(pe[4], pe[5]), pack2<dt>(pe[6], pe[7])};
-    float ps = 0.0f;
+      for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sc[e]);
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float mn = fmaxf(m[c], bm);
+      const bool empty = (mn == kNegInf);
+      const float corr = empty ? 1.0f : fast_exp2(m[c] - mn);
+      // The weights are rounded to 16 bits for the p.V MFMA; the row sum adds those same
+      // rounded weights (dot2 of each packed pair with (1, 1)), so numerator and denominator
+      // agree.
+      float pe[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ps = sum2<dt>(pw[j], ps);
-    const vec8 pop = __builtin_bit_cast(vec8, pw);
-    lsum = fmaf(lsum, corr, ps);
+      for (int e = 0; e < 8; ++e) pe[e] = empty ? 0.0f : fast_exp2(sc[e] - mn);
+      const u32x4 pw = {pack2<dt>(pe[0], pe[1]), pack2<dt>(pe[2], pe[3]),
+                        pack2<dt>(pe[4], pe[5]), pack2<dt>(pe[6], pe[7])};
+      float ps = 0.0f;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) oacc[mt] *= corr;
+      for (int j = 0; j < 4; ++j) ps = sum2<dt>(pw[j], ps);
+      pop[c] = __builtin_bit_cast(vec8, pw);
+      lsum[c] = fmaf(lsum[c], corr, ps);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) oacc[c][mt] *= corr;
+      m[c] = mn;
+    }
     if (tail) {  // V rows past the step's valid tokens may hold anything, NaN included
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -856,9 +883,10 @@ __device__ __forceinline__ void mfma_decode_run(MfmaSmem<D, NW, NBUF>& sm, const
         const uint32_t hi = vfrag_elem<D>(R.v[e1 / 4][e1 % 4], mt);
         vw[q2] = lo | (hi << 16);
       }
-      oacc[mt] = M::mma(__builtin_bit_cast(vec8, vw), pop, oacc[mt]);
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        oacc[c][mt] = M::mma(__builtin_bit_cast(vec8, vw), pop[c], oacc[c][mt]);
     }
-    m = mn;
   };
 
   if (ns > 0) {  // rings of NBUF slots, unconditional prefetch (see the VALU kernel)
@@ -877,19 +905,31 @@ __device__ __forceinline__ void mfma_decode_run(MfmaSmem<D, NW, NBUF>& sm, const
   }
 
   // Sum the per-lane partial sums over the four lane groups of each head.
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-  // oacc[mt][i] is O[head hh][dim MT*(4*gq + i) + mt].
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int c = 0; c < NC; ++c) {
+    lsum[c] += __shfl_xor(lsum[c], 16);
+    lsum[c] += __shfl_xor(lsum[c], 32);
+  }
+  // oacc[c][mt][i] is O[column 16c + hh][dim MT*(4*gq + i) + mt]. It goes where this wave's K
+  // ring was: first every load the wave issued must have landed (prefetches past its last step
+  // included, whose LDS loads write zeros).
+  wait_vmcnt<0>();
+  float (*const my_o)[D] = sm.o(w);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_o[w][hh][MT * (4 * gq + i) + mt] = oacc[mt][i];
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) my_o[16 * c + hh][MT * (4 * gq + i) + mt] = oacc[c][mt][i];
   if (gq == 0) {
-    lds_m[w][hh] = m;
-    lds_l[w][hh] = lsum;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      lds_m[w][16 * c + hh] = m[c];
+      lds_l[w][16 * c + hh] = lsum[c];
+    }
   }
   __syncthreads();
-  if (threadIdx.x < 16) {
+  if (threadIdx.x < 16 * NC) {
     const int k = threadIdx.x;
     float Mx = kNegInf;
 #pragma unroll
@@ -900,35 +940,38 @@ __device__ __forceinline__ void mfma_decode_run(MfmaSmem<D, NW, NBUF>& sm, const
     lds_fm[k] = Mx;
     lds_fl[k] = L;
   }
-  float* fo = &lds_o[0][0][0];  // merged output reuses wave 0's slab (read-before-write)
-  for (int idx = threadIdx.x; idx < 16 * D; idx += NT) {
+  float* fo = &sm.o(0)[0][0];  // merged output reuses wave 0's slab (read-before-write)
+  for (int idx = threadIdx.x; idx < 16 * NC * D; idx += NT) {
     const int k = idx / D, dim = idx % D;
     float Mx = kNegInf;
 #pragma unroll
     for (int x = 0; x < NW; ++x) Mx = fmaxf(Mx, lds_m[x][k]);
     float acc = 0.0f;
 #pragma unroll
-    for (int x = 0; x < NW; ++x) acc = fmaf(rescale(lds_m[x][k], Mx), lds_o[x][k][dim], acc);
+    for (int x = 0; x < NW; ++x) acc = fmaf(rescale(lds_m[x][k], Mx), sm.o(x)[k][dim], acc);
     fo[idx] = acc;
   }
   __syncthreads();
   store(lds_fm, lds_fl, fo);
 }
 
-template <DT dt, int D, int BS, int NW, int NBUF, int MINB>
+// NC = 2 (groups of more than 16 query heads): a workgroup takes 32 heads of one KV head, two
+// column tiles fed by each K/V step.
+template <DT dt, int D, int BS, int NW, int NBUF, int MINB, int NC>
 __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const DecodeArgs a) {
   constexpr int NT = NW * 64;
+  constexpr int CW = 16 * NC;  // query heads per workgroup
   int p = blockIdx.x, unit = blockIdx.y;
   int s = blockIdx.z;
   const int Hq = a.num_q_heads;
   const int g = Hq / a.num_kv_heads;
-  const int ntile = (g + 15) / 16;
+  const int ntile = (g + CW - 1) / CW;
   if (ntile > 1) {
-    // More than 16 query heads per KV head: the ntile head tiles of one (partition, KV head,
-    // sequence) read the same K/V tiles. The hardware deals workgroups round-robin over the 8
-    // XCDs by linear id, so the tiles take consecutive slots on one XCD: they run side by side
-    // and the second reader finds the lines in that XCD's L2. Ids past the last whole round of
-    // 8 * ntile keep a plain order.
+    // More query heads per KV head than one workgroup takes: the ntile head tiles of one
+    // (partition, KV head, sequence) read the same K/V tiles. The hardware deals workgroups
+    // round-robin over the 8 XCDs by linear id, so the tiles take consecutive slots on one XCD:
+    // they run side by side and the second reader finds the lines in that XCD's L2. Ids past
+    // the last whole round of 8 * ntile keep a plain order.
     const int64_t gx = gridDim.x, units = gridDim.y;
     const int64_t L = blockIdx.x + gx * (blockIdx.y + units * blockIdx.z);
     const int64_t span = 8 * (int64_t)ntile;
@@ -950,15 +993,19 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
     s = (int)(rest / Hkv);
   }
   const int kvh = unit / ntile, ht = unit % ntile;
-  const int h0 = kvh * g + ht * 16;
-  const int nh = (g - ht * 16 < 16) ? g - ht * 16 : 16;
+  const int h0 = kvh * g + ht * CW;
+  const int nh = (g - ht * CW < CW) ? g - ht * CW : CW;
   const int P = a.partition_tokens;
   const int hh = threadIdx.x & 15;
-  // column hh = query head h0 + hh of sequence s
-  const char* qrow =
-      hh < nh ? (const char*)a.q + ((int64_t)s * Hq + h0 + hh) * D * 2 : nullptr;
+  // column 16c + hh = query head h0 + 16c + hh of sequence s
+  const char* qrow[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    qrow[c] = 16 * c + hh < nh
+                  ? (const char*)a.q + ((int64_t)s * Hq + h0 + 16 * c + hh) * D * 2
+                  : nullptr;
   int nparts = 0;
-  __shared__ MfmaSmem<D, NW, NBUF> sm;
+  __shared__ MfmaSmem<D, NW, NBUF, NC> sm;
   auto end_fn = [&]() -> int {
     const int T = seq_len(a, s, BS);
     nparts = (T + P - 1) / P;
@@ -972,7 +1019,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
   RangeSteps<BS, NW, decltype(end_fn)> steps{a.block_tables + (int64_t)s * a.max_blocks_per_seq,
                                              p * (P / 32), P / 32, a.max_blocks_per_seq,
                                              wave_id(), end_fn};
-  mfma_decode_run<dt, D, BS, NW, NBUF>(
+  mfma_decode_run<dt, D, BS, NW, NBUF, NC>(
       sm, a, kvh, qrow, steps, [&](const float* fm, const float* fl, const float* fo) {
         finish_partition<dt, D, NT>(a, s, h0, nh, p, nparts, fm, fl, fo);
       });
@@ -1024,11 +1071,14 @@ template <DT dt, int D, int BS, int NW, int NBUF, int MINB>
 __global__ __launch_bounds__(NW * 64, MINB) void decode_group_kernel(const DecodeArgs a) {
   constexpr int NT = NW * 64;
   __shared__ MfmaSmem<D, NW, NBUF> sm;
-  // grid: (partition, KV head x column tile, group), partition fastest
+  // grid: (partition, KV head x column tile, group), partition fastest, with an odd partition
+  // count in the grid (the launcher's npg; see launch_t): slot p == np finds no work
   const int64_t L = blockIdx.x;
   const int np = a.group_parts;
-  const int p = (int)(L % np);
-  const int64_t rest = L / np;
+  const int npg = np > 1 ? (np | 1) : 1;
+  const int p = (int)(L % npg);
+  if (p >= np) return;  // uniform
+  const int64_t rest = L / npg;
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
   const int g = Hq / Hkv;
   const int units = Hkv * a.shared_ctiles;
@@ -1118,10 +1168,10 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_group_kernel(const Decod
   }
   ListSteps<BS> steps{row, index, meta, (pend - pbeg - w + NW - 1) / NW, M};
   if (steps.ns < 0) steps.ns = 0;
-  const char* qrow = c < ncols ? (const char*)a.q +
-                                     ((int64_t)(s0 + c / g) * Hq + kvh * g + c % g) * D * 2
-                               : nullptr;
-  mfma_decode_run<dt, D, BS, NW, NBUF>(
+  const char* const qrow[1] = {
+      c < ncols ? (const char*)a.q + ((int64_t)(s0 + c / g) * Hq + kvh * g + c % g) * D * 2
+                : nullptr};
+  mfma_decode_run<dt, D, BS, NW, NBUF, 1>(
       sm, a, kvh, qrow, steps, [&](const float* fm, const float* fl, const float* fo) {
         finish_group<dt, D, NT>(a, s0, ncols, ct, kvh, p, nparts, fm, fl, fo);
       });
@@ -1133,10 +1183,8 @@ constexpr int kWaves = 4;          // waves per workgroup
 // Prefetch depth and occupancy, measured on MI355X (13B-shape fp16 MHA and GQA bf16 batches):
 // more blocks in flight per wave beat more waves per SIMD up to these depths.
 constexpr int kValuBuffers = 4;    // VALU kernel: blocks in registers (NBUF-1 in flight)
-// fp32 blocks of 8 or more loads per tensor (d = 64 with B = 32, d = 128 with B >= 16) take 3:
-// four of them need more registers than a wave has and spill. The 16-bit B = 32 kernel keeps 4
-// although it then runs one wave per SIMD: with 3 (two waves per SIMD) the shared-prefix step's
-// decode took 174.9 against 169.9 us (measured on MI355X).
+// fp32 units of 8 or more loads per tensor (d = 128) take 3: four of them need more registers
+// than a wave has and spill.
 template <DT dt, int D, int BS>
 constexpr int valu_buffers() {
   return (dt == DT::F32 && ValuCfg<dt, D, valu_unit_tokens<BS>(), kWaves>::NL >= 8)
@@ -1145,6 +1193,13 @@ constexpr int valu_buffers() {
 }
 constexpr int kMfmaBuffers = 3;    // MFMA kernel: 32-token steps in registers
 constexpr int kMfmaMinBlocks = 1;  // MFMA kernel: workgroups per CU the registers must allow
+// The shared-prefix (group) kernel runs two workgroups per CU with two steps per wave in its
+// rings (66 KB of LDS, 188 VGPRs): its workgroups are fewer and shorter, and a second one on the
+// CU covers a first one's start and merge. Measured on MI355X, shared-prefix step (16 prompts x
+// 4 samples): 89.9 against 95.2 us with the MFMA kernel's three steps and one workgroup per CU.
+// The same change made the GQA batch's MFMA kernel slower (364.6 against 352.2 us).
+constexpr int kGroupBuffers = 2;
+constexpr int kGroupMinBlocks = 2;
 
 WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_parts,
                                  bool with_counts) {
@@ -1160,10 +1215,15 @@ WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int head_dim, in
   return L;
 }
 
+// Query heads one MFMA workgroup takes: 16 (one column tile), or 32 (two tiles fed by each K/V
+// step) when a KV head has more than 16.
+static int mfma_heads_per_workgroup(int g) { return g > 16 ? 32 : 16; }
+
 int decode_units_per_seq(DecodePath path, int num_q_heads, int num_kv_heads) {
   if (path == DecodePath::Valu) return num_q_heads;
   const int g = num_q_heads / num_kv_heads;
-  return num_kv_heads * ((g + 15) / 16);
+  const int cw = mfma_heads_per_workgroup(g);
+  return num_kv_heads * ((g + cw - 1) / cw);
 }
 
 template <int D, int BS>
@@ -1194,7 +1254,7 @@ hipError_t launch_prefill_valu(int head_dim, int block_size, const PrefillArgs& 
 
 int max_partition_tokens(DecodePath path, int block_size) {
   // every wave's unit (or step) ids must fit one register: kMaxPerWave per wave
-  const int unit = block_size > 32 ? 16 : block_size;  // valu_unit_tokens
+  const int unit = block_size > 16 ? 16 : block_size;  // valu_unit_tokens
   return path == DecodePath::Valu ? kMaxPerWave * kWaves * unit : kMaxPerWave * kWaves * 32;
 }
 
@@ -1217,7 +1277,9 @@ static hipError_t launch_t(DecodePath path, const DecodeArgs& a, hipStream_t str
   const void* fn = nullptr;
   if (path == DecodePath::Mfma) {
     if constexpr (dt != DT::F32) {
-      fn = (const void*)decode_mfma_kernel<dt, D, BS, kWaves, kMfmaBuffers, kMfmaMinBlocks>;
+      fn = mfma_heads_per_workgroup(a.num_q_heads / a.num_kv_heads) == 32
+               ? (const void*)decode_mfma_kernel<dt, D, BS, kWaves, kMfmaBuffers, kMfmaMinBlocks, 2>
+               : (const void*)decode_mfma_kernel<dt, D, BS, kWaves, kMfmaBuffers, kMfmaMinBlocks, 1>;
     } else {
       return hipErrorInvalidValue;
     }
@@ -1253,13 +1315,17 @@ static hipError_t launch_d(DecodePath path, int d, int bs, const DecodeArgs& a, 
 
 template <DT dt, int D, int BS>
 static hipError_t launch_shared_t(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t total = (int64_t)a.num_groups * a.num_kv_heads * a.shared_ctiles * a.group_parts;
+  // An odd partition count per (group, KV head, column tile) in the grid, as launch_t pads
+  // it, so that one partition index does not land on a fixed subset of the XCDs (measured on
+  // MI355X, shared-prefix step forced to 2048-token partitions: 210.8 us with two).
+  const int64_t npg = a.group_parts > 1 ? (a.group_parts | 1) : 1;
+  const int64_t total = (int64_t)a.num_groups * a.num_kv_heads * a.shared_ctiles * npg;
   if (total == 0) return hipSuccess;
   if (total > 0xffffffffLL) return hipErrorInvalidValue;  // the API checks this first
   DecodeArgs args_copy = a;
   void* args[] = {&args_copy};
   hipError_t e = hipLaunchKernel(
-      (const void*)decode_group_kernel<dt, D, BS, kWaves, kMfmaBuffers, kMfmaMinBlocks>,
+      (const void*)decode_group_kernel<dt, D, BS, kWaves, kGroupBuffers, kGroupMinBlocks>,
       dim3((unsigned)total), dim3(kWaves * 64), args, 0, stream);
   if (e != hipSuccess || a.max_parts <= 1) return e;
   return hipLaunchKernel((const void*)merge_partitions_kernel<dt, D, BS, true>,

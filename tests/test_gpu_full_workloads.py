@@ -3,6 +3,7 @@ benchmark times (automatic partition size), every output against the oracle:
 
   13B-shape fp16 MHA    (64 seqs, 40 heads, d=128, B=16, lognormal lengths)   and its fp32 twin
   GQA bf16              (256 seqs, 64/8 heads, uniform 128..4096)
+  wide-group GQA bf16   (128 seqs, 64/2 heads: 32 per KV head, two column tiles per workgroup)
   long-context bf16     (8 seqs, 32 heads, uniform 32k..128k, split-K)       and its fp32 twin
   shared-prefix fp16    (16 prompts x 4 samples, B=32)                        in test_gpu_parity
 
@@ -22,7 +23,8 @@ import oracle
 import paged_kv_cache_82_amd as pa
 from gpu_harness import (PARITY_LOG, DevStep, check_full_size, pools_equal, tight_failures,
                          to_host, uses_mfma_decode)
-from workloads import gqa_bf16, long_bf16, long_lengths, make_step, mha13b_f16, mha13b_lengths
+from workloads import (gqa32_bf16, gqa_bf16, long_bf16, long_lengths, make_step, mha13b_f16,
+                       mha13b_lengths)
 
 pytestmark = pytest.mark.gpu
 
@@ -79,6 +81,11 @@ def test_mha13b_f16_full():
 
 def test_gqa_bf16_full():
     _full(gqa_bf16(), negative_control=True)
+
+
+def test_gqa32_bf16_full():
+    # 32 query heads per KV head: one workgroup takes all 32 (two MFMA column tiles)
+    _full(gqa32_bf16(), negative_control=True)
 
 
 def test_long_bf16_full():

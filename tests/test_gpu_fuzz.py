@@ -33,7 +33,7 @@ def _decode_case(i):
     S = int(rng.integers(1, 13))
     lens = [int(x) for x in rng.choice([0, 1, 2, 15, 16, 17, 100, 333, 1024, 2500], size=S)]
     lens[0] = max(lens[0], 1)
-    cap = 64 * 4 * (B if B <= 32 else 16) if (dt == "f32" or g == 1) else 8192
+    cap = 64 * 4 * min(B, 16) if (dt == "f32" or g == 1) else 8192
     P = int(rng.choice([0, 0, 32, 64, 96, 512]))
     P = P if P <= cap else 0
     scale = float(rng.choice([1 / np.sqrt(d), 1 / np.sqrt(d), 0.5, -0.07]))

@@ -58,6 +58,18 @@ def test_shapes_gqa(dt, g, d, B):
     _run_and_check(step, what=f"gqa {dt} g{g} d{d} B{B}")
 
 
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("Hq,Hkv,d", [(24, 1, 128), (48, 1, 128), (64, 1, 128), (96, 2, 64),
+                                      (34, 2, 128)])
+@pytest.mark.parametrize("P", [0, 64])
+def test_wide_groups(dt, Hq, Hkv, d, P):
+    # more than 16 query heads per KV head: workgroups of 32 heads (two MFMA column tiles), the
+    # last one part-empty for g = 24, 48, 17; single-KV-head (multi-query) batches; whole and
+    # split sequences, empty and one-token sequences among them
+    step = make_step("wide", 90 + Hq + d, [0, 1, 31, 33, 200, 700], Hq, Hkv, d, 16, dt)
+    _run_and_check(step, partition_tokens=P, what=f"wide {dt} {Hq}/{Hkv} d{d} P{P}")
+
+
 @pytest.mark.parametrize("path", ["valu", "mfma"])
 def test_both_decode_paths_on_gqa(path, decode_kernel):
     decode_kernel(path)
