@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, vendor figure
 PEAK_MFMA_TFLOPS_16 = 2500.0  # MI355X dense fp16/bf16 matrix peak, vendor figure
-PEAK_VALU_TFLOPS_32 = 157.3  # MI355X fp32 vector peak, vendor figure (256 CUs at 2.4 GHz)
+PEAK_MFMA_TFLOPS_32 = 157.3  # MI355X dense fp32 matrix peak, vendor figure
 
 WORKLOADS = {
     "mha13b": ("mha13b_f16", "13B-shape fp16 MHA decode: 64 seqs, 40 heads, d=128, B=16, "
@@ -111,17 +111,16 @@ def source_hash(kind: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kind: str, workload: str, sources: str | None = None):
+def measured_traffic(kind: str, workload: str):
     """HBM bytes (read + written) per launch of the `kind` kernel from the committed rocprofv3
-    counter summary, if it was taken on the current sources of that kernel (`sources`: the
-    KERNEL_SOURCES entry it is built from, `kind` by default); else None."""
+    counter summary, if it was taken on the current sources of that kernel family; else None."""
     path = os.path.join(ROOT, "profiles", f"pa_{kind}_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     src = re.search(r"source_sha256_16:\s*(\w+)", text)
     val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not src or not val or src.group(1) != source_hash(sources or kind):
+    if not src or not val or src.group(1) != source_hash(kind):
         return None
     return float(val.group(1))
 
@@ -374,7 +373,7 @@ def run_prefill(args):
     fl = prefill_flops(step)
     n_new = step.num_q_tokens
     f32 = step.dtype == "f32"
-    peak = PEAK_VALU_TFLOPS_32 if f32 else PEAK_MFMA_TFLOPS_16
+    peak = PEAK_MFMA_TFLOPS_32 if f32 else PEAK_MFMA_TFLOPS_16
     res = {
         "metric": "paged prefill attention: achieved TFLOP/s (% of MFMA peak) + query tokens/s",
         "value": round(fl / (wall / args.steps) / 1e12, 3),
@@ -396,16 +395,14 @@ def run_prefill(args):
         "execution": "eager" if args.no_graph else f"HIP graph of {ncopy} steps, replayed",
         "eager_ms_per_step": round(eager_wall / args.steps * 1e3, 5),
         "roofline": {
-            "kernel": ("pa_prefill: prefill_valu_kernel" if f32 else
+            "kernel": ("pa_prefill: prefill_f32_kernel" if f32 else
                        "pa_prefill: prefill_mfma_kernel"),
-            "bound": "alu" if f32 else "mfma",
+            "bound": "mfma",
             "achieved": round(fl / att_s / 1e12, 3),
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(fl / att_s / 1e12 / peak, 4),
-            # the fp32 kernel is built from the decode sources
-            "traffic": measured_traffic("prefill", args.workload[len("prefill-"):],
-                                        "decode" if f32 else "prefill"),
+            "traffic": measured_traffic("prefill", args.workload[len("prefill-"):]),
             "algorithmic_flops_per_launch": fl,
             "algorithmic_bytes_per_launch": prefill_bytes(step),
             "avg_launch_us": round(att_s * 1e6, 3),

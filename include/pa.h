@@ -234,17 +234,16 @@ size_t pa_decode_shared_prefix_workspace_size(int num_seqs, int num_groups, int 
  * 0 .. T_s - n_s + i (the causal rule; a decode step is the case n_s = 1):
  *   out[r][h] = sum_{t <= p} exp(s_t - M) V_t / sum_{t <= p} exp(s_t - M),
  *   s_t = scale * q[r][h] . K_t,  K_t = k_cache[block_tables[s][t/B]][h/g][t%B],  p = T_s-n_s+i
- * computed in fp32 (on MFMA for f16/bf16, on the vector ALU for f32) and rounded to
- * nearest-even in `dt`.
+ * computed in fp32 (on MFMA: 16-bit operands for f16/bf16, fp32 operands for f32) and
+ * rounded to nearest-even in `dt`.
  * q, out: [num_q_tokens][num_q_heads][head_dim], 16-byte aligned; rows that belong to no
  * sequence are left untouched.
  * query_start: int32 [num_seqs + 1], device, non-decreasing, within [0, num_q_tokens].
  * max_query_len: host-known bound on every n_s; max_context_len: on every T_s (they size the
  * grid; no device read on the host). n_s > T_s or n_s > max_query_len is a caller error: only
  * min(n_s, T_s, max_query_len) rows are computed.
- * Supported: dt f32, f16 or bf16, head_dim 64 or 128, block_size 8, 16, 32 or 64; for f32,
- * num_q_tokens * num_q_heads <= 2^31 - 1 (PA_ERR_INVALID_ARG otherwise). No workspace. Device
- * indices are clamped as for pa_decode.
+ * Supported: dt f32, f16 or bf16, head_dim 64 or 128, block_size 8, 16, 32 or 64. No
+ * workspace. Device indices are clamped as for pa_decode.
  */
 pa_status pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
                      const int32_t *block_tables, const int32_t *context_lens,

@@ -426,12 +426,10 @@ pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* 
     return PA_ERR_INVALID_ARG;
   const int g = num_q_heads / num_kv_heads;
   const int64_t rows = (int64_t)max_query_len * g;
-  const int per_wg = pa::prefill_rows_per_workgroup();
+  const int per_wg = pa::prefill_rows_per_workgroup((int)dt);
   const int64_t row_tiles = (rows + per_wg - 1) / per_wg;
   if (rows > INT32_MAX || row_tiles * num_kv_heads * (int64_t)num_seqs > INT32_MAX)
     return PA_ERR_INVALID_ARG;  // one-dimensional grid
-  if (dt == PA_F32 && (int64_t)num_q_tokens * num_q_heads > INT32_MAX)
-    return PA_ERR_INVALID_ARG;  // fp32: one workgroup per (query row, query head)
 
   pa::PrefillArgs a{};
   a.out = out;

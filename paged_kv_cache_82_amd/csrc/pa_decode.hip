@@ -379,145 +379,6 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
   finish_partition<dt, D, NT>(a, s, h, 1, p, nparts, lds_fm, lds_fl, fo);
 }
 
-// ---- fp32 prefill on the vector ALU ---------------------------------------------------------
-
-// Causal multi-query attention for fp32 pools (the MFMA prefill kernel takes 16-bit data): one
-// workgroup per (query row, query head) runs the decode computation over the tokens the row
-// sees. [PA-summary] "The PagedAttention algorithm", applied to every query vector of a chunk:
-// query i of a sequence's n new tokens sits at position T - n + i and attends to positions
-// 0 .. T - n + i. Rows past the chunk (i >= n, with n = min(query rows, T, max_query_len))
-// are not written, as in the MFMA kernel. Block ids come 64 per wave at a time; K/V tiles are
-// double-buffered in registers. No part of the 16-bit workloads runs here.
-template <DT dt, int D, int BS, int NW>
-__global__ __launch_bounds__(NW * 64) void prefill_valu_kernel(const PrefillArgs a) {
-  constexpr int SB = valu_unit_tokens<BS>();  // tokens per unit; a block holds NSUB units
-  constexpr int NSUB = BS / SB;
-  using C = ValuCfg<dt, D, SB, NW>;
-  constexpr int E = C::E, VEC = C::VEC, R = C::R, TPI = C::TPI, NL = C::NL, NT = C::NT;
-  __shared__ float lds_o[NW][D];
-  __shared__ float lds_m[NW], lds_l[NW];
-
-  const int Hq = a.num_q_heads;
-  const int64_t L = blockIdx.x;
-  const int h = (int)(L % Hq);
-  const int row = (int)(L / Hq);
-  const int Nq = a.num_q_tokens;
-  // The sequence of this row: the last s with query_start[s] <= row (query_start ascending).
-  int lo = 0, hi = a.num_seqs;  // query_start[lo] <= row holds for lo = 0 when row is in range
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.query_start[mid] <= row) lo = mid; else hi = mid;
-  }
-  const int s = lo;
-  const int q0 = clampi(a.query_start[s], 0, Nq);
-  const int q1 = clampi(a.query_start[s + 1], q0, Nq);
-  const int64_t cap64 = (int64_t)a.max_blocks_per_seq * BS;
-  const int cap = (int)(cap64 < (int64_t)a.max_context_len ? cap64 : (int64_t)a.max_context_len);
-  const int T = clampi(a.context_lens[s], 0, cap);
-  int n = q1 - q0;
-  n = n < T ? n : T;
-  n = n < a.max_query_len ? n : a.max_query_len;
-  const int i = row - q0;
-  if (i < 0 || i >= n) return;  // uniform over the workgroup
-  const int t_end = T - n + i + 1;  // the row sees tokens 0 .. t_end - 1
-  const int nunit = (t_end + SB - 1) / SB;
-  const int kvh = h / (Hq / a.num_kv_heads);
-
-  const int lane = threadIdx.x & 63;
-  const int w = wave_id();
-  const int c = lane % R, r = lane / R;
-  float qf[VEC];
-  {
-    const u32x4 qraw = load16((const char*)a.q + (((int64_t)row * Hq + h) * D + c * VEC) * E);
-    const uint32_t wq[4] = {qraw[0], qraw[1], qraw[2], qraw[3]};
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) qf[e] = elem_of<dt>(wq, e) * a.scale_log2;
-  }
-  float m = kNegInf, l = 0.0f;
-  float o[VEC];
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) o[e] = 0.0f;
-
-  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  constexpr int row_bytes = D * E;
-  const uint32_t lane_off = (uint32_t)(r * row_bytes + c * 16);
-  const char* kbase = (const char*)a.k_cache;
-  const char* vbase = (const char*)a.v_cache;
-  // Chunks of 64 units per wave: wave w takes units base + w + k*NW, k < nb; lane k of
-  // my_id holds the id of the block holding the k-th.
-  for (int base = 0; base < nunit; base += 64 * NW) {
-    const int j = base + w + lane * NW;
-    const int my_id = (j < nunit) ? bt[j / NSUB] : 0;  // j / NSUB < max_blocks_per_seq
-    const int left = nunit - base < 64 * NW ? nunit - base : 64 * NW;
-    const int nb = (left - w + NW - 1) / NW;
-    auto fetch = [&](int k, u32x4* kr, u32x4* vr) {
-      const int32_t id = __builtin_amdgcn_readlane(my_id, k);
-      int64_t tile =
-          (clamp_block(id, a.num_blocks) * a.num_kv_heads + kvh) * (int64_t)(BS * row_bytes);
-      if constexpr (NSUB > 1) tile += (int64_t)(((base + w + k * NW) % NSUB) * SB * row_bytes);
-#pragma unroll
-      for (int q = 0; q < NL; ++q) {
-        kr[q] = load16(kbase + tile + lane_off + q * TPI * row_bytes);
-        vr[q] = load16(vbase + tile + lane_off + q * TPI * row_bytes);
-      }
-    };
-    auto consume = [&](int k, const u32x4* kr, const u32x4* vr) {
-      const int tok0 = (base + w + k * NW) * SB;
-      if (tok0 + SB <= t_end)
-        valu_block<dt, D, SB, NW, false>(qf, kr, vr, tok0, t_end, r, m, l, o);
-      else
-        valu_block<dt, D, SB, NW, true>(qf, kr, vr, tok0, t_end, r, m, l, o);
-    };
-    if (nb <= 0) continue;  // uniform
-    // Two buffers, unrolled so that both are register arrays; the fetch ahead is unconditional
-    // (past the end it re-reads the wave's last block).
-    u32x4 k0[NL], v0[NL], k1[NL], v1[NL];
-    fetch(0, k0, v0);
-    for (int k = 0; k < nb; k += 2) {
-      fetch(k + 1 < nb ? k + 1 : nb - 1, k1, v1);
-      consume(k, k0, v0);
-      if (k + 1 >= nb) break;
-      fetch(k + 2 < nb ? k + 2 : nb - 1, k0, v0);
-      consume(k + 1, k1, v1);
-    }
-  }
-
-  // Merge the TPI row states of this wave, then the waves (as in the decode kernel).
-#pragma unroll
-  for (int off = R; off < 64; off <<= 1) {
-    const float m2 = __shfl_xor(m, off);
-    const float l2 = __shfl_xor(l, off);
-    const float M = fmaxf(m, m2);
-    const float wa = rescale(m, M), wb = rescale(m2, M);
-    l = wa * l + wb * l2;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) o[e] = wa * o[e] + wb * __shfl_xor(o[e], off);
-    m = M;
-  }
-  if (r == 0) {
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) lds_o[w][c * VEC + e] = o[e];
-  }
-  if (lane == 0) {
-    lds_m[w] = m;
-    lds_l[w] = l;
-  }
-  __syncthreads();
-  for (int dim = threadIdx.x; dim < D; dim += NT) {
-    float M = kNegInf;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) M = fmaxf(M, lds_m[k]);
-    float acc = 0.0f, Lsum = 0.0f;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-      const float wgt = rescale(lds_m[k], M);
-      acc = fmaf(wgt, lds_o[k][dim], acc);
-      Lsum = fmaf(wgt, lds_l[k], Lsum);
-    }
-    store_elem<dt>(a.out, ((int64_t)row * Hq + h) * D + dim, acc / Lsum);
-  }
-}
-
 // ---- MFMA kernel (grouped query heads) -----------------------------------------------------
 
 // s_waitcnt vmcnt(N) (vmcnt in bits [3:0] and [15:14]), expcnt and lgkmcnt left at their maxima.
@@ -1224,32 +1085,6 @@ int decode_units_per_seq(DecodePath path, int num_q_heads, int num_kv_heads) {
   const int g = num_q_heads / num_kv_heads;
   const int cw = mfma_heads_per_workgroup(g);
   return num_kv_heads * ((g + cw - 1) / cw);
-}
-
-template <int D, int BS>
-static hipError_t launch_pf_valu_t(const PrefillArgs& a, hipStream_t stream) {
-  const int64_t total = (int64_t)a.num_q_tokens * a.num_q_heads;
-  if (total == 0) return hipSuccess;
-  if (total > INT32_MAX) return hipErrorInvalidValue;  // the API checks this first
-  PrefillArgs args_copy = a;
-  void* args[] = {&args_copy};
-  return hipLaunchKernel((const void*)prefill_valu_kernel<DT::F32, D, BS, kWaves>,
-                         dim3((unsigned)total), dim3(kWaves * 64), args, 0, stream);
-}
-
-hipError_t launch_prefill_valu(int head_dim, int block_size, const PrefillArgs& a,
-                               hipStream_t stream) {
-  switch (head_dim * 100 + block_size) {
-    case 6408: return launch_pf_valu_t<64, 8>(a, stream);
-    case 6416: return launch_pf_valu_t<64, 16>(a, stream);
-    case 6432: return launch_pf_valu_t<64, 32>(a, stream);
-    case 6464: return launch_pf_valu_t<64, 64>(a, stream);
-    case 12808: return launch_pf_valu_t<128, 8>(a, stream);
-    case 12816: return launch_pf_valu_t<128, 16>(a, stream);
-    case 12832: return launch_pf_valu_t<128, 32>(a, stream);
-    case 12864: return launch_pf_valu_t<128, 64>(a, stream);
-    default: return hipErrorInvalidValue;
-  }
 }
 
 int max_partition_tokens(DecodePath path, int block_size) {

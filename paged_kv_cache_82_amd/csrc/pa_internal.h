@@ -88,13 +88,10 @@ struct PrefillArgs {
 };
 
 bool prefill_supported(int dt, int head_dim, int block_size);
-// Query rows (query token x grouped head) one workgroup covers.
-int prefill_rows_per_workgroup();
+// Query rows (query token x grouped head) one workgroup covers, for dtype code dt.
+int prefill_rows_per_workgroup(int dt);
 hipError_t launch_prefill(int dt, int head_dim, int block_size, const PrefillArgs& a,
                           hipStream_t stream);
-// fp32 prefill: one workgroup per (query row, query head), on the vector ALU.
-hipError_t launch_prefill_valu(int head_dim, int block_size, const PrefillArgs& a,
-                               hipStream_t stream);
 
 hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                            const int32_t* slot_mapping, int n_tokens, int num_kv_heads,

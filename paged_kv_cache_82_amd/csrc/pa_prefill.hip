@@ -121,31 +121,15 @@ __device__ __forceinline__ float max8f(const f32x4& x, const f32x4& y) {
 }
 }  // namespace
 
-// Three workgroups per CU (12 waves, 144 KB of LDS at d = 128): the kernel fits 168 VGPRs by
-// reading K and V from LDS half a head dimension at a time and recomputing the few
-// lane-derived values that rare paths need; five values spill, each stored and reloaded once
-// per workgroup, outside both stage loops.
-template <DT dt, int D, int BS, int NW, int NCT, int NBUF>
-__global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillArgs a) {
-  static_assert(dt != DT::F32, "MFMA path takes 16-bit inputs");
-  using M = MfmaT<dt>;
-  using vec8 = typename M::vec8;
-  constexpr int E = 2;
-  constexpr int KC = D / 32;        // q.K MFMAs per 16-token tile
-  constexpr int MT = D / 16;        // p.V M-tiles; row r of tile mt is head dimension MT*r + mt
-  constexpr int RB = D * E;         // bytes per token row
-  constexpr int CPR = RB / 16;      // 16-byte chunks per row
-  constexpr int KT = 32;            // tokens per stage
-  constexpr int RPL = 1024 / RB;    // rows one wave-wide 16-byte-per-lane load covers
-  constexpr int WLW = KT * RB / 1024 / NW;  // wave-wide loads per wave per tensor per stage
-  constexpr int RPW = KT / NW;      // rows of a stage one wave loads: [RPW*w, RPW*(w+1))
-  constexpr int ROWS_W = 16 * NCT;
-  constexpr int ROWS = NW * ROWS_W;
-  constexpr int TILE = KT * RB;     // LDS bytes per tensor per stage
-  static_assert(KT * RB % (1024 * NW) == 0 && WLW * RPL == RPW, "a stage splits over the waves");
-  static_assert(BS % RPW == 0, "the rows one wave loads lie in one block");
-  __shared__ __attribute__((aligned(1024))) char lds[NBUF][2][TILE];  // [stage][K, V]
+// The work of one prefill workgroup: row tile `tile` of KV head kvh of sequence s, whose n
+// query tokens (rows q0 .. q0 + n - 1 of q and out) are the last n of its T cached tokens.
+struct PrefillTile {
+  int tile, kvh, s, q0, T, n;
+};
 
+template <int BS>
+__device__ __forceinline__ PrefillTile prefill_tile(const PrefillArgs& a) {
+  PrefillTile w;
   // Workgroup -> (row tile, KV head, sequence). Linear id L runs on XCD L % 8. The (sequence,
   // KV head) groups G = kvh + Hkv * s are dealt round-robin over the XCDs, so every XCD gets
   // its share of every sequence (handing each XCD a contiguous range of groups gave it whole
@@ -168,8 +152,8 @@ __global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillA
     G = dealt + r / rt;
     t_idx = (int)(r % rt);
   }
-  const int tile = rt - 1 - t_idx;
-  const int kvh = (int)(G % Hkv);
+  w.tile = rt - 1 - t_idx;
+  w.kvh = (int)(G % Hkv);
   // Extent of a sequence, clamped into the buffers the sizes describe.
   const int Nq = a.num_q_tokens;
   const int64_t cap64 = (int64_t)a.max_blocks_per_seq * BS;
@@ -215,6 +199,41 @@ __global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillA
   int n = q1 - q0;
   n = n < T ? n : T;
   n = n < a.max_query_len ? n : a.max_query_len;
+  w.s = s;
+  w.q0 = q0;
+  w.T = T;
+  w.n = n;
+  return w;
+}
+
+// Three workgroups per CU (12 waves, 144 KB of LDS at d = 128): the kernel fits 168 VGPRs by
+// reading K and V from LDS half a head dimension at a time and recomputing the few
+// lane-derived values that rare paths need; five values spill, each stored and reloaded once
+// per workgroup, outside both stage loops.
+template <DT dt, int D, int BS, int NW, int NCT, int NBUF>
+__global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillArgs a) {
+  static_assert(dt != DT::F32, "MFMA path takes 16-bit inputs");
+  using M = MfmaT<dt>;
+  using vec8 = typename M::vec8;
+  constexpr int E = 2;
+  constexpr int KC = D / 32;        // q.K MFMAs per 16-token tile
+  constexpr int MT = D / 16;        // p.V M-tiles; row r of tile mt is head dimension MT*r + mt
+  constexpr int RB = D * E;         // bytes per token row
+  constexpr int CPR = RB / 16;      // 16-byte chunks per row
+  constexpr int KT = 32;            // tokens per stage
+  constexpr int RPL = 1024 / RB;    // rows one wave-wide 16-byte-per-lane load covers
+  constexpr int WLW = KT * RB / 1024 / NW;  // wave-wide loads per wave per tensor per stage
+  constexpr int RPW = KT / NW;      // rows of a stage one wave loads: [RPW*w, RPW*(w+1))
+  constexpr int ROWS_W = 16 * NCT;
+  constexpr int ROWS = NW * ROWS_W;
+  constexpr int TILE = KT * RB;     // LDS bytes per tensor per stage
+  static_assert(KT * RB % (1024 * NW) == 0 && WLW * RPL == RPW, "a stage splits over the waves");
+  static_assert(BS % RPW == 0, "the rows one wave loads lie in one block");
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF][2][TILE];  // [stage][K, V]
+
+  const PrefillTile wk = prefill_tile<BS>(a);
+  const int tile = wk.tile, kvh = wk.kvh, s = wk.s, q0 = wk.q0, T = wk.T, n = wk.n;
+  const int Hkv = a.num_kv_heads;
   const int Hq = a.num_q_heads;
   const int g = Hq / Hkv;
   const int nrows = n * g;
@@ -576,12 +595,322 @@ __global__ __launch_bounds__(NW * 64, 3) void prefill_mfma_kernel(const PrefillA
   }
 }
 
+// ---- fp32 prefill on fp32 MFMA ---------------------------------------------------------------
+// The same attention with fp32 inputs, computed on v_mfma_f32_16x16x4_f32 (fp32 products and
+// sums throughout). Work decomposition as in the 16-bit kernel: a workgroup takes NW * NCT * 16
+// rows (query token, grouped head) of one (sequence, KV head), each wave NCT adjacent 16-row
+// column tiles, and walks the visible context in 32-token stages that come from HBM straight
+// into LDS (two stage buffers, one stage in flight while one is consumed), so each K/V row is
+// read once per workgroup instead of once per query row.
+//
+// Layouts of v_mfma_f32_16x16x4_f32, lane l = 16 j + r:
+//   A (16 x 4): lane l holds row r, k = j;   B (4 x 16): lane l holds column r, k = j;
+//   C (16 x 16): lane l holds rows 4 j .. 4 j + 3 of column r.
+// S^T = K Q^T: MFMA m of token tile u pairs k index j with head dimension (D/4) j + m, so lane
+// l reads D/4 consecutive floats of K row 16u + r and holds D/4 consecutive query floats.
+// O^T += V^T P^T: k-step (u, i) pairs k index j with token 16u + 4j + i, which makes the
+// lane's own weight for that token its P^T element. M-tile mt's row r is head dimension
+// 8r + 4((r >> 3) ^ (mt >> 2)) + (mt & 3) for D = 128 (4r + mt for D = 64): a lane reads its
+// V operands as two 16-byte chunks of one row, the first at chunk 2r + (r >> 3), so that the
+// 16 lanes reading one row hit 16 different bank groups.
+// K rows sit in LDS with their 16-byte chunks XOR-swizzled by the row's index mod 16 (the 16
+// lanes of a K read take 16 rows at one chunk); V rows are stored plain.
+template <int D, int BS, int NW, int NCT, int NBUF>
+__global__ __launch_bounds__(NW * 64, 2) void prefill_f32_kernel(const PrefillArgs a) {
+  constexpr int E = 4;
+  constexpr int KM = D / 4;         // q.K MFMAs per 16-token tile
+  constexpr int MT = D / 16;        // p.V M-tiles
+  constexpr int RB = D * E;         // bytes per token row
+  constexpr int CPR = RB / 16;      // 16-byte chunks per row
+  constexpr int KCH = D / 16;       // K chunks a lane reads per row (D/4 floats)
+  constexpr int KT = 32;            // tokens per stage
+  constexpr int RPL = 1024 / RB;    // rows one wave-wide 16-byte-per-lane load covers
+  constexpr int WLW = KT * RB / 1024 / NW;  // wave-wide loads per wave per tensor per stage
+  constexpr int RPW = KT / NW;      // rows of a stage one wave loads
+  constexpr int ROWS = NW * 16 * NCT;
+  constexpr int TILE = KT * RB;     // LDS bytes per tensor per stage
+  static_assert(D == 64 || D == 128, "head dims 64 and 128");
+  static_assert(KT * RB % (1024 * NW) == 0 && WLW * RPL == RPW, "a stage splits over the waves");
+  static_assert(BS % RPW == 0, "the rows one wave loads lie in one block");
+  static_assert(NBUF == 2, "one stage in flight while one is consumed");
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF][2][TILE];  // [stage][K, V]
+
+  const PrefillTile wk = prefill_tile<BS>(a);
+  const int kvh = wk.kvh, s = wk.s, q0 = wk.q0, T = wk.T, n = wk.n;
+  const int Hkv = a.num_kv_heads;
+  const int Hq = a.num_q_heads;
+  const int g = Hq / Hkv;
+  const int nrows = n * g;
+  const int W0 = wk.tile * ROWS;  // first row of the workgroup
+  if (W0 >= nrows) return;        // uniform over the workgroup: no barrier is skipped
+  const int base_pos = T - n;     // position of the chunk's first query token
+  const int p_hi_wg = base_pos + ((W0 + ROWS < nrows ? W0 + ROWS : nrows) - 1) / g;
+  const int nstages = (p_hi_wg + KT) / KT;  // stages covering positions 0 .. p_hi_wg
+  const int jlast = p_hi_wg / BS;           // last block the workgroup reads
+
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id();
+  const int r = lane & 15, j = lane >> 4;
+
+  // Scores are scaled by cs > 0 (see the 16-bit kernel): a negative scale is applied as
+  // |scale| to the negated query, a zero scale as 1 to a zero query; both are exact.
+  const float cs = a.scale_log2 == 0.0f ? 1.0f : __builtin_fabsf(a.scale_log2);
+  const uint32_t qflip = a.scale_log2 < 0.0f ? 0x80000000u : 0u;
+  const uint32_t qkeep = a.scale_log2 == 0.0f ? 0u : 0xffffffffu;
+
+  int pos[NCT];       // position of this lane's query row; -1 past the chunk
+  float qop[NCT][KM]; // Q^T operand: query row of column r, head dims (D/4) j + m
+  int p_hi_w = -1;    // last position any tile of this wave needs
+  int t_lo_w = 0x7fffffff;  // first position any tile of this wave starts at
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) {
+    const int Rt = W0 + 16 * (NCT * w + c);  // first row of the tile
+    const int R = Rt + r;
+    const bool valid = R < nrows;
+    const int i = valid ? R / g : 0;
+    const int head = kvh * g + (valid ? R % g : 0);
+    pos[c] = valid ? base_pos + i : -1;
+    const int t_lo = Rt < nrows ? base_pos + Rt / g : -1;
+    const int t_hi = Rt < nrows ? base_pos + ((Rt + 16 < nrows ? Rt + 16 : nrows) - 1) / g : -1;
+    p_hi_w = t_hi > p_hi_w ? t_hi : p_hi_w;
+    t_lo_w = t_lo < t_lo_w ? t_lo : t_lo_w;
+    const char* qp = (const char*)a.q + (((int64_t)(q0 + i) * Hq + head) * D + KM * j) * E;
+#pragma unroll
+    for (int x = 0; x < KM / 4; ++x) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (valid) raw = load16(qp + 16 * x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        qop[c][4 * x + e] = __builtin_bit_cast(float, (raw[e] ^ qflip) & qkeep);
+    }
+  }
+
+  f32x4 oacc[NCT][MT];
+  float nm[NCT], lsum[NCT], thr[NCT];  // running state, as in the 16-bit kernel
+  const float rcs = 1.0f / cs;
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) {
+    nm[c] = 0.0f;
+    thr[c] = kNegInf;
+    lsum[c] = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) oacc[c][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Block ids, 64 stages at a time (lane k = stage 64 * chunk + k), clamped into the pool.
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const int id_max = last_block_id(a.num_blocks);
+  auto load_ids = [&](int chunk) {
+    const int jb = (KT * (64 * chunk + fresh_lane()) + RPW * w) / BS;
+    return clamp_id(bt[jb < jlast ? jb : jlast], id_max);  // jlast < max_blocks_per_seq
+  };
+  int ids = load_ids(0);
+
+  auto kswz = [](int row) { return row & 15; };
+  // DMA offsets: lane L of wave-wide load k fills physical chunk L % CPR of stage row
+  // (w * WLW + k) * RPL + L / CPR.
+  const int64_t tile_bytes = (int64_t)BS * RB;
+  const uint64_t blk_bytes = (uint64_t)Hkv * tile_bytes;
+  const char* kbase = (const char*)a.k_cache + kvh * tile_bytes;
+  const char* vbase = (const char*)a.v_cache + kvh * tile_bytes;
+  uint32_t ko[WLW], vo[WLW];
+#pragma unroll
+  for (int k = 0; k < WLW; ++k) {
+    const int row = (w * WLW + k) * RPL + lane / CPR;
+    ko[k] = (uint32_t)((row % BS) * RB + ((lane % CPR) ^ kswz(row)) * 16);
+    vo[k] = (uint32_t)((row % BS) * RB + (lane % CPR) * 16);
+  }
+  auto issue_stage = [&](int st, int buf) {
+    if (st > 0 && (st & 63) == 0) {  // uniform
+      ids = load_ids(st >> 6);
+      __builtin_amdgcn_s_waitcnt(0x0F70 & ~0x0F);  // vmcnt(0): ids is never pending past here
+    }
+    uint64_t t = (uint64_t)(uint32_t)__builtin_amdgcn_readlane(ids, st & 63) * blk_bytes;
+    if constexpr (BS > KT) t += (uint64_t)((st % (BS / KT)) * TILE);
+    constexpr int span = BS > KT ? TILE : (int)(BS * RB);
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kbase + t, span);
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vbase + t, span);
+#pragma unroll
+    for (int k = 0; k < WLW; ++k) {
+      const int mload = w * WLW + k;
+      load16_tile_lds(kr, &lds[buf][0][mload * 1024], ko[k]);
+      load16_tile_lds(vr, &lds[buf][1][mload * 1024], vo[k]);
+    }
+  };
+
+  // LDS addresses this lane reads: K row 16u + r, logical chunk KCH j + x; V row 16u + 4j + i,
+  // chunks c0 = 2r + (r >> 3) and c1 = 2r + 1 - (r >> 3) (D = 128) or r (D = 64).
+  const int kc0 = KCH * j;
+  const int vc0 = D == 128 ? 2 * r + (r >> 3) : r;
+  const int vc1 = D == 128 ? 2 * r + 1 - (r >> 3) : r;
+
+  auto consume = [&](int tau0, auto bufc, bool mask, bool tail) {
+    constexpr int buf = decltype(bufc)::value;
+    const char* lk = &lds[buf][0][0];
+    const char* lv = &lds[buf][1][0];
+    // S^T = K Q^T: sacc[c][u][e] = score of token tau0 + 16u + 4j + e for column r; the two
+    // token tiles (and the column tiles) are independent accumulation chains, interleaved.
+    f32x4 sacc[NCT][2];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) sacc[c][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int x = 0; x < KCH; ++x) {
+      f32x4 kf[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)  // K row 16u + r: its swizzle is r
+        kf[u] = *reinterpret_cast<const f32x4*>(lk + (16 * u + r) * RB + ((kc0 + x) ^ r) * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int c = 0; c < NCT; ++c)
+            sacc[c][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[u][e], qop[c][4 * x + e],
+                                                               sacc[c][u], 0, 0, 0);
+    }
+    if (mask) {  // uniform; token tau0 + 16u + 4j + e is hidden from the lane's row past its position
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) {
+        const int lim = pos[c] - tau0 - 4 * j;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (16 * u + e > lim) sacc[c][u][e] = kNegInf;  // select
+      }
+    }
+    // Reference maximum raised only when a score exceeds it by more than kSlack (base 2), as
+    // in the 16-bit kernel.
+    float lr[NCT];
+    bool raise = false;
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      lr[c] = max8f(sacc[c][0], sacc[c][1]);
+      raise = raise || (lr[c] > thr[c]);
+    }
+    if (__builtin_amdgcn_ballot_w64(raise)) {  // uniform
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) {
+        const float lm = lr[c] * cs;
+        float bm = fmaxf(lm, __shfl_xor(lm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float mo = (thr[c] == kNegInf && nm[c] == 0.0f) ? kNegInf : -nm[c];
+        const float mn = fmaxf(mo, bm);
+        const float corr = (mo == kNegInf) ? (mn == kNegInf ? 1.0f : 0.0f) : fast_exp2(mo - mn);
+        lsum[c] *= corr;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) oacc[c][mt] *= corr;
+        nm[c] = mn == kNegInf ? 0.0f : -mn;
+        thr[c] = (mn + kSlack) * rcs;
+      }
+    }
+    float pw[NCT][2][4];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pw[c][u][e] = fast_exp2(__builtin_fmaf(sacc[c][u][e], cs, nm[c]));
+          lsum[c] += pw[c][u][e];
+        }
+    // O^T += V^T P^T, k-step (u, e): V row 16u + 4j + e.
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * u + 4 * j + e;
+        f32x4 va = *reinterpret_cast<const f32x4*>(lv + row * RB + vc0 * 16);
+        f32x4 vb = va;
+        if constexpr (D == 128) vb = *reinterpret_cast<const f32x4*>(lv + row * RB + vc1 * 16);
+        if (tail && tau0 + row > p_hi_wg) {  // stand-in or unused rows may hold anything
+          va = f32x4{0.f, 0.f, 0.f, 0.f};
+          vb = va;
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const float av = mt < 4 ? va[mt & 3] : vb[mt & 3];
+#pragma unroll
+          for (int c = 0; c < NCT; ++c)
+            oacc[c][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, pw[c][u][e], oacc[c][mt],
+                                                                0, 0, 0);
+        }
+      }
+  };
+
+  issue_stage(0, 0);
+  // One stage: wait for its loads (this wave's, then every wave's at the barrier, which also
+  // says the buffer the next loads go to has been consumed), issue the next stage's loads,
+  // consume. Unrolled two at a time so that buffer offsets are constants.
+  for (int st0 = 0; st0 < nstages; st0 += 2) {
+    static_for<2>([&](auto bc) {
+      constexpr int b = decltype(bc)::value;
+      const int st = st0 + b;
+      if (st >= nstages) return;  // uniform
+      __builtin_amdgcn_s_waitcnt(0x0F70 & ~0x0F);  // vmcnt(0): this wave's loads of stage st
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (st + 1 < nstages) issue_stage(st + 1, b ^ 1);
+      const int tau0 = st * KT;
+      if (tau0 > p_hi_w) return;  // uniform: every tile of this wave is done
+      consume(tau0, bc, tau0 + KT - 1 > t_lo_w, tau0 + KT - 1 > p_hi_wg);
+    });
+  }
+
+  // Normalise and store. oacc[c][mt][v] is O[column r][head dim of M-tile mt, row 4j + v].
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) {
+    float l = lsum[c];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (pos[c] < 0) continue;
+    const int R = W0 + 16 * (NCT * w + c) + r;
+    const int i = R / g;
+    const int head = kvh * g + R % g;
+    float* orow = (float*)a.out + ((int64_t)(q0 + i) * Hq + head) * D;
+    const float rl = 1.0f / l;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 4 * j + v;
+      if constexpr (D == 128) {
+        // head dims 8m .. 8m + 7: M-tiles 0..3 hold the first four unless m >= 8 (j >= 2)
+        const bool swap = j >= 2;
+        f32x4 lo, hi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = oacc[c][e][v] * rl, x1 = oacc[c][4 + e][v] * rl;
+          lo[e] = swap ? x1 : x0;
+          hi[e] = swap ? x0 : x1;
+        }
+        *reinterpret_cast<f32x4*>(orow + 8 * m) = lo;
+        *reinterpret_cast<f32x4*>(orow + 8 * m + 4) = hi;
+      } else {
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = oacc[c][e][v] * rl;
+        *reinterpret_cast<f32x4*>(orow + 4 * m) = o;
+      }
+    }
+  }
+}
+
 // ---- host side ------------------------------------------------------------------------------
 
-int prefill_rows_per_workgroup() { return kPrefillWaves * kPrefillColTiles * 16; }
+// fp32 workgroups take one 16-row column tile per wave: 64 rows, so that a 64-token MHA chunk
+// (64 rows per sequence and head) keeps all four waves busy. Measured on MI355X, 13B-shape fp32
+// chunks of 64 tokens: 215.3 us against 338.4 us with two tiles per wave (128-row workgroups,
+// half of whose waves had no row).
+constexpr int kPrefillF32ColTiles = 1;
+
+int prefill_rows_per_workgroup(int dt) {
+  return kPrefillWaves * (dt == 0 ? kPrefillF32ColTiles : kPrefillColTiles) * 16;
+}
 
 bool prefill_supported(int dt, int head_dim, int block_size) {
-  if (dt < 0 || dt > 2) return false;  // 16-bit inputs on MFMA, fp32 on the vector ALU
+  if (dt < 0 || dt > 2) return false;  // fp32, fp16 and bf16, each on its own MFMA kernel
   if (head_dim != 64 && head_dim != 128) return false;
   return block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64;
 }
@@ -609,6 +938,36 @@ static hipError_t launch_pf_bs(int bs, const PrefillArgs& a, hipStream_t st) {
   }
 }
 
+template <int D, int BS>
+static hipError_t launch_pf32(const PrefillArgs& a, hipStream_t stream) {
+  const int64_t total = (int64_t)a.row_tiles * a.num_kv_heads * a.num_seqs;
+  if (total == 0) return hipSuccess;
+  PrefillArgs args_copy = a;
+  void* args[] = {&args_copy};
+  return hipLaunchKernel(
+      (const void*)prefill_f32_kernel<D, BS, kPrefillWaves, kPrefillF32ColTiles, 2>,
+      dim3((unsigned)total), dim3(kPrefillWaves * 64), args, 0, stream);
+}
+
+template <int D>
+static hipError_t launch_pf32_bs(int bs, const PrefillArgs& a, hipStream_t st) {
+  switch (bs) {
+    case 8: return launch_pf32<D, 8>(a, st);
+    case 16: return launch_pf32<D, 16>(a, st);
+    case 32: return launch_pf32<D, 32>(a, st);
+    case 64: return launch_pf32<D, 64>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+static hipError_t launch_pf32_d(int d, int bs, const PrefillArgs& a, hipStream_t st) {
+  switch (d) {
+    case 64: return launch_pf32_bs<64>(bs, a, st);
+    case 128: return launch_pf32_bs<128>(bs, a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <DT dt>
 static hipError_t launch_pf_d(int d, int bs, const PrefillArgs& a, hipStream_t st) {
   switch (d) {
@@ -621,7 +980,7 @@ static hipError_t launch_pf_d(int d, int bs, const PrefillArgs& a, hipStream_t s
 hipError_t launch_prefill(int dt, int head_dim, int block_size, const PrefillArgs& a,
                           hipStream_t stream) {
   switch (dt) {
-    case 0: return launch_prefill_valu(head_dim, block_size, a, stream);
+    case 0: return launch_pf32_d(head_dim, block_size, a, stream);
     case 1: return launch_pf_d<DT::F16>(head_dim, block_size, a, stream);
     case 2: return launch_pf_d<DT::BF16>(head_dim, block_size, a, stream);
     default: return hipErrorInvalidValue;

@@ -62,7 +62,6 @@ def do_pmc(args) -> str:
     f_factor = COPY_BYTES / (cf * 1024)
     w_factor = COPY_BYTES / (cw * 1024)
     kind = args.kind
-    sources = kind
     if kind == "decode":
         step = bench.make_workload(args.workload, poison=False)
         alg = bench.algorithmic_bytes(step)["decode"]
@@ -72,9 +71,7 @@ def do_pmc(args) -> str:
 
         step = getattr(workloads, bench.WORKLOADS["prefill-" + args.workload][0])(poison=False)
         alg = bench.prefill_bytes(step)
-        # fp32 prefill runs on the vector-ALU kernel, which is built from the decode sources
-        needle, sources = (("prefill_valu_kernel", "decode") if step.dtype == "f32"
-                           else ("prefill_mfma_kernel", "prefill"))
+        needle = "prefill_f32_kernel" if step.dtype == "f32" else "prefill_mfma_kernel"
     name, fk = pick(fetch, needle)
     _, wk = pick(write, needle)
     rd = fk * 1024 * f_factor
@@ -91,7 +88,7 @@ def do_pmc(args) -> str:
         f"hbm_bytes_per_launch: {rd + wr:.6g}",
         f"algorithmic_bytes_per_launch: {alg:.6g}",
         f"traffic_over_algorithmic: {(rd + wr) / alg:.4f}",
-        f"source_sha256_16: {bench.source_hash(sources)}",
+        f"source_sha256_16: {bench.source_hash(kind)}",
     ]
     return "\n".join(lines) + "\n"
 

@@ -191,9 +191,10 @@ def test_prefill_argument_checks(lib):
     assert call(qs=None) == PA_ERR_INVALID_ARG
     assert call(out=V(0x1008)) == PA_ERR_INVALID_ARG  # q/out rows need 16-byte alignment
     assert call(Hq=8, Hkv=3) == PA_ERR_INVALID_ARG
-    # fp32 runs on the vector ALU: one workgroup per (query row, query head), at most 2^31 - 1
+    # fp32 takes the same grid as the 16-bit kernel (64-row workgroups): its limits are the grid's
     assert call(dt=F32, d=96) == PA_ERR_UNSUPPORTED
-    assert call(dt=F32, Nq=1 << 29, Hq=8, Hkv=8) == PA_ERR_INVALID_ARG
+    assert call(dt=F32, maxn=1 << 29, Hq=16, Hkv=2) == PA_ERR_INVALID_ARG  # rows > 2^31 - 1
+    assert call(dt=F32, maxn=1 << 27, S=2048, Hq=8, Hkv=8) == PA_ERR_INVALID_ARG  # grid too large
     assert call(d=96) == PA_ERR_UNSUPPORTED
     assert call(B=128) == PA_ERR_UNSUPPORTED
     assert call(M=0) == PA_ERR_INVALID_ARG
