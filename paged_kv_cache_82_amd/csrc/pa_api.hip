@@ -52,26 +52,46 @@ bool choose_path(pa_dtype dt, int num_q_heads, int num_kv_heads, int head_dim, i
 // per CU, 100-132 KB of LDS). Measured on MI355X: unsplit 13B-shape and GQA batches ran 25-35%
 // faster than with 512-token partitions; long contexts peaked at 2048; a batch of 256
 // (sequence, 32-head) units (128 sequences, 64 query / 2 KV heads, lengths 128..4096) took 59.9
-// us whole against 69.6 / 78.6 / 98.8 us with 2048 / 1024 / 512-token partitions. 0 = automatic.
+// us whole against 69.6 / 78.6 / 98.8 us with 2048 / 1024 / 512-token partitions. The halving
+// counts the grid at half the longest length for the vector-ALU kernel and at the longest for
+// the MFMA kernel, whose short workgroups cost more than its idle CUs: 128 (sequence, 32-head)
+// units (64 sequences, 64 query / 2 KV heads, lengths 128..4096) took 37.3 us with 2048-token
+// partitions against 46.4 us with 1024. 0 = automatic.
 int choose_partition(int num_seqs, int units_per_seq, int max_context_len, int cap,
-                     int requested, int many) {
+                     int requested, pa::DecodePath path) {
   if (requested > 0) return requested;
+  const bool mfma = path == pa::DecodePath::Mfma;
+  const int many = mfma ? 256 : 1024;
   const int64_t units = (int64_t)num_seqs * units_per_seq;
   const int whole = ((max_context_len + 31) / 32) * 32;
   if (whole <= 0) return 32;
   if (units >= many && whole <= cap) return whole;
   int P = 2048 < cap ? 2048 : cap;
-  // workgroups if lengths average half the maximum
-  auto est = [&](int p) { return units * ((max_context_len / 2 + p - 1) / p); };
+  const int span = mfma ? max_context_len : max_context_len / 2;
+  auto est = [&](int p) { return units * ((span + p - 1) / p); };
   while (P > 256 && est(P) < many) P /= 2;
   return P < whole ? P : whole;
 }
 
-int many_units(pa::DecodePath path) { return path == pa::DecodePath::Mfma ? 256 : 1024; }
-
 int parts_for(int max_context_len, int P) {
   const int n = (max_context_len + P - 1) / P;
   return n > 1 ? n : 1;
+}
+
+// The automatic plan of a decode call: partition size, partition count and workspace.
+struct DecodePlan {
+  int P, max_parts;
+  pa::WorkspaceLayout L;
+};
+
+DecodePlan plan_decode(DecodePath path, int num_seqs, int num_q_heads, int num_kv_heads,
+                       int head_dim, int max_context_len, int partition_tokens, int cap) {
+  DecodePlan pl{};
+  pl.P = choose_partition(num_seqs, pa::decode_units_per_seq(path, num_q_heads, num_kv_heads),
+                          max_context_len, cap, partition_tokens, path);
+  pl.max_parts = parts_for(max_context_len, pl.P);
+  pl.L = pa::workspace_layout(num_seqs, num_q_heads, head_dim, pl.max_parts);
+  return pl;
 }
 
 pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
@@ -135,12 +155,9 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
       !aligned(out, elem_bytes(dt)) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
     return PA_ERR_INVALID_ARG;
 
-  const int P = choose_partition(num_seqs,
-                                 pa::decode_units_per_seq(path, num_q_heads, num_kv_heads),
-                                 max_context_len, cap, partition_tokens, many_units(path));
-  const int max_parts = parts_for(max_context_len, P);
-  const pa::WorkspaceLayout L =
-      pa::workspace_layout(num_seqs, num_q_heads, head_dim, max_parts);
+  const DecodePlan plan = plan_decode(path, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                      max_context_len, partition_tokens, cap);
+  const pa::WorkspaceLayout& L = plan.L;
   if (use_scratch) {
     workspace = nullptr;
     workspace_bytes = PA_DECODE_SCRATCH_BYTES;
@@ -167,8 +184,8 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.max_context_len = max_context_len;
-  a.partition_tokens = P;
-  a.max_parts = max_parts;
+  a.partition_tokens = plan.P;
+  a.max_parts = plan.max_parts;
   char* ws = (char*)workspace;
   a.part_m = L.total ? (float*)(ws + L.m_off) : nullptr;
   a.part_l = L.total ? (float*)(ws + L.l_off) : nullptr;
@@ -266,11 +283,9 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
   if (!choose_path(dt, num_q_heads, num_kv_heads, head_dim, block_size, &path)) return 0;
   const int cap = pa::max_partition_tokens(path, block_size);
   if (partition_tokens > cap) return 0;
-  const int P = choose_partition(num_seqs,
-                                 pa::decode_units_per_seq(path, num_q_heads, num_kv_heads),
-                                 max_context_len, cap, partition_tokens, many_units(path));
-  return pa::workspace_layout(num_seqs, num_q_heads, head_dim, parts_for(max_context_len, P))
-      .total;
+  return plan_decode(path, num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                     partition_tokens, cap)
+      .L.total;
 }
 
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -70,6 +70,41 @@ def test_wide_groups(dt, Hq, Hkv, d, P):
     _run_and_check(step, partition_tokens=P, what=f"wide {dt} {Hq}/{Hkv} d{d} P{P}")
 
 
+FEW_UNIT_CASES = [
+    # (Hq, Hkv, d, B, lengths): small grouped-query batches with very uneven lengths
+    (16, 2, 128, 16, [4000] + [1] * 30 + [0] * 5),     # one long sequence, many tiny and empty
+    (64, 2, 128, 16, [0, 1, 33, 64, 65, 500, 1025, 2047]),  # 32-head units
+    (48, 1, 128, 32, [17, 900, 3000, 0, 64]),          # 2 head tiles of 32, the second part-empty
+    (8, 2, 64, 8, [257, 1, 31, 2500, 96]),
+    (32, 4, 128, 64, [130, 4095, 7, 640]),
+]
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("case", range(len(FEW_UNIT_CASES)))
+def test_few_unit_batches(dt, case):
+    # few (sequence, head tile) units: the automatic plan splits the long sequences into
+    # partitions and leaves the short ones whole
+    Hq, Hkv, d, B, lens = FEW_UNIT_CASES[case]
+    step = make_step("few", 500 + case, lens, Hq, Hkv, d, B, dt)
+    _run_and_check(step, what=f"few units {dt} case {case}")
+
+
+def test_workspace_reused_with_other_lengths():
+    # partial states are rewritten by every call: a second call with other lengths (other
+    # splits) on the same workspace must not see the first call's
+    shared_ws = None
+    for lens in ([3000, 5, 700, 0, 64], [10, 2990, 0, 650, 1]):
+        step = make_step("reuse", 520, lens, 16, 2, 128, 16, "bf16")
+        ref, _, _ = oracle.run_step(step)
+        dev = DevStep(step)
+        if shared_ws is None:
+            shared_ws = dev.workspace
+        assert dev.workspace.numel() <= shared_ws.numel()
+        dev.workspace = shared_ws
+        assert_attention_close(dev.run(), ref, step.dtype, f"reused workspace {lens}")
+
+
 @pytest.mark.parametrize("path", ["valu", "mfma"])
 def test_both_decode_paths_on_gqa(path, decode_kernel):
     decode_kernel(path)
