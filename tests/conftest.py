@@ -44,3 +44,13 @@ def pytest_terminal_summary(terminalreporter):
         terminalreporter.write_line("full-size parity (observed max errors):")
         for line in PARITY_LOG:
             terminalreporter.write_line("  " + line)
+        # the same lines as JSON, in the folder a GPU run's outputs are collected from
+        import json
+
+        out = os.path.join(ROOT, "gpurun_out")
+        try:
+            os.makedirs(out, exist_ok=True)
+            with open(os.path.join(out, "parity_observed.json"), "w") as f:
+                json.dump({"full_size_parity": list(PARITY_LOG)}, f, indent=1)
+        except OSError:
+            pass
