@@ -42,7 +42,7 @@ def _decode_case(i):
 
 def _prefill_case(i):
     rng = np.random.default_rng(8000 + i)
-    dt = ["f16", "bf16"][rng.integers(2)]
+    dt = ["f16", "bf16", "f32"][rng.integers(3)]
     d = int(rng.choice([64, 128]))
     B = int(rng.choice([8, 16, 32, 64]))
     Hkv = int(rng.choice([1, 2]))
@@ -81,4 +81,14 @@ def test_prefill_random_shapes(i):
     got = dev.run()
     assert np.array_equal(_bits(to_host(dev.k_cache, step.dtype)), _bits(kc))
     assert np.array_equal(_bits(to_host(dev.v_cache, step.dtype)), _bits(vc))
-    assert_attention_close(got, ref, step.dtype, f"prefill fuzz {i}")
+    factor = abs(c["scale"]) * c["d"] ** 0.5
+    if step.dtype == "f32" and factor > 1.0:
+        # scores larger than N(0,1) data at scale 1/sqrt(d) carry a proportionally larger fp32
+        # rounding error (see test_gpu_prefill): the 1e-5 bound scales with them
+        owned = np.zeros(step.num_q_tokens, bool)
+        owned[step.query_start[0]:step.query_start[-1]] = True
+        assert np.isfinite(got[owned]).all()
+        err = float(np.abs(got[owned].astype(np.float64) - ref[owned]).max())
+        assert err <= factor * 1e-5, (i, err)
+    else:
+        assert_attention_close(got, ref, step.dtype, f"prefill fuzz {i}")

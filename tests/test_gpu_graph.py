@@ -72,9 +72,9 @@ def test_shared_prefix_step_graph_replay():
     _replays_match(run_step, [dev.out, dev.k_cache, dev.v_cache], step.dtype)
 
 
-def test_prefill_step_graph_replay():
-    step = make_prefill_step("gprefill", 510, [300, 41, 129], [200, 41, 3], 16, 2, 128, 16,
-                             "bf16")
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_prefill_step_graph_replay(dt):
+    step = make_prefill_step("gprefill", 510, [300, 41, 129], [200, 41, 3], 16, 2, 128, 16, dt)
     dev = DevPrefill(step)
 
     def run_step():
