@@ -564,6 +564,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="time the default (13B-shape) workload only, not the other decode "
                          "workloads after it")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="decode steps: pa_write_kv then pa_decode, not pa_decode_append")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of replays of a captured step graph")
     ap.add_argument("--placement", default="random", choices=["random", "contiguous"],
@@ -691,10 +693,25 @@ def measure_decode(workload: str, args, cpu: bool, compare_plain: bool = False) 
 
     torch.cuda.synchronize()
 
+    # The step's KV write and decode in one launch (pa_decode_append) when the step writes
+    # exactly one new token per sequence, in sequence order, and copies nothing; otherwise (and
+    # with --separate-write) pa_write_kv, then the decode.
+    fused = (not args.separate_write and not shared_api and len(step.copies) == 0
+             and len(step.writes) == 1 and step.writes[0].k_new.shape[0] == step.num_seqs
+             and bool((step.context_lens > 0).all()))
+
     def one_step(i, ev=None):
         kc, vc = pools[i % ncopy]
         if len(step.copies):
             pa.pa_copy_blocks(kc, vc, copies)
+        if fused:
+            kn, vn, sm = writes[0]
+            if ev is not None:
+                ev[0].record()
+            pa.pa_decode_append(out, q, kc, vc, kn, vn, sm, bt, cl, scale, maxT, ws, P)
+            if ev is not None:
+                ev[1].record()
+            return
         for kn, vn, sm in writes:
             pa.pa_write_kv(kc, vc, kn, vn, sm)
         if ev is not None:
@@ -798,6 +815,10 @@ def measure_decode(workload: str, args, cpu: bool, compare_plain: bool = False) 
             "parallelism": "single GPU",
         },
         "execution": "eager" if args.no_graph else f"HIP graph of {ncopy} steps, replayed",
+        "step_calls": ("pa_decode_append (the KV write and the decode in one launch)" if fused
+                       else ("pa_copy_blocks + " if len(step.copies) else "")
+                       + "pa_write_kv + " + ("pa_decode_shared_prefix" if shared_api
+                                             else "pa_decode")),
         "eager_ms_per_step": round(eager_wall / args.steps * 1e3, 5),
         "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
         "seq_tokens_per_s": round(nb["tokens"] / (wall / args.steps), 1),

@@ -164,6 +164,33 @@ pa_status pa_decode_noalloc(void *out, const void *q, const void *k_cache, const
                             pa_dtype dt, void *stream);
 
 /*
+ * pa_decode_append — the decode step's KV write and attention in one launch: every sequence's
+ * newest token is stored in the pool and attended to together with its cached tokens.
+ * [PA-summary] "Key idea: virtual memory for the KV cache" (the token a step generates goes to
+ * the sequence's last block, through its slot) and "The PagedAttention algorithm".
+ * With T = context_lens[s] counting the new token: positions 0 .. T-2 are read from the pool
+ * through block_tables[s] exactly as pa_decode reads them; position T-1 is k_new[s], v_new[s]
+ * ([num_seqs][num_kv_heads][head_dim], dtype `dt`, 16-byte aligned), folded into the running
+ * softmax of the sequence's last partition as one more token. The rows are also stored bit for
+ * bit at slot_mapping[s] (int32 [num_seqs]; a negative slot, or one past the pool, stores
+ * nothing; the token is attended to either way), as pa_write_kv would. T == 0 gives out = 0 and
+ * stores nothing.
+ * The result equals pa_write_kv followed by pa_decode when slot_mapping[s] is the slot of
+ * position T-1 in the table (the decode step's invariant), within the attention tolerance (the
+ * new token enters the sums last rather than in its block's place). Other pool rows are only
+ * read; concurrent readers of the new token's slot in the same call see it masked.
+ * Arguments otherwise as pa_decode (same workspace size: pa_decode_workspace_size with the
+ * same sizes), same errors; k_new, v_new and slot_mapping must be non-null when num_seqs > 0.
+ */
+pa_status pa_decode_append(void *out, const void *q, void *k_cache, void *v_cache,
+                           const void *k_new, const void *v_new, const int32_t *slot_mapping,
+                           const int32_t *block_tables, const int32_t *context_lens,
+                           float scale, int num_seqs, int num_q_heads, int num_kv_heads,
+                           int head_dim, int block_size, int max_blocks_per_seq,
+                           int64_t num_blocks, int max_context_len, int partition_tokens,
+                           void *workspace, size_t workspace_bytes, pa_dtype dt, void *stream);
+
+/*
  * pa_set_decode_kernel — which decode kernel pa_decode, pa_decode_noalloc and
  * pa_decode_workspace_size use from now on, process-wide. PA_DECODE_AUTO (the default): the
  * MFMA kernel for f16/bf16 with at least two query heads per KV head, the vector-ALU kernel

@@ -57,6 +57,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.pa_decode.restype = I
         lib.pa_decode_noalloc.argtypes = [P, P, P, P, P, P, F, I, I, I, I, I, I, I64, I, I, I, P]
         lib.pa_decode_noalloc.restype = I
+        lib.pa_decode_append.argtypes = [P, P, P, P, P, P, P, P, P, F, I, I, I, I, I, I, I64, I,
+                                         I, P, SZ, I, P]
+        lib.pa_decode_append.restype = I
         lib.pa_decode_shared_prefix.argtypes = [P, P, P, P, P, P, P, P, F, I, I, I, I, I, I, I,
                                                 I64, I, I, I, I, P, SZ, I, P]
         lib.pa_decode_shared_prefix.restype = I
@@ -150,6 +153,22 @@ def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scal
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         _ptr(context_lens), float(scale), S, Hq, Hkv, d, B, block_tables.shape[1], N,
         int(max_context_len), int(partition_tokens), _dtype_code(q), _stream(stream)))
+
+
+def pa_decode_append(out, q, k_cache, v_cache, k_new, v_new, slot_mapping, block_tables,
+                     context_lens, scale, max_context_len, workspace=None, partition_tokens=0,
+                     stream=None) -> None:
+    """The decode step's KV write and attention in one launch: k_new, v_new [S, Hkv, d] are
+    every sequence's newest token (position context_lens[s] - 1), attended to directly and
+    stored at slot_mapping[s] (int32 [S]; negative: not stored). Workspace as pa_decode."""
+    S, Hq, d = q.shape
+    N, Hkv, B, _ = k_cache.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pa_decode_append", load().pa_decode_append(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+        _ptr(slot_mapping), _ptr(block_tables), _ptr(context_lens), float(scale), S, Hq, Hkv, d,
+        B, block_tables.shape[1], N, int(max_context_len), int(partition_tokens),
+        _ptr(workspace), ws_bytes, _dtype_code(q), _stream(stream)))
 
 
 def pa_decode_shared_prefix_workspace_size(num_seqs, num_groups, num_q_heads, num_kv_heads,

@@ -125,14 +125,23 @@ pa_status scratch_ptr(void** ptr) {
   return PA_OK;
 }
 
+// The newest token of each sequence, for pa_decode_append (all null otherwise).
+struct AppendRows {
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  const int32_t* slots = nullptr;
+};
+
 // pa_decode with the split-K partials in `workspace` (the caller's buffer), or, with
-// use_scratch, in the library's static scratch array (pa_decode_noalloc; workspace ignored).
+// use_scratch, in the library's static scratch array (pa_decode_noalloc; workspace ignored);
+// with `app`, pa_decode_append.
 pa_status decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, const int32_t* context_lens, float scale,
                       int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                       int block_size, int max_blocks_per_seq, int64_t num_blocks,
                       int max_context_len, int partition_tokens, void* workspace,
-                      size_t workspace_bytes, bool use_scratch, pa_dtype dt, void* stream) {
+                      size_t workspace_bytes, bool use_scratch, pa_dtype dt, void* stream,
+                      const AppendRows& app = AppendRows{}) {
   if (!valid_dtype(dt)) return PA_ERR_INVALID_ARG;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       block_size <= 0 || max_blocks_per_seq < 0 || num_blocks <= 0 || max_context_len < 0 ||
@@ -154,6 +163,11 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(out, elem_bytes(dt)) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
     return PA_ERR_INVALID_ARG;
+  const bool append = app.k_new || app.v_new || app.slots;
+  if (append && (!app.k_new || !app.v_new || !app.slots || !aligned(app.k_new, 16) ||
+                 !aligned(app.v_new, 16) || !aligned(app.slots, 4)))
+    return PA_ERR_INVALID_ARG;
+  if (append && num_seqs > 65534) return PA_ERR_INVALID_ARG;  // one more grid slice stores
 
   const DecodePlan plan = plan_decode(path, num_seqs, num_q_heads, num_kv_heads, head_dim,
                                       max_context_len, partition_tokens, cap);
@@ -190,6 +204,12 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   a.part_m = L.total ? (float*)(ws + L.m_off) : nullptr;
   a.part_l = L.total ? (float*)(ws + L.l_off) : nullptr;
   a.part_o = L.total ? (float*)(ws + L.o_off) : nullptr;
+  if (append) {
+    a.k_new = app.k_new;
+    a.v_new = app.v_new;
+    a.new_slots = app.slots;
+    a.append = 1;
+  }
   return from_hip(pa::launch_decode(path, (int)dt, head_dim, block_size, a, (hipStream_t)stream));
 }
 
@@ -310,6 +330,24 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const
                      num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                      num_blocks, max_context_len, partition_tokens, nullptr, 0, true, dt,
                      stream);
+}
+
+pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cache,
+                           const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           float scale, int num_seqs, int num_q_heads, int num_kv_heads,
+                           int head_dim, int block_size, int max_blocks_per_seq,
+                           int64_t num_blocks, int max_context_len, int partition_tokens,
+                           void* workspace, size_t workspace_bytes, pa_dtype dt, void* stream) {
+  AppendRows app;
+  app.k_new = k_new;
+  app.v_new = v_new;
+  app.slots = slot_mapping;
+  if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping)) return PA_ERR_INVALID_ARG;
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                     num_blocks, max_context_len, partition_tokens, workspace, workspace_bytes,
+                     false, dt, stream, app);
 }
 
 pa_status pa_set_decode_kernel(pa_decode_kernel kernel) {

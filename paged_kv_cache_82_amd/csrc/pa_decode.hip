@@ -50,6 +50,42 @@ __device__ __forceinline__ int seq_len(const DecodeArgs& a, int s, int BS) {
   return T < 0 ? 0 : (T > cap ? cap : T);
 }
 
+// Tokens of a sequence of T (seq_len) read from the pool: all of them, or all but the newest
+// when the call appends it (pa_decode_append).
+__device__ __forceinline__ int pool_len(const DecodeArgs& a, int T) {
+  return a.append ? (T > 0 ? T - 1 : 0) : T;
+}
+
+// Partitions of a sequence of T tokens: 0 for an empty sequence; with an appended token at
+// least one, whose last partition folds the new token in.
+__device__ __forceinline__ int parts_of(const DecodeArgs& a, int T) {
+  const int P = a.partition_tokens;
+  if (T == 0) return 0;
+  const int n = (pool_len(a, T) + P - 1) / P;
+  return n > 0 ? n : 1;
+}
+
+// The appended tokens' K and V rows of KV head kvh, every sequence's stored at new_slots[s]
+// (as pa_write_kv would; nothing for a negative slot, one past the pool, or an empty sequence),
+// in 16-byte chunks. A workgroup of the grid's last sequence slice does this: at the end of a
+// decode workgroup the stores would hold it (and its CU slot) until they complete.
+template <DT dt, int D, int NT>
+__device__ void store_new_tokens(const DecodeArgs& a, int kvh, int BS) {
+  constexpr int CH = D * Elem<dt>::bytes / 16;  // 16-byte chunks per row
+  for (int64_t i = threadIdx.x; i < (int64_t)a.num_seqs * 2 * CH; i += NT) {
+    const int s = (int)(i / (2 * CH));
+    const int j = (int)(i % (2 * CH));
+    const int slot = a.new_slots[s];
+    if (slot < 0 || slot / BS >= a.num_blocks || seq_len(a, s, BS) == 0) continue;
+    const bool v = j >= CH;
+    const int c = v ? j - CH : j;
+    const int64_t row = (((int64_t)(slot / BS) * a.num_kv_heads + kvh) * BS + slot % BS) * CH;
+    const int64_t src = ((int64_t)s * a.num_kv_heads + kvh) * CH;
+    const u32x4 x = reinterpret_cast<const u32x4*>(v ? a.v_new : a.k_new)[src + c];
+    reinterpret_cast<u32x4*>(const_cast<void*>(v ? a.v_cache : a.k_cache))[row + c] = x;
+  }
+}
+
 // After a workgroup has merged its partition into (fm, fl, fo[nh][D]) in LDS: store the final
 // output when the sequence has a single partition, otherwise the partial state for the merge
 // kernel.
@@ -105,8 +141,7 @@ __global__ __launch_bounds__(D) void merge_partitions_kernel(const DecodeArgs a)
   if constexpr (GROUP) {
     nparts = clampi(a.part_n[(int64_t)s * a.num_q_heads + h], 0, a.max_parts);
   } else {
-    const int T = seq_len(a, s, BS);
-    nparts = (T + a.partition_tokens - 1) / a.partition_tokens;
+    nparts = parts_of(a, seq_len(a, s, BS));
   }
   if (nparts <= 1) return;
   const int64_t base = ((int64_t)s * a.num_q_heads + h) * a.max_parts;
@@ -240,6 +275,11 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
 
   const int p = blockIdx.x, h = blockIdx.y;
   const int s = blockIdx.z;
+  if (s == a.num_seqs) {  // the appended tokens' store slice (pa_decode_append only)
+    const int g = a.num_q_heads / a.num_kv_heads;
+    if (p == 0 && h % g == 0) store_new_tokens<dt, D, NT>(a, h / g, BS);
+    return;
+  }
   const int P = a.partition_tokens;
   const int jb0 = p * (P / SB);  // first unit of the partition
   const int lane = threadIdx.x & 63;
@@ -258,15 +298,17 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
       load16((const char*)a.q + (((int64_t)s * a.num_q_heads + h) * D + c * VEC) * E);
 
   const int T = seq_len(a, s, BS);
-  const int nparts = (T + P - 1) / P;
+  const int nparts = parts_of(a, T);
   if (T == 0) {
     if (p == 0) store_zeros<dt, D, NT>(a, s, h, 1);
     return;
   }
   if (p >= nparts) return;
-  const int kvh = h / (a.num_q_heads / a.num_kv_heads);
+  const int g = a.num_q_heads / a.num_kv_heads;
+  const int kvh = h / g;
+  const int Tp = pool_len(a, T);  // tokens read from the pool (an appended one is not)
   const int t0 = p * P;
-  const int t1 = (T < t0 + P) ? T : t0 + P;
+  const int t1 = (Tp < t0 + P) ? Tp : t0 + P;
   const int jb1 = (t1 + SB - 1) / SB;
 
   float qf[VEC];
@@ -274,6 +316,16 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
     const uint32_t wq[4] = {qraw[0], qraw[1], qraw[2], qraw[3]};
 #pragma unroll
     for (int e = 0; e < VEC; ++e) qf[e] = elem_of<dt>(wq, e) * a.scale_log2;
+  }
+  // An appended token (pa_decode_append): wave 0 of the last partition folds it into its
+  // running state after its blocks, as one more token; its rows load now, in flight during the
+  // loop. (The grid's last slice stores it in the pool.)
+  const bool fold_new = a.append && p == nparts - 1 && w == 0;  // uniform per wave
+  u32x4 kn_raw = {0u, 0u, 0u, 0u}, vn_raw = {0u, 0u, 0u, 0u};
+  if (fold_new) {
+    const int64_t row = (((int64_t)s * a.num_kv_heads + kvh) * D + c * VEC) * E;
+    kn_raw = load16((const char*)a.k_new + row);
+    vn_raw = load16((const char*)a.v_new + row);
   }
 
   float m = kNegInf, l = 0.0f;
@@ -335,6 +387,23 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
     }
   }
 
+  if (fold_new) {  // the appended token joins lane row 0 of wave 0
+    const uint32_t wk[4] = {kn_raw[0], kn_raw[1], kn_raw[2], kn_raw[3]};
+    const uint32_t wv[4] = {vn_raw[0], vn_raw[1], vn_raw[2], vn_raw[3]};
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc = fmaf(qf[e], elem_of<dt>(wk, e), acc);
+    const float sn = group_sum<R>(acc);  // every lane row computes it; row 0 takes it
+    if (r == 0) {
+      const float mn = fmaxf(m, sn);
+      const float corr = rescale(m, mn);
+      const float pw = fast_exp2(sn - mn);
+      l = fmaf(l, corr, pw);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[e] = fmaf(o[e], corr, pw * elem_of<dt>(wv, e));
+      m = mn;
+    }
+  }
   // Merge the TPI row states of this wave (lanes with equal c), then the waves.
 #pragma unroll
   for (int off = R; off < 64; off <<= 1) {
@@ -423,8 +492,8 @@ __device__ __forceinline__ void lds_read_k(u32x4 (&t)[2][2], const uint32_t (&ka
 // tile c, reads its query row at qrow[c], null for an empty column) against the tokens of one
 // table row `bt`, KV head kvh, in 32-token steps st0, st0 + 1, ... The block ids of at most
 // max_steps steps are loaded first, with the queries; end_fn() then returns the token at which
-// the workgroup's range ends (a range ending at or before token 32 * st0 means no work: the
-// workgroup returns). The workgroup's waves take the steps in turn, merge their (max, sum,
+// the workgroup's range ends, or -1 for no work (the workgroup returns; a range ending at token
+// 32 * st0 has no step but still merges and stores its empty state). The workgroup's waves take the steps in turn, merge their (max, sum,
 // output) states in LDS and hand the merged state of each column to store(fm, fl, fo) (fo:
 // [16 NC][D]). Each K/V step is read once for all NC tiles.
 // The LDS of one MFMA decode workgroup, declared once per kernel (a kernel may run the core
@@ -447,6 +516,13 @@ struct MfmaSmem {
 // serves, [clo, chi).
 struct StepDesc {
   int index, valid, clo, chi;
+};
+
+// An appended token's K and V rows (pa_decode_append) for the workgroup's KV head, set by the
+// step source's end function when this workgroup folds it in (null otherwise).
+struct NewToken {
+  const char* k = nullptr;
+  const char* v = nullptr;
 };
 
 // Consecutive steps st0, st0 + 1, ... of one table row, up to the token end_fn() returns,
@@ -476,8 +552,9 @@ struct RangeSteps {
     // divergent loop (the zero stores of an empty sequence) is otherwise taken as per-lane, and
     // every buffer resource built from it would be loaded through a waterfall loop.
     t1 = __builtin_amdgcn_readfirstlane(end_fn());
-    if (t1 <= 32 * st0) return false;
-    ns = ((t1 + 31) / 32 - st0 - w + NW - 1) / NW;
+    if (t1 < 0) return false;
+    ns = t1 > 32 * st0 ? ((t1 + 31) / 32 - st0 - w + NW - 1) / NW : 0;
+    if (ns < 0) ns = 0;
     return true;
   }
   __device__ __forceinline__ StepDesc step(int k) const {
@@ -516,7 +593,7 @@ template <DT dt, int D, int BS, int NW, int NBUF, int NC, class Steps, class Sto
 __device__ __forceinline__ void mfma_decode_run(MfmaSmem<D, NW, NBUF, NC>& sm,
                                                 const DecodeArgs& a, int kvh,
                                                 const char* const (&qrow)[NC], Steps& steps,
-                                                StoreFn store) {
+                                                StoreFn store, const NewToken& nt = NewToken{}) {
   static_assert(dt != DT::F32, "MFMA path takes 16-bit inputs");
   static_assert(NC == 1 || Steps::kAllColumns, "per-step column ranges take one tile");
   static_assert(32 % BS == 0 || BS % 32 == 0, "a 32-token step spans whole blocks or part of one");
@@ -552,6 +629,24 @@ __device__ __forceinline__ void mfma_decode_run(MfmaSmem<D, NW, NBUF, NC>& sm,
       qop[c][kk] = __builtin_bit_cast(vec8, raw);
     }
   if (!steps.finalize()) return;  // a step source returns false for the whole workgroup only
+  // An appended token: wave 0 folds it in after its steps; its rows load now. K as the Q^T
+  // operand's head dims (32kk + 8gq ..), V as the output's (MT (4gq + i) .. + MT - 1).
+  using VT = typename VF::T;
+  const bool fold_new = nt.k != nullptr && wave_id() == 0;  // uniform per wave
+  u32x4 kn[KC];
+  VT vn[4];
+#pragma unroll
+  for (int kk = 0; kk < KC; ++kk) kn[kk] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vn[i] = VT{};
+  if (fold_new) {
+    const int gq0 = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) kn[kk] = load16(nt.k + (32 * kk + 8 * gq0) * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      vn[i] = *reinterpret_cast<const VT*>(nt.v + (D / 16) * (4 * gq0 + i) * 2);
+  }
 
   f32x4 oacc[NC][MT];
   float m[NC], lsum[NC];
@@ -765,6 +860,34 @@ __device__ __forceinline__ void mfma_decode_run(MfmaSmem<D, NW, NBUF, NC>& sm,
     }
   }
 
+  if (fold_new) {  // the appended token, one more token of every column of wave 0
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float part = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk) {
+        const u32x4 qw = __builtin_bit_cast(u32x4, qop[c][kk]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          part = fmaf(widen16<dt>(qw[e / 2], e & 1), widen16<dt>(kn[kk][e / 2], e & 1), part);
+      }
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      const float sn = part * a.scale_log2;
+      const float mn = fmaxf(m[c], sn);
+      const float corr = rescale(m[c], mn);
+      const float pw = fast_exp2(sn - mn);
+      lsum[c] = fmaf(lsum[c], corr, gq == 0 ? pw : 0.0f);  // lsum is summed over gq below
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          oacc[c][mt][i] = fmaf(oacc[c][mt][i], corr,
+                                pw * widen16<dt>(vfrag_elem<D>(vn[i], mt), 0));
+      m[c] = mn;
+    }
+  }
+
   // Sum the per-lane partial sums over the four lane groups of each head.
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -827,6 +950,10 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
   const int Hq = a.num_q_heads;
   const int g = Hq / a.num_kv_heads;
   const int ntile = (g + CW - 1) / CW;
+  if (s == a.num_seqs) {  // the appended tokens' store slice (pa_decode_append only)
+    if (p == 0 && unit % ntile == 0) store_new_tokens<dt, D, NT>(a, unit / ntile, BS);
+    return;
+  }
   if (ntile > 1) {
     // More query heads per KV head than one workgroup takes: the ntile head tiles of one
     // (partition, KV head, sequence) read the same K/V tiles. The hardware deals workgroups
@@ -836,7 +963,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
     const int64_t gx = gridDim.x, units = gridDim.y;
     const int64_t L = blockIdx.x + gx * (blockIdx.y + units * blockIdx.z);
     const int64_t span = 8 * (int64_t)ntile;
-    const int64_t full = gx * units * gridDim.z / span * span;
+    const int64_t full = gx * units * a.num_seqs / span * span;
     int64_t W;  // work index over (partition, KV head, sequence)
     int ht;
     if (L < full) {
@@ -867,23 +994,31 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_mfma_kernel(const Decode
                   : nullptr;
   int nparts = 0;
   __shared__ MfmaSmem<D, NW, NBUF, NC> sm;
+  NewToken nt;
   auto end_fn = [&]() -> int {
     const int T = seq_len(a, s, BS);
-    nparts = (T + P - 1) / P;
+    nparts = parts_of(a, T);
     if (T == 0) {
       if (p == 0) store_zeros<dt, D, NT>(a, s, h0, nh);
-      return 0;
+      return -1;
     }
-    if (p >= nparts) return 0;
-    return (T < (p + 1) * P) ? T : (p + 1) * P;
+    if (p >= nparts) return -1;
+    if (a.append && p == nparts - 1) {  // the last partition takes the appended token
+      const int64_t row = ((int64_t)s * a.num_kv_heads + kvh) * D * 2;
+      nt.k = (const char*)a.k_new + row;
+      nt.v = (const char*)a.v_new + row;
+    }
+    const int Tp = pool_len(a, T);  // the pool part; an appended token is folded in after it
+    return (Tp < (p + 1) * P) ? Tp : (p + 1) * P;
   };
   RangeSteps<BS, NW, decltype(end_fn)> steps{a.block_tables + (int64_t)s * a.max_blocks_per_seq,
                                              p * (P / 32), P / 32, a.max_blocks_per_seq,
                                              wave_id(), end_fn};
   mfma_decode_run<dt, D, BS, NW, NBUF, NC>(
-      sm, a, kvh, qrow, steps, [&](const float* fm, const float* fl, const float* fo) {
+      sm, a, kvh, qrow, steps, [&](float* fm, float* fl, float* fo) {
         finish_partition<dt, D, NT>(a, s, h0, nh, p, nparts, fm, fl, fo);
-      });
+      }, nt);
+
 }
 
 // ---- shared-prefix decode ------------------------------------------------------------------
@@ -1033,7 +1168,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void decode_group_kernel(const Decod
       c < ncols ? (const char*)a.q + ((int64_t)(s0 + c / g) * Hq + kvh * g + c % g) * D * 2
                 : nullptr};
   mfma_decode_run<dt, D, BS, NW, NBUF, 1>(
-      sm, a, kvh, qrow, steps, [&](const float* fm, const float* fl, const float* fo) {
+      sm, a, kvh, qrow, steps, [&](float* fm, float* fl, float* fo) {
         finish_group<dt, D, NT>(a, s0, ncols, ct, kvh, p, nparts, fm, fl, fo);
       });
 }
@@ -1105,8 +1240,9 @@ static hipError_t launch_t(DecodePath path, const DecodeArgs& a, hipStream_t str
   // tokens, 192 / 246 us instead of 156 us). An odd gx steps every (unit, sequence) through all
   // eight; the extra partition slot finds no work and returns at once.
   const unsigned gx = (unsigned)a.max_parts | 1u;
+  // pa_decode_append: one more sequence slice, dispatched last, stores the appended tokens
   const dim3 grid(gx, (unsigned)decode_units_per_seq(path, a.num_q_heads, a.num_kv_heads),
-                  (unsigned)a.num_seqs);
+                  (unsigned)(a.num_seqs + (a.append ? 1 : 0)));
   DecodeArgs args_copy = a;
   void* args[] = {&args_copy};
   const void* fn = nullptr;

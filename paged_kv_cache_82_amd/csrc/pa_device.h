@@ -59,6 +59,17 @@ __device__ __forceinline__ float elem_of(const uint32_t (&w)[NWORDS], int i) {
   }
 }
 
+// Element idx of an array of `dt` values, widened to float.
+template <DT dt>
+__device__ __forceinline__ float load_elem(const void* base, int64_t idx) {
+  if constexpr (dt == DT::F32) {
+    return reinterpret_cast<const float*>(base)[idx];
+  } else {
+    const uint32_t w = reinterpret_cast<const uint16_t*>(base)[idx];
+    return widen16<dt>(w, 0);
+  }
+}
+
 // Round a float to the storage type (nearest, ties to even), returned as raw bits.
 template <DT dt>
 __device__ __forceinline__ uint32_t narrow_bits(float x) {

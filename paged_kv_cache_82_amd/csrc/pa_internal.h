@@ -41,6 +41,14 @@ struct DecodeArgs {
   int shared_ctiles;     // 16-column tiles of the largest group (members x query heads per KV head)
   int max_shared;        // host bound on the shared tokens of any sequence (a multiple of 32)
   int32_t* part_n;       // [S][Hq] partitions each (sequence, query head) was split into
+  // Fused append (pa_decode_append; null / 0 otherwise): the newest token of sequence s,
+  // position context_lens[s] - 1, comes from k_new / v_new ([S][Hkv][D]) instead of the pool:
+  // the pool part is the first context_lens[s] - 1 tokens, the last partition folds the new
+  // token into its state, and the new K/V rows are stored at new_slots[s] (not when < 0).
+  const void* k_new;
+  const void* v_new;
+  const int32_t* new_slots;
+  int append;
 };
 
 // Workspace layout for a given problem: byte offsets of each region.

@@ -40,7 +40,8 @@ def declared_functions(header=HEADER):
 
 
 def test_header_declares_the_calls():
-    assert declared_functions() == ["pa_copy_blocks", "pa_decode", "pa_decode_noalloc",
+    assert declared_functions() == ["pa_copy_blocks", "pa_decode", "pa_decode_append",
+                                    "pa_decode_noalloc",
                                     "pa_decode_shared_prefix",
                                     "pa_decode_shared_prefix_workspace_size",
                                     "pa_decode_workspace_size", "pa_prefill",
@@ -143,6 +144,31 @@ def test_decode_argument_checks(lib):
         assert lib.pa_set_decode_kernel(0) == PA_OK
     assert lib.pa_set_decode_kernel(3) == PA_ERR_INVALID_ARG
     assert lib.pa_set_decode_kernel(-1) == PA_ERR_INVALID_ARG
+
+
+def test_decode_append_argument_checks(lib):
+    """The fused append shares pa_decode's checks and needs its three extra arrays, aligned."""
+    f = lib.pa_decode_append
+    args = [BAD, BAD, BAD, BAD, BAD, BAD, BAD, BAD, BAD, 0.125, 4, 8, 8, 128, 16, 4, 64, 50, 0,
+            None, 0, F16, None]
+    names = ["out", "q", "k", "v", "kn", "vn", "slots", "bt", "cl", "scale", "S", "Hq", "Hkv",
+             "d", "B", "M", "N", "maxT", "P", "ws", "wsb", "dt", "stream"]
+
+    def call(**kw):
+        a = list(args)
+        for k, val in kw.items():
+            a[names.index(k)] = val
+        return f(*a)
+
+    assert call(S=0) == PA_OK
+    assert call(S=0, kn=None, vn=None, slots=None) == PA_OK
+    for k in ("kn", "vn", "slots", "q", "bt"):
+        assert call(**{k: None}) == PA_ERR_INVALID_ARG, k
+    assert call(kn=V(0x1008)) == PA_ERR_INVALID_ARG  # k_new rows need 16-byte alignment
+    assert call(slots=V(0x1002)) == PA_ERR_INVALID_ARG
+    assert call(Hq=8, Hkv=3) == PA_ERR_INVALID_ARG
+    assert call(d=96) == PA_ERR_UNSUPPORTED
+    assert call(maxT=4096) == PA_ERR_WORKSPACE  # split: needs pa_decode's workspace
 
 
 def test_decode_noalloc_argument_checks(lib):
