@@ -493,9 +493,10 @@ __device__ __forceinline__ void lds_read_k(u32x4 (&t)[2][2], const uint32_t (&ka
 // table row `bt`, KV head kvh, in 32-token steps st0, st0 + 1, ... The block ids of at most
 // max_steps steps are loaded first, with the queries; end_fn() then returns the token at which
 // the workgroup's range ends, or -1 for no work (the workgroup returns; a range ending at token
-// 32 * st0 has no step but still merges and stores its empty state). The workgroup's waves take the steps in turn, merge their (max, sum,
-// output) states in LDS and hand the merged state of each column to store(fm, fl, fo) (fo:
-// [16 NC][D]). Each K/V step is read once for all NC tiles.
+// 32 * st0 has no step but still merges and stores its empty state). The workgroup's waves take
+// the steps in turn, merge their (max, sum, output) states in LDS and hand the merged state of
+// each column to store(fm, fl, fo) (fo: [16 NC][D]). Each K/V step is read once for all NC
+// tiles.
 // The LDS of one MFMA decode workgroup, declared once per kernel (a kernel may run the core
 // from more than one place). A wave's output state for the merge, [16][D] floats, takes the
 // place of its own K ring once its steps are done (no other wave touches that ring).
