@@ -372,7 +372,12 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeArgs a
   // A ring of NBUF register buffers: the loads of the next NBUF-1 blocks are in flight while
   // one block is consumed. Prefetches are unconditional (past the end they read the shared
   // first tile, a cache hit) so that the compiler's wait before each consume only covers the
-  // oldest buffer.
+  // oldest buffer. The round can stop part-way, which gives the loop a path back to its head
+  // with slots still loading: the compiler waits for every load in flight there, once per
+  // round. The form without that wait (whole rounds, then the last steps on their own, as in
+  // the MFMA kernel) was 0.7% slower on the 13B-shape batch and no faster elsewhere (MI355X,
+  // same box): at this kernel's load count the memory system is saturated, and the extra
+  // requests in flight only queue.
   if (nb > 0) {
     u32x4 kbuf[NBUF][NL], vbuf[NBUF][NL];
 #pragma unroll
@@ -650,12 +655,15 @@ __device__ __forceinline__ void mfma_decode_run(MfmaSmem<D, NW, NBUF, NC>& sm,
   }
 
   f32x4 oacc[NC][MT];
-  float m[NC], lsum[NC];
+  // Running state per column: reference maximum m (base 2), the shift nm = -m (0 while m is
+  // -inf), the row sum and the output, all relative to m.
+  float m[NC], nm[NC], lsum[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) oacc[c][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     m[c] = kNegInf;
+    nm[c] = 0.0f;
     lsum[c] = 0.0f;
   }
 
@@ -760,14 +768,15 @@ __device__ __forceinline__ void mfma_decode_run(MfmaSmem<D, NW, NBUF, NC>& sm,
     __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the consume that follows
   };
 
-  auto consume = [&](int k, auto slotc, VRegs<D>& R) {
+  // waitc: loads that may still be in flight once this step's K loads (and every load issued
+  // before them) are done: its own 8 V loads and those of the fetches issued after it (8 V and
+  // KD K loads each).
+  auto consume = [&](int k, auto slotc, VRegs<D>& R, auto waitc) {
     constexpr int slot = decltype(slotc)::value;
     const StepDesc sd = steps.step(k);
     // token r of the step counts for this lane's column: r < valid, and the column is served
     const bool col_ok = Steps::kAllColumns || (hh >= sd.clo && hh < sd.chi);
-    // This step's K loads (and all loads issued before them) are done once at most its own 8 V
-    // loads and those of the NBUF - 1 later fetches (8 V and KD K loads each) are outstanding.
-    wait_vmcnt<(NBUF - 1) * (8 + KD) + 8>();
+    wait_vmcnt<decltype(waitc)::value>();
     u32x4 kf[2][KC];
     lds_read_k<slot * KSTEP, 16 * RB>(kf, ka);
     // S^T = K Q^T: sacc[c][u][i] = score of token tau0 + 16u + 4*gq + i for column 16c + hh;
@@ -785,42 +794,59 @@ __device__ __forceinline__ void mfma_decode_run(MfmaSmem<D, NW, NBUF, NC>& sm,
         for (int c = 0; c < NC; ++c)
           sacc[c][u] = M::mma(__builtin_bit_cast(vec8, kf[u][kk]), qop[c][kk], sacc[c][u]);
     const bool tail = sd.valid < 32 || (!Steps::kAllColumns && (sd.clo > 0 || sd.chi < 16));
-    vec8 pop[NC];
+    // Weights are taken against a reference maximum m[c] (base 2) that is raised only when a
+    // score passes it by more than kSlack: weights stay below 2^kSlack, and the running sum and
+    // the output share the reference, so the normalised result is that of the exact running
+    // maximum. In most steps neither the maximum's lane shuffles nor the rescale of the output
+    // accumulators (held in AGPRs: a read, a multiply and a write each) run.
+    float sc[NC][8], lm[NC];
+    bool raise = false;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      float sc[8];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float x = sacc[c][u][i] * a.scale_log2;
           if (tail && (16 * u + 4 * gq + i >= sd.valid || !col_ok)) x = kNegInf;
-          sc[4 * u + i] = x;
+          sc[c][4 * u + i] = x;
         }
-      float bm = sc[0];
+      float x = sc[c][0];
 #pragma unroll
-      for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sc[e]);
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      const float mn = fmaxf(m[c], bm);
-      const bool empty = (mn == kNegInf);
-      const float corr = empty ? 1.0f : fast_exp2(m[c] - mn);
+      for (int e = 1; e < 8; ++e) x = fmaxf(x, sc[c][e]);
+      lm[c] = x;
+      raise = raise || (x > m[c] + kSlack);  // m = -inf: any finite score raises
+    }
+    if (__builtin_amdgcn_ballot_w64(raise)) {  // uniform; rare once the maxima settle
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        float bm = fmaxf(lm[c], __shfl_xor(lm[c], 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float mn = fmaxf(m[c], bm);
+        const float corr = rescale(m[c], mn);  // 0 while m is -inf (nothing accumulated yet)
+        lsum[c] *= corr;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) oacc[c][mt] *= corr;
+        m[c] = mn;
+        // m stays -inf only while every score of the column was -inf; the shift is 0 then,
+        // and the weights exp2(-inf) = 0
+        nm[c] = mn == kNegInf ? 0.0f : -mn;
+      }
+    }
+    vec8 pop[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float pe[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(sc[c][e] + nm[c]);
+      const u32x4 pw = {pack2<dt>(pe[0], pe[1]), pack2<dt>(pe[2], pe[3]),
+                        pack2<dt>(pe[4], pe[5]), pack2<dt>(pe[6], pe[7])};
       // The weights are rounded to 16 bits for the p.V MFMA; the row sum adds those same
       // rounded weights (dot2 of each packed pair with (1, 1)), so numerator and denominator
       // agree.
-      float pe[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pe[e] = empty ? 0.0f : fast_exp2(sc[e] - mn);
-      const u32x4 pw = {pack2<dt>(pe[0], pe[1]), pack2<dt>(pe[2], pe[3]),
-                        pack2<dt>(pe[4], pe[5]), pack2<dt>(pe[6], pe[7])};
-      float ps = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ps = sum2<dt>(pw[j], ps);
+      for (int j = 0; j < 4; ++j) lsum[c] = sum2<dt>(pw[j], lsum[c]);
       pop[c] = __builtin_bit_cast(vec8, pw);
-      lsum[c] = fmaf(lsum[c], corr, ps);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) oacc[c][mt] *= corr;
-      m[c] = mn;
     }
     if (tail) {  // V rows past the step's valid tokens may hold anything, NaN included
 #pragma unroll
@@ -849,16 +875,21 @@ __device__ __forceinline__ void mfma_decode_run(MfmaSmem<D, NW, NBUF, NC>& sm,
   if (ns > 0) {  // rings of NBUF slots, unconditional prefetch (see the VALU kernel)
     VRegs<D> rb[NBUF];
     static_for<NBUF - 1>([&](auto uc) { fetch(decltype(uc)::value, uc, rb[decltype(uc)::value]); });
-    // Unrolled NBUF steps at a time so that every slot index is a constant.
-    for (int k = 0; k < ns; k += NBUF) {
-      static_for<NBUF>([&](auto uc) {
-        constexpr int u = decltype(uc)::value;
-        if (k + u >= ns) return;  // uniform
-        constexpr int ahead = (u + NBUF - 1) % NBUF;
-        fetch(k + u + NBUF - 1, std::integral_constant<int, ahead>{}, rb[ahead]);
-        consume(k + u, uc, rb[u]);
-      });
-    }
+    // Every slot index is a constant: step k uses slot k % NBUF. In whole rounds NBUF - 1
+    // fetches follow a step's; in the last ns % NBUF steps (u = k % NBUF), which fetch nothing,
+    // NBUF - 2 - u.
+    ring_loop<NBUF>(
+        ns,
+        [&](int k, auto uc) {
+          constexpr int u = decltype(uc)::value;
+          constexpr int ahead = (u + NBUF - 1) % NBUF;
+          fetch(k + NBUF - 1, std::integral_constant<int, ahead>{}, rb[ahead]);
+          consume(k, uc, rb[u], std::integral_constant<int, (NBUF - 1) * (8 + KD) + 8>{});
+        },
+        [&](int k, auto uc) {
+          constexpr int u = decltype(uc)::value;
+          consume(k, uc, rb[u], std::integral_constant<int, (NBUF - 2 - u) * (8 + KD) + 8>{});
+        });
   }
 
   if (fold_new) {  // the appended token, one more token of every column of wave 0

@@ -19,6 +19,32 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// A register/LDS ring of NBUF slots over n steps, step k in slot k % NBUF: whole rounds of
+// NBUF steps in a loop, step(k, integral_constant<int, k % NBUF>) each, then the last n % NBUF
+// steps as last_step(k, ...), each inside the previous one's test. last_step issues no loads:
+// every step it would prefetch lies past the end (and loads whose registers nothing reads would
+// be removed by the compiler, which would upset a counted wait). A round that could stop
+// part-way would give the loop a path back to its head with ring slots still loading; the
+// compiler's wait insertion takes that path into account and waits for more loads than a step
+// needs (a slot reused at the head then waits for every load in flight), which cuts the
+// prefetch depth.
+template <int U, int N, typename F>
+__device__ __forceinline__ void ring_tail(int left, int k, F& f) {
+  if constexpr (U < N) {
+    if (U < left) {
+      f(k + U, std::integral_constant<int, U>{});
+      ring_tail<U + 1, N>(left, k, f);
+    }
+  }
+}
+template <int NBUF, typename F, typename G>
+__device__ __forceinline__ void ring_loop(int n, F&& step, G&& last_step) {
+  int k = 0;
+  for (; k + NBUF <= n; k += NBUF)
+    static_for<NBUF>([&](auto uc) { step(k + decltype(uc)::value, uc); });
+  ring_tail<0, NBUF - 1>(n - k, k, last_step);
+}
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -35,6 +61,9 @@ struct Elem {
 
 constexpr float kLog2e = 1.4426950408889634f;  // log2(e): exp(x) = exp2(x * log2(e))
 constexpr float kNegInf = -__builtin_inff();
+// A score may exceed the reference maximum by this much (base 2) before a running softmax state
+// is rescaled: weights stay below 2^8 = 256, well inside fp16/bf16 and fp32 sums.
+constexpr float kSlack = 8.0f;
 
 // ---- element access inside packed 32-bit words ------------------------------------------
 
