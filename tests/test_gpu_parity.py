@@ -105,6 +105,20 @@ def test_workspace_reused_with_other_lengths():
         assert_attention_close(dev.run(), ref, step.dtype, f"reused workspace {lens}")
 
 
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("Hq,B", [(8, 16), (32, 8), (64, 32), (8, 64)])
+def test_mfma_ring_tails(dt, Hq, B, decode_kernel):
+    # A wave of an MFMA workgroup takes every 4th 32-token step of its partition through a ring
+    # of 3 slots: whole rounds of 3 in a loop, then the last 1 or 2 steps on their own, with
+    # counted waits of their own. Lengths 32 s - 5 (s = 1 .. 28 steps, whole sequences) give the
+    # waves 0 to 7 steps each, so every remainder follows 0, 1 and 2 whole rounds; 16- and
+    # 32-head workgroups, every block-size path of the loads.
+    decode_kernel("mfma")
+    lens = [32 * s - 5 for s in range(1, 29)]
+    step = make_step("ring", 700 + Hq + B, lens, Hq, 2, 128, B, dt)
+    _run_and_check(step, partition_tokens=1024, what=f"ring tails {dt} Hq{Hq} B{B}")
+
+
 @pytest.mark.parametrize("path", ["valu", "mfma"])
 def test_both_decode_paths_on_gqa(path, decode_kernel):
     decode_kernel(path)
