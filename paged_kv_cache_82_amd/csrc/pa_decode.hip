@@ -1212,12 +1212,14 @@ constexpr int kWaves = 4;          // waves per workgroup
 // more blocks in flight per wave beat more waves per SIMD up to these depths.
 constexpr int kValuBuffers = 4;    // VALU kernel: blocks in registers (NBUF-1 in flight)
 // fp32 units of 8 or more loads per tensor (d = 128) take 3: four of them need more registers
-// than a wave has and spill.
+// than a wave has and spill. Units of one or two loads per tensor (8-token blocks, or d = 64 at
+// 16-bit) take 8, so that a wave keeps about as many bytes in flight as with 4-load units:
+// measured on MI355X, the 13B-shape batch with 8-token blocks went from 168.5 to 157.7 us, and
+// 64-dim batches by 1.5% (10 or 12 buffers were slower).
 template <DT dt, int D, int BS>
 constexpr int valu_buffers() {
-  return (dt == DT::F32 && ValuCfg<dt, D, valu_unit_tokens<BS>(), kWaves>::NL >= 8)
-             ? 3
-             : kValuBuffers;
+  constexpr int NL = ValuCfg<dt, D, valu_unit_tokens<BS>(), kWaves>::NL;
+  return (dt == DT::F32 && NL >= 8) ? 3 : NL <= 2 ? 8 : kValuBuffers;
 }
 constexpr int kMfmaBuffers = 3;    // MFMA kernel: 32-token steps in registers
 constexpr int kMfmaMinBlocks = 1;  // MFMA kernel: workgroups per CU the registers must allow
