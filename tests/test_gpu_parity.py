@@ -119,6 +119,19 @@ def test_mfma_ring_tails(dt, Hq, B, decode_kernel):
     _run_and_check(step, partition_tokens=1024, what=f"ring tails {dt} Hq{Hq} B{B}")
 
 
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d,B", [(128, 8), (64, 16), (128, 16)])
+def test_valu_ring_tails(dt, d, B, decode_kernel):
+    # The vector-ALU kernel's register ring is 8 deep for units of one or two loads per tensor
+    # (8-token blocks, 64-dim heads at 16-bit) and 3 or 4 deep otherwise. Lengths 32 k + 5
+    # (k = 0 .. 39, whole sequences) give the waves up to 39 units each: several whole rounds of
+    # every ring depth, then every remainder.
+    decode_kernel("valu")
+    lens = [32 * k + 5 for k in range(40)]
+    step = make_step("vring", 740 + d + B, lens, 4, 4, d, B, dt)
+    _run_and_check(step, partition_tokens=2048, what=f"valu ring tails {dt} d{d} B{B}")
+
+
 @pytest.mark.parametrize("path", ["valu", "mfma"])
 def test_both_decode_paths_on_gqa(path, decode_kernel):
     decode_kernel(path)
