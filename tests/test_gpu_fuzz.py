@@ -15,7 +15,7 @@ from workloads import make_prefill_step, make_step
 
 pytestmark = pytest.mark.gpu
 
-DECODE_CASES = 24
+DECODE_CASES = 32
 PREFILL_CASES = 16
 
 
@@ -29,7 +29,7 @@ def _decode_case(i):
     d = int(rng.choice([64, 128]))
     B = int(rng.choice([8, 16, 32, 64]))
     Hkv = int(rng.choice([1, 2, 4]))
-    g = int(rng.choice([1, 2, 4, 8, 16]))
+    g = int(rng.choice([1, 2, 4, 8, 16, 24, 32]))  # 24, 32: two 16-head MFMA column tiles
     S = int(rng.integers(1, 13))
     lens = [int(x) for x in rng.choice([0, 1, 2, 15, 16, 17, 100, 333, 1024, 2500], size=S)]
     lens[0] = max(lens[0], 1)
