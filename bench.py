@@ -292,7 +292,7 @@ def prefill_cpu_baseline(step, budget_s: float = 12.0) -> dict:
                       f"tokens), fp64 oracle, {reps} passes in {elapsed:.1f} s"}
 
 
-def run_prefill(args):
+def measure_prefill(workload: str, args, cpu: bool) -> dict:
     """One step = pa_write_kv of every sequence's chunk, then pa_prefill. The bound is the
     matrix cores (about 2d flops per byte of K/V per query row): the roofline is the dense
     fp16/bf16 MFMA peak."""
@@ -303,7 +303,7 @@ def run_prefill(args):
     import workloads
 
     t_gen = time.perf_counter()
-    step = getattr(workloads, WORKLOADS[args.workload][0])(poison=False)
+    step = getattr(workloads, WORKLOADS[workload][0])(poison=False)
     t_gen = time.perf_counter() - t_gen
     dev = torch.device("cuda")
 
@@ -384,7 +384,7 @@ def run_prefill(args):
         "dtype": step.dtype, "accumulate": "f32",
         "data": "synthetic (seeded N(0,1) K/V/q; lengths and placement as described)",
         "config": {
-            "workload": WORKLOADS[args.workload][1],
+            "workload": WORKLOADS[workload][1],
             "num_seqs": step.num_seqs, "num_q_heads": step.num_q_heads,
             "num_kv_heads": step.num_kv_heads, "head_dim": step.head_dim,
             "block_size": step.block_size, "num_blocks": step.num_blocks,
@@ -402,16 +402,25 @@ def run_prefill(args):
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(fl / att_s / 1e12 / peak, 4),
-            "traffic": measured_traffic("prefill", args.workload[len("prefill-"):]),
+            "traffic": measured_traffic("prefill", workload[len("prefill-"):]),
             "algorithmic_flops_per_launch": fl,
             "algorithmic_bytes_per_launch": prefill_bytes(step),
             "avg_launch_us": round(att_s * 1e6, 3),
         },
         "input_generation_s": round(t_gen, 2),
     }
-    if not args.no_cpu_baseline:
+    if cpu:
         res["cpu_baseline"] = prefill_cpu_baseline(step)
-    print(json.dumps(res))
+    del pools, kc0, vc0, q, bt, cl, qs, writes, out
+    if not args.no_graph:
+        del graph
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_prefill(args):
+    print(json.dumps(measure_prefill(args.workload, args, cpu=not args.no_cpu_baseline)))
 
 
 def run_copy_calibration(args):
@@ -563,7 +572,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="time the default (13B-shape) workload only, not the other decode "
-                         "workloads after it")
+                         "and prefill workloads after it")
     ap.add_argument("--separate-write", action="store_true",
                     help="decode steps: pa_write_kv then pa_decode, not pa_decode_append")
     ap.add_argument("--no-graph", action="store_true",
@@ -608,10 +617,29 @@ def main():
                                                             compare_plain=True))
             print(f"bench: {name} measured in {time.perf_counter() - t0:.1f} s", file=sys.stderr,
                   flush=True)
+        # The chunked-prefill workloads (the matrix-core-bound path), same contract, under
+        # their own keys; their roofline is the MFMA peak.
+        for name in EXTRA_PREFILL:
+            t0 = time.perf_counter()
+            res["workloads"][name] = prefill_summary(measure_prefill(name, args, cpu=False))
+            print(f"bench: {name} measured in {time.perf_counter() - t0:.1f} s", file=sys.stderr,
+                  flush=True)
     print(json.dumps(res))
 
 
 EXTRA_WORKLOADS = ("gqa", "long", "shared")
+EXTRA_PREFILL = ("prefill-mha13b", "prefill-gqa")
+
+
+def prefill_summary(res: dict) -> dict:
+    """The per-workload figures of one prefill measurement."""
+    r = res["roofline"]
+    return {"workload": res["config"]["workload"], "dtype": res["dtype"], "value": res["value"],
+            "unit": res["unit"], "ms_per_step": res["ms_per_step"],
+            "query_tokens_per_s": res["query_tokens_per_s"],
+            "roofline": {k: r[k] for k in ("kernel", "bound", "achieved", "peak", "unit", "frac",
+                                           "traffic", "algorithmic_flops_per_launch",
+                                           "algorithmic_bytes_per_launch", "avg_launch_us")}}
 
 
 def summary(res: dict) -> dict:
