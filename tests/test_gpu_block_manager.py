@@ -5,6 +5,8 @@ into samples that share its blocks, each sample appends its own tokens (copy-on-
 applied with pa_copy_blocks first), and pa_decode over the manager's tables matches the CPU
 oracle on the same pool. Preemption ([PA-summary] "vLLM"): a sequence moves to a pinned host
 pool and back to other device blocks (pa_bm_move + pa_swap_blocks) and decodes bit-identically.
+A serving loop: decode steps through pa_decode_append over the manager's slots, with a fork and
+a finished sequence inside the loop.
 """
 import numpy as np
 import pytest
@@ -153,3 +155,66 @@ def test_chunked_prefill_fork_and_decode_driven_by_the_native_manager():
     assert_attention_close(to_host(out, dt), oracle.decode(q, kc, vc, tables, lens, scale, dt),
                            dt, "decode after fork")
     assert_attention_close(got, to_float64(to_host(out, dt), dt), dt, "prefill n=1 vs decode")
+
+
+def test_decode_loop_with_fused_append_driven_by_the_native_manager():
+    # A serving loop ([PA-summary] "vLLM": each iteration, every running sequence generates one
+    # token): prompts of mixed lengths are written, then 12 decode steps run through
+    # pa_decode_append, each sequence's new token attended to directly and stored at the slot
+    # the manager reserved for it. Sequence 0 forks into a second sample before step 3 (the
+    # loop then copies its partly filled last block, copy-on-write, before the fused call) and
+    # sequence 1 finishes before step 6 (its blocks return to the free list and are taken
+    # again). Every step matches the oracle's write-then-decode on the same pool, and the pools
+    # match bit for bit at the end.
+    rng = np.random.default_rng(930)
+    N, B, Hq, Hkv, d, dt = 160, 16, 16, 2, 128, "f16"
+    scale = np.float32(1 / np.sqrt(d))
+    bm = BlockManager(N, B, rng.permutation(N))
+    kc = full((N, Hkv, B, d), nan_value(dt), dt)
+    vc = kc.copy()
+    dk, dv = to_dev(kc, dt), to_dev(vc, dt)
+    running = []
+    for s, T in enumerate([37, 200, 1, 16, 95]):
+        bm.add(s)
+        slots, pairs = bm.append(s, T)
+        assert len(pairs) == 0
+        k1, v1 = _kv(rng, T, Hkv, d, dt)
+        oracle.write_kv(kc, vc, k1, v1, slots, dt)
+        pa.pa_write_kv(dk, dv, to_dev(k1, dt), to_dev(v1, dt), to_dev(slots))
+        running.append(s)
+    copies = 0
+    for it in range(12):
+        if it == 3:
+            bm.fork(0, 5)
+            running.append(5)
+        if it == 6:
+            bm.release(1)
+            running.remove(1)
+        slots = []
+        for s in running:
+            sl, pairs = bm.append(s, 1)
+            if len(pairs):
+                copies += len(pairs)
+                oracle.copy_blocks(kc, vc, pairs, dt)
+                pa.pa_copy_blocks(dk, dv, to_dev(pairs))
+            slots.append(int(sl[0]))
+        slots = np.asarray(slots, np.int32)
+        S = len(running)
+        kn, vn = _kv(rng, S, Hkv, d, dt)
+        q = to_storage(rng.standard_normal((S, Hq, d)).astype(np.float32), dt)
+        tables = bm.tables(running)
+        lens = np.array([bm.length(s) for s in running], np.int32)
+        oracle.write_kv(kc, vc, kn, vn, slots, dt)
+        ref = oracle.decode(q, kc, vc, tables, lens, scale, dt)
+        dq = to_dev(q, dt)
+        out = torch.empty_like(dq)
+        ws = torch.empty(max(1, pa.pa_decode_workspace_size(S, Hq, Hkv, d, B, int(lens.max()), 0,
+                                                            torch.float16)),
+                         dtype=torch.uint8, device="cuda")
+        pa.pa_decode_append(out, dq, dk, dv, to_dev(kn, dt), to_dev(vn, dt), to_dev(slots),
+                            to_dev(tables), to_dev(lens), float(scale), int(lens.max()), ws)
+        torch.cuda.synchronize()
+        assert_attention_close(to_host(out, dt), ref, dt, f"decode step {it} ({S} sequences)")
+    assert copies >= 1, "the fork's first write must copy the shared last block"
+    assert np.array_equal(to_host(dk, dt).view(np.uint16), kc.view(np.uint16))
+    assert np.array_equal(to_host(dv, dt).view(np.uint16), vc.view(np.uint16))
