@@ -791,8 +791,8 @@ def measure_decode(workload: str, args, cpu: bool, compare_plain: bool = False) 
     # Part 2: K decode launches back to back (rotating pool copies) between two events on the
     # launch stream; the average is the decode kernel's launch duration for the roofline (an
     # event right before each launch would also time the dispatch gap after the KV write).
-    # At least 100 launches: with the driver's 20 steps a short batch (7 ms for the GQA step)
-    # read a few percent slow.
+    # At least 100 launches: with 20 a short batch (7 ms for the GQA step) read a few percent
+    # slow.
     n_roof = max(args.steps, 100)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()

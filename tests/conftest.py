@@ -44,13 +44,14 @@ def pytest_terminal_summary(terminalreporter):
         terminalreporter.write_line("full-size parity (observed max errors):")
         for line in PARITY_LOG:
             terminalreporter.write_line("  " + line)
-        # the same lines as JSON, in the folder a GPU run's outputs are collected from
-        import json
+        # the same lines as JSON, when PA_PARITY_JSON names a file to write them to
+        path = os.environ.get("PA_PARITY_JSON")
+        if path:
+            import json
 
-        out = os.path.join(ROOT, "gpurun_out")
-        try:
-            os.makedirs(out, exist_ok=True)
-            with open(os.path.join(out, "parity_observed.json"), "w") as f:
-                json.dump({"full_size_parity": list(PARITY_LOG)}, f, indent=1)
-        except OSError:
-            pass
+            try:
+                os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+                with open(path, "w") as f:
+                    json.dump({"full_size_parity": list(PARITY_LOG)}, f, indent=1)
+            except OSError:
+                pass
