@@ -618,7 +618,7 @@ def main():
             print(f"bench: {name} measured in {time.perf_counter() - t0:.1f} s", file=sys.stderr,
                   flush=True)
         # The chunked-prefill workloads (the matrix-core-bound path), same contract, under
-        # their own keys; their roofline is the MFMA peak.
+        # their own keys; their roofline is the MFMA peak of their dtype.
         for name in EXTRA_PREFILL:
             t0 = time.perf_counter()
             res["workloads"][name] = prefill_summary(measure_prefill(name, args, cpu=False))
@@ -628,7 +628,7 @@ def main():
 
 
 EXTRA_WORKLOADS = ("gqa", "long", "shared")
-EXTRA_PREFILL = ("prefill-mha13b", "prefill-gqa")
+EXTRA_PREFILL = ("prefill-mha13b", "prefill-gqa", "prefill-f32")
 
 
 def prefill_summary(res: dict) -> dict:
