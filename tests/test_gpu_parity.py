@@ -132,6 +132,55 @@ def test_valu_ring_tails(dt, d, B, decode_kernel):
     _run_and_check(step, partition_tokens=2048, what=f"valu ring tails {dt} d{d} B{B}")
 
 
+def _rising_scores(step, rise_log2, rng):
+    """Rewrite the single sequence of a decode step so that its scores climb by about
+    rise_log2 (base-2 exponent, times 1 + h/16 for query head h) from one 32-token step to the
+    next, with small noise inside each step: the running maximum keeps rising, in jumps below
+    and above any fixed slack. K dim 0 carries the ramp, the other dims and V are random."""
+    from workloads import to_storage
+
+    dt, B, d, Hkv = step.dtype, step.block_size, step.head_dim, step.num_kv_heads
+    T = int(step.context_lens[0])
+    n_new = sum(w.k_new.shape[0] for w in step.writes)
+    prefix = T - n_new
+    unit = 1.0 / (4.0 * float(step.scale) * np.log2(np.e))  # K dim 0 per unit of log2 score
+    k = 0.3 * rng.standard_normal((T, Hkv, d))
+    k[:, :, 0] = rise_log2 * unit * (np.arange(T) // 32)[:, None]
+    v = rng.standard_normal((T, Hkv, d))
+    table = step.block_tables[0]
+    for t in range(prefix):
+        step.k_cache[table[t // B], :, t % B, :] = to_storage(k[t], dt)
+        step.v_cache[table[t // B], :, t % B, :] = to_storage(v[t], dt)
+    at = prefix
+    for w in step.writes:
+        m = w.k_new.shape[0]
+        w.k_new[...] = to_storage(k[at:at + m], dt)
+        w.v_new[...] = to_storage(v[at:at + m], dt)
+        at += m
+    Hq = step.q.shape[1]
+    q = 0.3 * rng.standard_normal(step.q.shape)
+    q[..., 0] = 4.0 * (1.0 + np.arange(Hq) / 16.0)
+    step.q[...] = to_storage(q, dt)
+    return step
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("Hq", [16, 64])
+@pytest.mark.parametrize("rise", [0.5, 1.9, 2.1, 8.5])
+@pytest.mark.parametrize("P", [0, 256])
+def test_mfma_rising_maximum(dt, Hq, rise, P, decode_kernel):
+    # The MFMA kernels take weights against a reference maximum that is raised only when a
+    # score passes it by more than a slack (2^8 in weight). Scores that climb from step to step
+    # (a wave sees every 4th step, so 4 x rise per wave step: 2, 7.6, 8.4 and 34 in the base-2
+    # exponent, more for the later heads) raise it never, sometimes or at every step; whole
+    # sequences and 256-token partitions (the merge then combines partials with different
+    # references).
+    decode_kernel("mfma")
+    rng = np.random.default_rng(int(rise * 10) + Hq)
+    step = _rising_scores(make_step("rise", 760 + Hq, [1000], Hq, 2, 128, 16, dt), rise, rng)
+    _run_and_check(step, partition_tokens=P, what=f"rising maximum {dt} Hq{Hq} rise {rise} P{P}")
+
+
 @pytest.mark.parametrize("path", ["valu", "mfma"])
 def test_both_decode_paths_on_gqa(path, decode_kernel):
     decode_kernel(path)
