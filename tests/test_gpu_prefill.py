@@ -135,6 +135,42 @@ def test_prefill_small_weights_below_fp16_normal(dt, g):
     _check(step, f"dominant token {dt} g{g}")
 
 
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("g", [1, 8])
+@pytest.mark.parametrize("rise", [2.0, 7.9, 8.1, 20.0])
+def test_prefill_rising_maximum(dt, g, rise):
+    # The prefill kernels take weights against a reference maximum raised only past a slack of
+    # 2^8. Scores that climb by about `rise` in the base-2 exponent (times 1 + h/16 for query
+    # head h) from one 32-token stage to the next, prefix and chunk alike, raise it never,
+    # sometimes or at every stage. fp32 scores this large (up to about 2e3) carry rounding
+    # errors of their own, hence the scaled fp32 bound.
+    from workloads import to_storage
+
+    Hkv, d, B = 2, 128, 16
+    prefix, n = 700, 300
+    step = make_prefill_step("rise", 780 + g, [prefix + n], [n], g * Hkv, Hkv, d, B, dt)
+    rng = np.random.default_rng(int(rise * 10) + g)
+    T = prefix + n
+    unit = 1.0 / (4.0 * float(step.scale) * np.log2(np.e))
+    k = 0.3 * rng.standard_normal((T, Hkv, d))
+    k[:, :, 0] = rise * unit * (np.arange(T) // 32)[:, None]
+    v = rng.standard_normal((T, Hkv, d))
+    table = step.block_tables[0]
+    for t in range(prefix):
+        step.k_cache[table[t // B], :, t % B, :] = to_storage(k[t], dt)
+        step.v_cache[table[t // B], :, t % B, :] = to_storage(v[t], dt)
+    at = prefix
+    for w in step.writes:
+        m = w.k_new.shape[0]
+        w.k_new[...] = to_storage(k[at:at + m], dt)
+        w.v_new[...] = to_storage(v[at:at + m], dt)
+        at += m
+    q = 0.3 * rng.standard_normal(step.q.shape)
+    q[..., 0] = 4.0 * (1.0 + np.arange(g * Hkv) / 16.0)
+    step.q[...] = to_storage(q, dt)
+    _check(step, f"rising maximum {dt} g{g} rise {rise}", f32_score_factor=1000.0)
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("scale", [0.0, -1.0 / 128 ** 0.5, 3.0])
 def test_prefill_scale_zero_negative_large(dt, scale):
