@@ -63,6 +63,8 @@ CASES = [
     (16, 2, 128, 16, "bf16", [1, 5, 16, 33, 130, 1500]),       # MFMA kernel
     (64, 2, 128, 64, "bf16", [1, 63, 64, 65, 900]),            # 32 heads per workgroup
     (8, 2, 64, 8, "f16", [0, 1, 9, 0, 300]),                   # empty sequences
+    (8, 8, 64, 16, "bf16", [1, 15, 16, 17, 250, 1100]),        # vector-ALU, 8-deep ring
+    (8, 8, 128, 8, "f16", [1, 7, 8, 9, 400, 1500]),            # vector-ALU, 8-deep ring
 ]
 
 
